@@ -1,0 +1,291 @@
+"""Seeded synthetic inputs for the MoE decode-layer step (shared by tests, bench and smoke).
+
+This module is the only code that both the fp64 oracle's callers and the HIP path's
+callers use.  It draws numbers and lays them out; it holds none of the layer's arithmetic
+(no projection, routing or activation function).
+
+Generator: Philox4x32-10 (Salmon et al., SC'11), implemented twice from its published
+definition -- in C for the host (``philox_host.c``) and in HIP for the device
+(``fill_device.hip``) -- so that the ~34 GB of routed-expert weights can be filled in HBM
+while the oracle regenerates exactly the experts it needs on the host.  Element n of the
+stream (key0, key1) sums the four 32-bit Philox words of counter (n, 0, 0) (an Irwin-Hall
+approximation of a normal draw), centres and scales the sum in double to the requested
+standard deviation, then rounds RNE to fp32 and, for bf16 tensors, RNE to bf16.
+
+Workload shapes follow the layer description (hidden 7168, 384 experts top-8, SwiGLU
+intermediate 2048, a tensor-parallel rank's share with o-proj slice 448 and intermediate 128,
+and a tiny fp32 layer); the per-token resample attempts that keep the top-k boundary gap
+>= 1e-3 are stored in ``tests/golden/attempts.json`` (written by a script that calls the
+oracle).
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import math
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_ROOT = os.path.dirname(_HERE)
+HOST_LIB = os.path.join(_HERE, "libsynth_host.so")
+DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
+ATTEMPTS_JSON = os.path.join(_ROOT, "tests", "golden", "attempts.json")
+
+# Tensor stream ids (key1) for weights; key0 is the layer seed.
+T_WO, T_WR, T_BIAS, T_W13, T_W2, T_WS13, T_WS2, T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+# Token streams: key0 = token seed, key1 = TOKEN_BASE + 16 * attempt + kind.
+TOKEN_BASE = 0x100
+KIND_X, KIND_R = 0, 1
+
+WEIGHT_SIGMA = 0.02
+ACT_SIGMA = 1.0
+BIAS_SIGMA = 0.1
+ZIPF_S = 1.2
+
+# std of the sum of four independent uniform 32-bit words
+_SUM_STD = math.sqrt((2.0**64 - 1.0) / 3.0)
+
+
+def scale_for(sigma: float) -> float:
+    return float(sigma) / _SUM_STD
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    hidden: int
+    oproj_in: int
+    n_experts: int
+    top_k: int
+    inter: int
+    shared_inter: int
+    dtype: str  # "f32" or "bf16" (weights, x, r, out)
+    batches: tuple
+    bias: str  # "normal" | "zero" | "zipf"
+    gap_space: str  # "key" | "logit"
+    layer_seed: int = 0
+    description: str = ""
+
+    @property
+    def wbytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def max_batch(self) -> int:
+        return max(self.batches)
+
+
+CONFIGS = {
+    c.name: c
+    for c in [
+        LayerConfig("tiny_fp32", 256, 256, 16, 2, 128, 128, "f32", (1,), "normal", "key",
+                    description="tiny fp32 layer, batch 1"),
+        LayerConfig("full_b1", 7168, 7168, 384, 8, 2048, 2048, "bf16", (1,), "normal", "key",
+                    description="full-size layer, batch 1 (GEMV path)"),
+        LayerConfig("full_b8", 7168, 7168, 384, 8, 2048, 2048, "bf16", (8,), "normal", "key",
+                    description="full-size layer, batch 8, token seeds 0-7"),
+        LayerConfig("full_b64", 7168, 7168, 384, 8, 2048, 2048, "bf16", (64,), "zero", "logit",
+                    description="full-size layer, batch 64, uniform router bias"),
+        LayerConfig("tp_rank", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8, 64), "zipf", "key",
+                    description="one TP16 rank's share, Zipf(1.2) router bias, batch sweep"),
+    ]
+}
+
+
+# ----------------------------------------------------------------------------- host library
+_host = None
+
+
+def _build_host_lib() -> None:
+    src = os.path.join(_HERE, "philox_host.c")
+    tmp = HOST_LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", tmp])
+    os.replace(tmp, HOST_LIB)
+
+
+def build(force: bool = True) -> None:
+    """Compile the host generator (gcc) and the device fill (hipcc, gfx950)."""
+    if force or not os.path.exists(HOST_LIB):
+        _build_host_lib()
+    if force or not os.path.exists(DEV_LIB):
+        src = os.path.join(_HERE, "fill_device.hip")
+        tmp = DEV_LIB + ".tmp"
+        subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-shared", "-fPIC",
+                               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                               src, "-o", tmp], stderr=subprocess.DEVNULL)
+        os.replace(tmp, DEV_LIB)
+
+
+def _lib():
+    global _host
+    if _host is None:
+        if not os.path.exists(HOST_LIB):
+            _build_host_lib()
+        lib = ctypes.CDLL(HOST_LIB)
+        lib.synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                   ctypes.c_uint32, ctypes.c_uint32, ctypes.c_double]
+        lib.synth_fill.restype = None
+        lib.synth_u32.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                  ctypes.c_uint32, ctypes.c_uint32]
+        lib.synth_u32.restype = None
+        lib.synth_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.synth_philox4x32_10.restype = None
+        _host = lib
+    return _host
+
+
+def philox4x32_10(counter, key):
+    """Raw Philox4x32-10 block: 4 counter words, 2 key words -> 4 output words."""
+    c = np.asarray(counter, dtype=np.uint32).copy()
+    k = np.asarray(key, dtype=np.uint32).copy()
+    out = np.zeros(4, dtype=np.uint32)
+    _lib().synth_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
+def host_stream(count: int, key0: int, key1: int, sigma: float, dtype: str, first: int = 0):
+    """Elements first..first+count-1 of stream (key0, key1): float32 array or bf16 bits (uint16)."""
+    if dtype == "f32":
+        out = np.empty(count, dtype=np.float32)
+        code = 0
+    elif dtype == "bf16":
+        out = np.empty(count, dtype=np.uint16)
+        code = 1
+    else:
+        raise ValueError(dtype)
+    if count:
+        _lib().synth_fill(out.ctypes.data, code, first, count, key0 & 0xFFFFFFFF, key1 & 0xFFFFFFFF,
+                          scale_for(sigma))
+    return out
+
+
+def host_u32(count: int, key0: int, key1: int, first: int = 0):
+    out = np.empty(count, dtype=np.uint32)
+    if count:
+        _lib().synth_u32(out.ctypes.data, first, count, key0, key1)
+    return out
+
+
+# ----------------------------------------------------------------------------- layer tensors
+def weight_spec(cfg: LayerConfig):
+    """name -> (shape, stream id, sigma).  Out-major layouts (each output row contiguous)."""
+    H, Ko, E, I, Is = cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.inter, cfg.shared_inter
+    return {
+        "w_o": ((H, Ko), T_WO, WEIGHT_SIGMA),
+        "w_r": ((E, H), T_WR, WEIGHT_SIGMA),
+        "w13": ((E, 2 * I, H), T_W13, WEIGHT_SIGMA),
+        "w2": ((E, H, I), T_W2, WEIGHT_SIGMA),
+        "ws13": ((2 * Is, H), T_WS13, WEIGHT_SIGMA),
+        "ws2": ((H, Is), T_WS2, WEIGHT_SIGMA),
+    }
+
+
+def host_weight(cfg: LayerConfig, name: str):
+    shape, tid, sigma = weight_spec(cfg)[name]
+    n = int(np.prod(shape))
+    return host_stream(n, cfg.layer_seed, tid, sigma, cfg.dtype).reshape(shape)
+
+
+def host_expert(cfg: LayerConfig, e: int):
+    """(w13_e [2I][H], w2_e [H][I]) of routed expert e, generated on the host."""
+    H, I = cfg.hidden, cfg.inter
+    n13, n2 = 2 * I * H, H * I
+    w13 = host_stream(n13, cfg.layer_seed, T_W13, WEIGHT_SIGMA, cfg.dtype, first=e * n13)
+    w2 = host_stream(n2, cfg.layer_seed, T_W2, WEIGHT_SIGMA, cfg.dtype, first=e * n2)
+    return w13.reshape(2 * I, H), w2.reshape(H, I)
+
+
+def host_bias(cfg: LayerConfig):
+    """Router bias, fp32 [E]."""
+    E = cfg.n_experts
+    if cfg.bias == "normal":
+        return host_stream(E, cfg.layer_seed, T_BIAS, BIAS_SIGMA, "f32")
+    if cfg.bias == "zero":
+        return np.zeros(E, dtype=np.float32)
+    if cfg.bias == "zipf":
+        # Zipf(s) probability mass over ranks 1..E, placed through a random permutation of
+        # the experts (rank r -> expert perm[r-1]); permutation = experts ordered by a
+        # Philox draw, ties by index.
+        u = host_u32(E, cfg.layer_seed, T_PERM)
+        perm = np.lexsort((np.arange(E), u))
+        ranks = np.arange(1, E + 1, dtype=np.float64)
+        pmf = ranks ** (-ZIPF_S)
+        pmf /= pmf.sum()
+        b = np.empty(E, dtype=np.float64)
+        b[perm] = pmf
+        return b.astype(np.float32)
+    raise ValueError(cfg.bias)
+
+
+def token_key(attempt: int, kind: int) -> int:
+    return TOKEN_BASE + 16 * int(attempt) + kind
+
+
+def host_token(cfg: LayerConfig, t: int, attempt: int):
+    """(x_t [Ko], r_t [H]) for token seed t, resample attempt `attempt`."""
+    x = host_stream(cfg.oproj_in, t, token_key(attempt, KIND_X), ACT_SIGMA, cfg.dtype)
+    r = host_stream(cfg.hidden, t, token_key(attempt, KIND_R), ACT_SIGMA, cfg.dtype)
+    return x, r
+
+
+def load_attempts(path: str = ATTEMPTS_JSON) -> dict:
+    with open(path) as f:
+        return json.load(f)
+
+
+def attempts_for(cfg: LayerConfig, B: int, table: dict | None = None):
+    table = load_attempts() if table is None else table
+    ent = table["configs"][cfg.name]["attempts"]
+    if B > len(ent):
+        raise ValueError(f"{cfg.name}: attempts stored for {len(ent)} tokens, asked for {B}")
+    return [int(a) for a in ent[:B]]
+
+
+def host_tokens(cfg: LayerConfig, B: int, attempts=None):
+    """x [B][Ko], r [B][H] for token seeds 0..B-1 (attempts from the stored table by default)."""
+    if attempts is None:
+        attempts = attempts_for(cfg, B)
+    xs, rs = zip(*(host_token(cfg, t, attempts[t]) for t in range(B)))
+    return np.stack(xs), np.stack(rs)
+
+
+def bf16_bits_to_f32(bits):
+    """bf16 bit patterns (uint16) -> float32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------- device fill
+_dev = None
+
+
+def _dev_lib():
+    global _dev
+    if _dev is None:
+        if not os.path.exists(DEV_LIB):
+            raise RuntimeError(f"{DEV_LIB} is not built: run __graft_entry__.build()")
+        lib = ctypes.CDLL(DEV_LIB)
+        lib.synth_dev_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64,
+                                       ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_double, ctypes.c_void_p]
+        lib.synth_dev_fill.restype = ctypes.c_int
+        _dev = lib
+    return _dev
+
+
+def device_stream(ptr: int, count: int, key0: int, key1: int, sigma: float, dtype: str,
+                  first: int = 0, stream: int = 0) -> None:
+    """Fill `count` elements at device address `ptr` with elements first.. of stream (key0, key1)."""
+    code = {"f32": 0, "bf16": 1}[dtype]
+    rc = _dev_lib().synth_dev_fill(ptr, code, first, count, key0 & 0xFFFFFFFF, key1 & 0xFFFFFFFF,
+                                   scale_for(sigma), stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_dev_fill failed: hip error {rc}")
+
+
+def device_weight(cfg: LayerConfig, name: str, ptr: int, stream: int = 0) -> None:
+    shape, tid, sigma = weight_spec(cfg)[name]
+    device_stream(ptr, int(np.prod(shape)), cfg.layer_seed, tid, sigma, cfg.dtype, stream=stream)

@@ -1,0 +1,107 @@
+"""Seeded input generator: Philox known answers, stream consistency, distributions, gap table."""
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+
+# Known-answer vectors of Philox4x32-10 published with the generator's definition
+# (Salmon, Moraes, Dror, Shaw, SC'11; Random123 distribution, kat_vectors):
+# (counter words, key words) -> output words.
+KAT = [
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", KAT)
+def test_philox_known_answers(ctr, key, want):
+    assert tuple(int(v) for v in synth.philox4x32_10(ctr, key)) == want
+
+
+def test_element_is_scaled_centred_sum_of_words():
+    # element n = fp32(double(sum of the 4 words of counter (n,0,0,0) - (2^33-2)) * scale)
+    for n in [0, 1, 12345, 2**32 + 7]:
+        w = synth.philox4x32_10((n & 0xFFFFFFFF, n >> 32, 0, 0), (3, 77))
+        c = int(w.astype(np.uint64).sum()) - (2**33 - 2)
+        want = np.float32(float(c) * synth.scale_for(0.5))
+        got = synth.host_stream(1, 3, 77, 0.5, "f32", first=n)[0]
+        assert got == want
+
+
+def test_stream_offsets_are_consistent():
+    full = synth.host_stream(5000, 0, 4, 0.02, "bf16")
+    part = synth.host_stream(1000, 0, 4, 0.02, "bf16", first=3000)
+    assert np.array_equal(full[3000:4000], part)
+
+
+def test_bf16_is_rne_of_fp32():
+    f = synth.host_stream(100000, 1, 9, 1.0, "f32")
+    b = synth.host_stream(100000, 1, 9, 1.0, "bf16")
+    u = f.view(np.uint32).astype(np.uint64)
+    rne = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(b, rne)
+
+
+def test_distribution_moments():
+    v = synth.host_stream(2_000_000, 0, 5, 0.02, "f32").astype(np.float64)
+    assert abs(v.mean()) < 1e-4
+    assert v.std() == pytest.approx(0.02, rel=2e-3)
+    # Irwin-Hall(4): bounded at sqrt(12)*sigma, kurtosis 2.7
+    assert np.abs(v).max() <= np.sqrt(12) * 0.02 + 1e-6
+    k = ((v - v.mean()) ** 4).mean() / v.var() ** 2
+    assert k == pytest.approx(2.7, abs=0.02)
+
+
+def test_expert_slices_match_whole_tensor():
+    cfg = synth.CONFIGS["tiny_fp32"]
+    w13 = synth.host_weight(cfg, "w13")
+    w2 = synth.host_weight(cfg, "w2")
+    for e in [0, 5, 15]:
+        a, b = synth.host_expert(cfg, e)
+        assert np.array_equal(a, w13[e]) and np.array_equal(b, w2[e])
+
+
+def test_bias_recipes():
+    b = synth.host_bias(synth.CONFIGS["tp_rank"]).astype(np.float64)
+    assert b.sum() == pytest.approx(1.0, abs=1e-6)
+    ranks = np.arange(1, 385, dtype=np.float64)
+    pmf = ranks ** -1.2 / (ranks ** -1.2).sum()
+    np.testing.assert_allclose(np.sort(b)[::-1], pmf, rtol=1e-6)
+    assert b.max() == pytest.approx(0.246, abs=1e-3)
+    assert np.all(synth.host_bias(synth.CONFIGS["full_b64"]) == 0)
+    n = synth.host_bias(synth.CONFIGS["full_b1"]).astype(np.float64)
+    assert n.std() == pytest.approx(0.1, rel=0.15)
+
+
+def test_config_shapes():
+    c = synth.CONFIGS
+    assert (c["full_b1"].hidden, c["full_b1"].n_experts, c["full_b1"].top_k, c["full_b1"].inter) == (7168, 384, 8, 2048)
+    assert (c["tp_rank"].oproj_in, c["tp_rank"].inter, c["tp_rank"].batches) == (448, 128, (1, 2, 8, 64))
+    assert (c["tiny_fp32"].hidden, c["tiny_fp32"].n_experts, c["tiny_fp32"].top_k) == (256, 16, 2)
+    assert c["full_b64"].bias == "zero" and c["full_b64"].gap_space == "logit"
+
+
+def test_attempt_table_gaps_hold():
+    table = synth.load_attempts()
+    for name, cfg in synth.CONFIGS.items():
+        ent = table["configs"][name]
+        assert len(ent["attempts"]) == cfg.max_batch
+        assert min(ent["gaps"]) >= 1e-3
+
+
+def test_attempt_table_tiny_recomputed():
+    cfg = synth.CONFIGS["tiny_fp32"]
+    (j,) = synth.attempts_for(cfg, 1)
+    x, r = synth.host_token(cfg, 0, j)
+    h = O.oproj_residual(x[None], r[None], synth.host_weight(cfg, "w_o"))
+    key = O.selection_keys(O.sigmoid(O.router_logits(h, synth.host_weight(cfg, "w_r"))), synth.host_bias(cfg))
+    assert O.topk_gap(key, cfg.top_k)[0] >= 1e-3
+    for jj in range(j):  # earlier attempts were rejected
+        x, r = synth.host_token(cfg, 0, jj)
+        h = O.oproj_residual(x[None], r[None], synth.host_weight(cfg, "w_o"))
+        key = O.selection_keys(O.sigmoid(O.router_logits(h, synth.host_weight(cfg, "w_r"))), synth.host_bias(cfg))
+        assert O.topk_gap(key, cfg.top_k)[0] < 1e-3
