@@ -1,0 +1,215 @@
+"""Benchmark: one decode-layer step (o-proj + residual, router/top-k, routed experts || shared
+expert, combine) per timed step, on one MI355X, through the C ABI with a replayed HIP graph.
+
+Prints ONE JSON line on stdout (everything else goes to stderr).  Default workload: the
+full-size layer (hidden 7168, 384 experts top-8, SwiGLU intermediate 2048, bf16 weights,
+~34 GB of routed experts resident in HBM) at batch 1.
+
+Timing protocol: weights and inputs are resident in HBM before timing starts.  Each timed
+step is {flush the last-level cache by streaming a 1 GiB buffer; event A; graph launch;
+event B} on one stream, so every weight byte is fetched from HBM; value = median(B - A).
+The whole bracket (barrier + synchronize on both sides, flushes included) is reported as
+wall_ms_per_iter.  A "warm" figure (back-to-back steps, no flush) is reported separately and
+never used for the roofline fraction.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def unique_bytes(cfg, n_act: int) -> dict:
+    wb = cfg.wbytes
+    H, Ko, E, I, Is = cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.inter, cfg.shared_inter
+    parts = {
+        "oproj": wb * H * Ko,
+        "router": wb * E * H + 4 * E,
+        "shared_gateup": wb * 2 * Is * H,
+        "routed_gateup": wb * n_act * 2 * I * H,
+        "down_combine": wb * (n_act * H * I + H * Is),
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def cpu_baseline(cfg, B: int, reps: int) -> dict:
+    """The fp64 oracle on the host cores, on one step of the same workload (bounded sample)."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    x, r = synth.host_tokens(cfg, B)
+    dense = {n: synth.host_weight(cfg, n) for n in ("w_o", "w_r", "ws13", "ws2")}
+    bias = synth.host_bias(cfg)
+    # routing first (untimed) to pre-generate exactly the experts the step touches
+    probe = O.layer_step(x, r, O.LayerWeights(dense["w_o"], dense["w_r"], bias,
+                                              lambda e: (np.zeros((2 * cfg.inter, cfg.hidden)),
+                                                         np.zeros((cfg.hidden, cfg.inter))),
+                                              dense["ws13"], dense["ws2"]), cfg.top_k)
+    experts = {int(e): synth.host_expert(cfg, int(e)) for e in probe["act"]}
+    W = O.LayerWeights(dense["w_o"], dense["w_r"], bias, lambda e: experts[int(e)], dense["ws13"],
+                       dense["ws2"])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        O.layer_step(x, r, W, cfg.top_k)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    cores = len(os.sched_getaffinity(0))
+    return {"value": t * 1e6, "unit": "us/step", "tokens_per_s": B / t, "cores": cores,
+            "kind": "oracle", "reps": reps,
+            "sample": f"one whole step of {cfg.name} at batch {B} ({len(experts)} routed experts "
+                      f"touched); fp64 numpy incl. bf16->fp64 upcasts; weights pre-generated"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="full_b1")
+    ap.add_argument("--batch", type=int, default=0, help="default: the workload's first batch")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=1)
+    ap.add_argument("--no-timing-pass", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import synth.device as sd
+    from moe_layer_skinny_amd import kk
+
+    cfg = synth.CONFIGS[args.config]
+    B = args.batch or cfg.batches[0]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] {cfg.name} B={B}: filling weights on device")
+    w = sd.device_weights(cfg, device=dev)
+    layer = kk.Layer(kk.make_config(cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.top_k, cfg.inter,
+                                    cfg.shared_inter, cfg.dtype), w, B)
+    plan = layer.query_plan(B)
+    x, r, _, _ = sd.device_tokens(cfg, B, device=dev)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out = torch.empty(B, cfg.hidden, dtype=dt, device=dev)
+    idx = torch.empty(B, cfg.top_k, dtype=torch.int32, device=dev)
+    gate = torch.empty(B, cfg.top_k, dtype=torch.float32, device=dev)
+    ws = layer.new_workspace(dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    s = torch.cuda.Stream(dev)
+
+    def step():
+        layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=True)
+
+    with torch.cuda.stream(s):
+        for _ in range(args.warmup):
+            flush.add_(1.0)
+            step()
+    s.synchronize()
+    n_act = int(torch.unique(idx).numel())
+    by = unique_bytes(cfg, n_act)
+
+    # ---- timed region: K steps, each preceded by an (untimed) cache flush
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for a, b in evs:
+            flush.add_(1.0)
+            a.record(s)
+            step()
+            b.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    med = statistics.median(us)
+    p10, p90 = us[int(0.1 * (len(us) - 1))], us[int(0.9 * (len(us) - 1))]
+
+    # ---- warm figure: back-to-back steps, no flush (cache-assisted; not the headline)
+    wa, wb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        wa.record(s)
+        for _ in range(args.steps):
+            step()
+        wb_.record(s)
+    s.synchronize()
+    warm_us = wa.elapsed_time(wb_) * 1e3 / args.steps
+
+    # ---- per-kernel durations (eager launches, library HIP events on each kernel's stream)
+    kernels = {}
+    if not args.no_timing_pass:
+        layer.set_kernel_timing(True)
+        layer.read_kernel_timing()
+        with torch.cuda.stream(s):
+            for _ in range(args.steps):
+                flush.add_(1.0)
+                layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=False)
+        s.synchronize()
+        recs = layer.read_kernel_timing()
+        layer.set_kernel_timing(False)
+        for name, ms in recs:
+            kernels.setdefault(name, []).append(ms * 1e3)
+        kernels = {k: statistics.mean(v) for k, v in kernels.items()}
+
+    dom_name = "gateup_gemv_routed" if plan["path_name"] == "gemv" else "gateup_mfma_routed"
+    roofline = None
+    if dom_name in kernels:
+        dom_bytes = by["routed_gateup"]
+        ach = dom_bytes / (kernels[dom_name] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": None, "bytes_per_launch": dom_bytes,
+                    "avg_launch_us": round(kernels[dom_name], 3)}
+
+    gbs = by["total"] / (med * 1e-6) / 1e9
+    res = {
+        "metric": "µs per decode-layer step + achieved HBM GB/s (% of peak) at batch 1/8/64",
+        "value": round(med, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(med / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "accum_dtype": "f32",
+        "data": "synthetic (seeded Philox weights N(0,0.02)-like, tokens N(0,1)-like, random init)",
+        "config": {"workload": cfg.name, "description": cfg.description, "batch": B,
+                   "hidden": cfg.hidden, "oproj_in": cfg.oproj_in, "n_experts": cfg.n_experts,
+                   "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
+                   "router_bias": cfg.bias, "path": plan["path_name"],
+                   "kernels_per_step": plan["kernels_per_step"], "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(B / (med * 1e-6), 1),
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "unique_bytes": by["total"], "n_act": n_act,
+        "p10_us": round(p10, 3), "p90_us": round(p90, 3),
+        "wall_ms_per_iter_incl_flush": round(wall * 1e3 / args.steps, 4),
+        "warm_us_per_step_no_flush": round(warm_us, 3),
+        "kernel_us_eager": {k: round(v, 3) for k, v in kernels.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu:
+        log("[bench] timing the oracle on the host cores")
+        res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_reps)
+    layer.close()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

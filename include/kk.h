@@ -1,0 +1,164 @@
+/*
+ * kk.h -- C ABI of the MI355X (gfx950) MoE decode-layer step.
+ *
+ * One small-batch (1..64 token) decode step of the weight-bandwidth-bound part of a
+ * Kimi-K3-style layer:
+ *   h   = r + x W_o^T                       attention output projection + residual
+ *   l   = h W_r^T, s = sigmoid(l)            router scores
+ *   S_t = top-k of (s + b)                   selection (bias steers selection only)
+ *   g   = s[S_t] / sum s[S_t] * routed_scale renormalised gates
+ *   out = h + sum_j g_j SwiGLU_{S_t,j}(h) + SwiGLU_shared(h)
+ * Sources: "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section
+ * "Recovering time between operators" (o-proj fused with residual processing; router
+ * scores; selected experts; the shared expert on another stream; small-matrix kernels at
+ * batch 1-2 and split-K at larger batch); "vLLM Hyper-Optimizes Kimi K3 on NVIDIA GB300 for
+ * Blazing-FAST Inference", section "What's Optimized" (per-batch kernel choice, shared
+ * expert in parallel on a separate stream).  The pages print no formula; the math above
+ * is the plain reading of the operations they name (sigmoid + bias router, renormalised
+ * gates, gated SwiGLU with gate rows before up rows, no norm before the experts).
+ *
+ * Layouts (all row-major, "out-major": each output row contiguous along its reduction dim)
+ *   w_o  [H][Ko]     w_r [E][H]     router_bias [E] (fp32)
+ *   w13  [E][2I][H]  rows 0..I-1 gate (W1), rows I..2I-1 up (W3)
+ *   w2   [E][H][I]   ws13 [2Is][H]  ws2 [H][Is]
+ *   x [B][Ko], resid [B][H], out [B][H]  in the config dtype; h32 [B][H] fp32.
+ *   topk_idx [B][k] int32, ascending expert index within each token; topk_gate [B][k] fp32
+ *   in the same order.  Slot of (token t, position j) = t*k + j.
+ *   expert_offsets [E+1] int32: exclusive prefix sum of per-expert slot counts.
+ *   perm [B*k] int32: slots ordered by (expert, token).
+ *
+ * Ownership: the caller owns every buffer (weights, activations, outputs, workspace).
+ * Weights passed to kk_create must stay alive and unchanged until kk_destroy.  The
+ * context owns an auxiliary HIP stream, events, a small counter buffer and cached HIP
+ * graphs.  Every device pointer must be 16-byte aligned; ws must be 256-byte aligned.
+ *
+ * Concurrency: every op is asynchronous on the caller's stream; no host synchronisation.
+ * One host thread and one stream at a time per context (the ops share the context's
+ * counters and auxiliary stream).
+ *
+ * Errors: arguments are validated on the host before anything is enqueued; a failure
+ * returns a status and sets kk_last_error() (thread-local text).  A shape outside the
+ * supported set returns KK_ERR_UNSUPPORTED -- there is no slower fallback.  A failed HIP
+ * launch returns KK_ERR_HIP; device faults surface at the caller's next synchronisation.
+ * No op writes the weights.
+ */
+#ifndef KK_H_
+#define KK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KK_OK = 0,
+  KK_ERR_INVALID_ARG = 1,
+  KK_ERR_UNSUPPORTED = 2,
+  KK_ERR_WORKSPACE = 3,
+  KK_ERR_HIP = 4
+} kk_status;
+
+typedef enum { KK_F32 = 0, KK_BF16 = 1 } kk_dtype;
+
+typedef enum {
+  KK_PATH_GEMV = 0,       /* batch 1-2: bf16/fp32 weight rows streamed with 128-bit loads */
+  KK_PATH_SPLITK_MFMA = 1 /* batch 3-64: MFMA tiles, split-K with an fp32 second stage */
+} kk_path;
+
+/* kk_layer_decode flags */
+#define KK_GRAPH 1u /* capture the step once per (B, buffers, stream) and replay it */
+
+typedef struct {
+  int32_t hidden;       /* H  */
+  int32_t oproj_in;     /* Ko */
+  int32_t n_experts;    /* E  */
+  int32_t top_k;        /* k  */
+  int32_t inter;        /* I  (routed SwiGLU intermediate) */
+  int32_t shared_inter; /* Is (shared SwiGLU intermediate) */
+  int32_t dtype;        /* kk_dtype of weights, x, resid and out */
+  float routed_scale;   /* multiplies the renormalised gates; 1.0 */
+} kk_config;
+
+typedef struct {
+  const void* w_o;
+  const void* w_r;
+  const float* router_bias;
+  const void* w13;
+  const void* w2;
+  const void* ws13;
+  const void* ws2;
+} kk_weights;
+
+typedef struct {
+  int32_t path;             /* kk_path chosen for this batch */
+  int32_t forced;           /* 1 if the KK_FORCE_PLAN environment variable chose it */
+  int32_t oproj_splitk;     /* K splits of the o-proj (1 on the GEMV path) */
+  int32_t router_splitk;    /* K splits of the router logits */
+  int32_t kernels_per_step; /* kernel launches of one kk_layer_decode step */
+  int32_t streams;          /* streams one step uses (2: main + shared expert) */
+} kk_plan;
+
+typedef struct kk_ctx kk_ctx;
+typedef void* kk_stream; /* a hipStream_t; NULL = the null stream */
+
+/* Supported set today: max_batch 1..64; E <= 512 with k <= min(E, 16); bf16: H = 7168,
+ * Ko in {448, 7168}, I and Is in {128, 2048}; fp32: H = Ko = 256, I = Is = 128 and
+ * batch <= 2.  Host-only: enqueues nothing and touches no device. */
+kk_status kk_validate(const kk_config* cfg, int32_t max_batch);
+
+/* Bytes of workspace every op needs for any B <= max_batch (0 if cfg is invalid). */
+size_t kk_workspace_bytes(const kk_config* cfg, int32_t max_batch);
+
+/* Creates a context on the current HIP device; weights are referenced, not copied. */
+kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch, kk_ctx** out);
+kk_status kk_destroy(kk_ctx* ctx);
+
+/* Which path and how many launches a step of batch B uses (no device work). */
+kk_status kk_query_plan(const kk_ctx* ctx, int32_t B, kk_plan* out);
+
+/* h32 = resid + x W_o^T (fp32); h_out (nullable) = the same rounded RNE to the config
+ * dtype. "Recovering time between operators": o-proj fused with residual processing. */
+kk_status kk_oproj_residual(kk_ctx* ctx, int32_t B, const void* x, const void* resid, float* h32,
+                            void* h_out, void* ws, kk_stream stream);
+
+/* Router: logits from fp32 h32, sigmoid scores, selection keys (s + b, fp64), top-k,
+ * renormalised gates, and the token->expert permutation with expert offsets (prefix sum).
+ * "Recovering time between operators": router scores in MoE preparation. */
+kk_status kk_router_topk(kk_ctx* ctx, int32_t B, const float* h32, int32_t* topk_idx,
+                         float* topk_gate, int32_t* expert_offsets, int32_t* perm, void* ws,
+                         kk_stream stream);
+
+/* Routed experts (each selected expert's weights read once) on `stream`, the shared expert
+ * on the context's auxiliary stream, and the combine out = h32 + sum g y + y_shared (RNE to
+ * the config dtype).  Routing tables as written by kk_router_topk.
+ * "Recovering time between operators": selected experts; shared expert on another stream. */
+kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t* topk_idx,
+                        const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
+                        void* out, void* ws, kk_stream stream);
+
+/* The whole step: o-proj + residual, router, routed experts || shared expert, combine.
+ * topk_idx / topk_gate are optional copies of the routing (nullable).  With KK_GRAPH the
+ * step is captured into a HIP graph on first use for these (B, pointers, stream) and
+ * replayed afterwards (one host->device submission per step). */
+kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,
+                          int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
+                          uint32_t flags);
+
+/* Per-kernel timing of eager (non-graph) launches: when enabled, every kernel the context
+ * launches is bracketed by HIP events on its own stream.  kk_read_kernel_timing waits for
+ * the recorded events and returns up to `cap` (name, milliseconds) records of the launches
+ * since the last read, clearing them.  Names stay valid until kk_destroy. */
+kk_status kk_set_kernel_timing(kk_ctx* ctx, int32_t enable);
+kk_status kk_read_kernel_timing(kk_ctx* ctx, const char** names, float* ms, int32_t cap,
+                                int32_t* count);
+
+const char* kk_status_string(kk_status s);
+const char* kk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KK_H_ */

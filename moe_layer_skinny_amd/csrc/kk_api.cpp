@@ -1,0 +1,595 @@
+// Host side of the C ABI (include/kk.h): argument validation, plan selection, workspace
+// layout, the context (auxiliary stream + fork/join events), HIP graph capture/replay and
+// optional per-kernel event timing.  All device work is in kk_gemv.hip / kk_mfma.hip.
+//
+// "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", sections "Recovering
+// time between operators" (per-batch kernel choice, the shared expert on another stream,
+// fewer launches) and "Faster code needs targeted validation" (the chosen path must be
+// visible to callers and tests: no silent fallback to another implementation).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/kk.h"
+#include "kk_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+kk_status fail(kk_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+kk_status hip_fail(hipError_t e, const char* what) {
+  return fail(KK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxBatch = 64;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxOprojSplits = 16;
+constexpr int kMaxRouterSplits = 32;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace carve-up (offsets in bytes from ws, each 256-byte aligned).
+struct Layout {
+  size_t h32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, A, As, Y, ys,
+      oproj_part, total;
+};
+
+Layout make_layout(const kk_config& c, int Bm) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  const size_t slots = (size_t)Bm * c.top_k;
+  L.h32 = take((size_t)Bm * c.hidden * 4);
+  L.logit_part = take((size_t)kMaxRouterSplits * Bm * c.n_experts * 4);
+  L.topk_idx = take(slots * 4);
+  L.topk_gate = take(slots * 4);
+  L.offsets = take((size_t)(c.n_experts + 1) * 4);
+  L.perm = take(slots * 4);
+  L.inv_perm = take(slots * 4);
+  L.act = take((size_t)c.n_experts * 4);
+  L.n_act = take(16);
+  L.A = take(slots * c.inter * 4);
+  L.As = take((size_t)Bm * c.shared_inter * 4);
+  L.Y = take(slots * c.hidden * 4);
+  L.ys = take((size_t)Bm * c.hidden * 4);
+  L.oproj_part = take((size_t)kMaxOprojSplits * Bm * c.hidden * 4);
+  L.total = o;
+  return L;
+}
+
+kk::Shape to_shape(const kk_config& c) {
+  return kk::Shape{c.hidden, c.oproj_in, c.n_experts, c.top_k, c.inter, c.shared_inter, c.dtype,
+                   c.routed_scale};
+}
+
+bool misaligned(const void* p, size_t a = 16) { return ((uintptr_t)p) % a != 0; }
+
+kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
+  if (!c) return fail(KK_ERR_INVALID_ARG, "config is NULL");
+  if (max_batch < 1 || max_batch > kMaxBatch)
+    return fail(KK_ERR_INVALID_ARG, "max_batch %d outside 1..%d", max_batch, kMaxBatch);
+  if (c->dtype != KK_F32 && c->dtype != KK_BF16)
+    return fail(KK_ERR_INVALID_ARG, "dtype %d is neither KK_F32 nor KK_BF16", c->dtype);
+  if (c->hidden <= 0 || c->oproj_in <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->inter <= 0 ||
+      c->shared_inter <= 0)
+    return fail(KK_ERR_INVALID_ARG, "every dimension must be positive");
+  if (c->top_k > c->n_experts)
+    return fail(KK_ERR_INVALID_ARG, "top_k %d > n_experts %d", c->top_k, c->n_experts);
+  if (!(c->routed_scale > 0.f) || c->routed_scale != c->routed_scale)
+    return fail(KK_ERR_INVALID_ARG, "routed_scale must be a positive number");
+  if (c->top_k > kMaxTopK)
+    return fail(KK_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
+  if (c->n_experts > kMaxExperts)
+    return fail(KK_ERR_UNSUPPORTED, "n_experts %d > %d", c->n_experts, kMaxExperts);
+  const int esz = c->dtype == KK_BF16 ? 2 : 4;
+  if ((c->hidden * esz) % 16 || (c->oproj_in * esz) % 16 || (c->inter * esz) % 16 ||
+      (c->shared_inter * esz) % 16)
+    return fail(KK_ERR_INVALID_ARG, "rows must be whole 16-byte chunks (H, Ko, I, Is multiple of %d)",
+                16 / esz);
+  kk::Shape s = to_shape(*c);
+  if (c->dtype == KK_BF16) {
+    if (!(s.H == 7168 && (s.Ko == 7168 || s.Ko == 448) && (s.I == 2048 || s.I == 128) && s.I == s.Is))
+      return fail(KK_ERR_UNSUPPORTED,
+                  "bf16 shapes supported: H=7168, Ko in {448,7168}, I=Is in {128,2048}");
+  } else {
+    if (!(s.H == 256 && s.Ko == 256 && s.I == 128 && s.Is == 128))
+      return fail(KK_ERR_UNSUPPORTED, "fp32 shapes supported: H=Ko=256, I=Is=128");
+    if (max_batch > 2) return fail(KK_ERR_UNSUPPORTED, "fp32 layers run batch <= 2 only");
+  }
+  return KK_OK;
+}
+
+const char* kernel_names[] = {"oproj_gemv", "router_gemv", "gateup_gemv_shared",
+                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep"};
+enum KName { K_OPROJ, K_ROUTER, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP };
+
+struct TimingRec {
+  int name;
+  hipEvent_t a, b;
+};
+
+struct GraphEntry {
+  int B;
+  const void *x, *r, *out, *idx, *gate, *ws;
+  hipStream_t stream;
+  hipGraphExec_t exec;
+  unsigned long long uses;
+};
+
+}  // namespace
+
+struct kk_ctx {
+  kk_config cfg;
+  kk::Shape shape;
+  kk::Weights w;
+  int max_batch;
+  int device;
+  kk::Device dev;
+  Layout L;
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  unsigned* counter = nullptr;  // router last-block ticket, self-resetting
+  std::vector<GraphEntry> graphs;
+  unsigned long long clock = 0;
+  bool timing = false;
+  std::vector<TimingRec> trecs;
+  std::vector<hipEvent_t> tpool;
+};
+
+namespace {
+
+int forced_path() {
+  const char* f = std::getenv("KK_FORCE_PLAN");
+  if (!f || !*f) return -1;
+  if (!std::strcmp(f, "gemv")) return KK_PATH_GEMV;
+  if (!std::strcmp(f, "mfma") || !std::strcmp(f, "splitk")) return KK_PATH_SPLITK_MFMA;
+  return -2;
+}
+
+kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
+  std::memset(p, 0, sizeof *p);
+  const int f = forced_path();
+  if (f == -2) return fail(KK_ERR_INVALID_ARG, "KK_FORCE_PLAN must be 'gemv' or 'mfma'");
+  p->forced = f >= 0;
+  p->path = f >= 0 ? f : (B <= 2 ? KK_PATH_GEMV : KK_PATH_SPLITK_MFMA);
+  p->streams = 2;
+  if (p->path == KK_PATH_GEMV) {
+    if (!kk::gemv_supported(c->shape, B))
+      return fail(KK_ERR_UNSUPPORTED, "GEMV path has no kernels for batch %d of this shape", B);
+    const size_t lds_down = (size_t)(B * c->shape.k + B) * c->shape.I * 4;
+    if ((long)lds_down > c->dev.max_lds)
+      return fail(KK_ERR_UNSUPPORTED, "GEMV down-projection needs %zu B of LDS (device: %d)",
+                  lds_down, c->dev.max_lds);
+    p->oproj_splitk = 1;
+    p->router_splitk = kk::router_gemv_splits(c->shape);
+    p->kernels_per_step = 5;  // oproj, router, shared gate/up, routed gate/up, down+combine
+    return KK_OK;
+  }
+  return fail(KK_ERR_UNSUPPORTED, "the split-K MFMA path (batch %d) is not built in this library",
+              B);
+}
+
+hipEvent_t pool_event(kk_ctx* c) {
+  if (!c->tpool.empty()) {
+    hipEvent_t e = c->tpool.back();
+    c->tpool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// Runs one launch, bracketed by timing events when enabled (never inside a capture).
+template <typename F>
+hipError_t timed(kk_ctx* c, int name, hipStream_t s, F&& launch) {
+  if (!c->timing || capturing(s)) return launch();
+  TimingRec r{name, pool_event(c), pool_event(c)};
+  if (r.a) (void)hipEventRecord(r.a, s);
+  hipError_t e = launch();
+  if (r.b) (void)hipEventRecord(r.b, s);
+  if (r.a && r.b) c->trecs.push_back(r);
+  return e;
+}
+
+struct WsPtrs {
+  float* h32;
+  float* logit_part;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  int32_t* act;
+  int32_t* n_act;
+  float* A;
+  float* As;
+};
+
+WsPtrs carve(const kk_ctx* c, void* ws) {
+  char* b = (char*)ws;
+  const Layout& L = c->L;
+  return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
+                (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
+                (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
+                (float*)(b + L.A),         (float*)(b + L.As)};
+}
+
+kk_status check_common(const kk_ctx* c, int B, void* ws) {
+  if (!c) return fail(KK_ERR_INVALID_ARG, "context is NULL");
+  if (B < 1 || B > c->max_batch)
+    return fail(KK_ERR_INVALID_ARG, "batch %d outside 1..%d (max_batch of this context)", B,
+                c->max_batch);
+  if (!ws) return fail(KK_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", c->L.total);
+  if (misaligned(ws, 256)) return fail(KK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != c->device)
+    return fail(KK_ERR_INVALID_ARG, "current device %d is not the context's device %d", dev,
+                c->device);
+  return KK_OK;
+}
+
+#define KK_PTR(p, name)                                                            \
+  do {                                                                             \
+    if (!(p)) return fail(KK_ERR_INVALID_ARG, "%s is NULL", name);                 \
+    if (misaligned(p)) return fail(KK_ERR_INVALID_ARG, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define KK_HIP(expr, what)                      \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+// ---- step pieces (GEMV path) ----------------------------------------------------------
+kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h32, void* h_out,
+                        hipStream_t s) {
+  KK_HIP(timed(c, K_OPROJ, s,
+               [&] { return kk::launch_oproj_gemv(c->shape, c->dev, B, x, r, c->w.w_o, h32, h_out, s); }),
+         "oproj launch");
+  return KK_OK;
+}
+
+kk_status enqueue_router(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                         float* logit_part, hipStream_t s) {
+  KK_HIP(timed(c, K_ROUTER, s,
+               [&] {
+                 return kk::launch_router_gemv(c->shape, c->dev, B, h32, c->w.w_r, c->w.bias,
+                                               logit_part, c->counter, rt, s);
+               }),
+         "router launch");
+  return KK_OK;
+}
+
+// Routed experts on s, shared expert on the auxiliary stream, combine on s.
+kk_status enqueue_experts(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                          const WsPtrs& p, void* out, hipStream_t s, bool fork_here) {
+  if (fork_here) {
+    KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
+    KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
+    KK_HIP(timed(c, K_GU_SHARED, c->aux,
+                 [&] {
+                   return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt,
+                                                 p.As, c->aux);
+                 }),
+           "shared gate/up launch");
+    KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
+  }
+  KK_HIP(timed(c, K_GU_ROUTED, s,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A, s);
+               }),
+         "routed gate/up launch");
+  KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
+  KK_HIP(timed(c, K_DOWN, s,
+               [&] {
+                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
+                                                     c->w.ws2, rt, h32, out, s);
+               }),
+         "down+combine launch");
+  return KK_OK;
+}
+
+kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
+                        float* gate, void* ws, hipStream_t s) {
+  WsPtrs p = carve(c, ws);
+  kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
+                 p.inv_perm, p.act, p.n_act};
+  kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, s);
+  if (st != KK_OK) return st;
+  // shared expert forks right after the o-proj and overlaps the router + routed experts
+  KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
+  KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
+  KK_HIP(timed(c, K_GU_SHARED, c->aux,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, p.h32, c->w.ws13, true, rt,
+                                               p.As, c->aux);
+               }),
+         "shared gate/up launch");
+  KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
+  st = enqueue_router(c, B, p.h32, rt, p.logit_part, s);
+  if (st != KK_OK) return st;
+  return enqueue_experts(c, B, p.h32, rt, p, out, s, false);
+}
+
+void destroy_graphs(kk_ctx* c) {
+  for (auto& g : c->graphs) (void)hipGraphExecDestroy(g.exec);
+  c->graphs.clear();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kk_status_string(kk_status s) {
+  switch (s) {
+    case KK_OK: return "KK_OK";
+    case KK_ERR_INVALID_ARG: return "KK_ERR_INVALID_ARG";
+    case KK_ERR_UNSUPPORTED: return "KK_ERR_UNSUPPORTED";
+    case KK_ERR_WORKSPACE: return "KK_ERR_WORKSPACE";
+    case KK_ERR_HIP: return "KK_ERR_HIP";
+  }
+  return "KK_ERR_UNKNOWN";
+}
+
+const char* kk_last_error(void) { return g_err.c_str(); }
+
+kk_status kk_validate(const kk_config* cfg, int32_t max_batch) {
+  try {
+    return validate_cfg(cfg, max_batch);
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_validate");
+  }
+}
+
+size_t kk_workspace_bytes(const kk_config* cfg, int32_t max_batch) {
+  if (validate_cfg(cfg, max_batch) != KK_OK) return 0;
+  return make_layout(*cfg, max_batch).total;
+}
+
+kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch, kk_ctx** out) {
+  try {
+    if (!out) return fail(KK_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    kk_status st = validate_cfg(cfg, max_batch);
+    if (st != KK_OK) return st;
+    if (!w) return fail(KK_ERR_INVALID_ARG, "weights is NULL");
+    KK_PTR(w->w_o, "w_o");
+    KK_PTR(w->w_r, "w_r");
+    KK_PTR(w->router_bias, "router_bias");
+    KK_PTR(w->w13, "w13");
+    KK_PTR(w->w2, "w2");
+    KK_PTR(w->ws13, "ws13");
+    KK_PTR(w->ws2, "ws2");
+    kk_ctx* c = new kk_ctx();
+    c->cfg = *cfg;
+    c->shape = to_shape(*cfg);
+    c->w = kk::Weights{w->w_o, w->w_r, w->router_bias, w->w13, w->w2, w->ws13, w->ws2};
+    c->max_batch = max_batch;
+    c->L = make_layout(*cfg, max_batch);
+    auto bail = [&](hipError_t e, const char* what) {
+      kk_destroy(c);
+      return hip_fail(e, what);
+    };
+    hipError_t e = hipGetDevice(&c->device);
+    if (e != hipSuccess) return bail(e, "hipGetDevice");
+    int ncu = 0, lds = 0;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device);
+    if (e != hipSuccess) return bail(e, "CU count");
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
+    if (e != hipSuccess) return bail(e, "LDS size");
+    c->dev = kk::Device{ncu, lds};
+    e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
+    if (e != hipSuccess) return bail(e, "aux stream");
+    e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
+    if (e != hipSuccess) return bail(e, "fork event");
+    e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
+    if (e != hipSuccess) return bail(e, "join event");
+    e = hipMalloc((void**)&c->counter, 256);
+    if (e != hipSuccess) return bail(e, "counter buffer");
+    e = hipMemset(c->counter, 0, 256);
+    if (e != hipSuccess) return bail(e, "counter clear");
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return bail(e, "create sync");
+    *out = c;
+    return KK_OK;
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_create");
+  }
+}
+
+kk_status kk_destroy(kk_ctx* c) {
+  if (!c) return KK_OK;
+  if (c->aux) (void)hipStreamSynchronize(c->aux);
+  destroy_graphs(c);
+  for (auto& r : c->trecs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto ev : c->tpool) (void)hipEventDestroy(ev);
+  if (c->counter) (void)hipFree(c->counter);
+  if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
+  if (c->ev_join) (void)hipEventDestroy(c->ev_join);
+  if (c->aux) (void)hipStreamDestroy(c->aux);
+  delete c;
+  return KK_OK;
+}
+
+kk_status kk_query_plan(const kk_ctx* c, int32_t B, kk_plan* out) {
+  if (!c || !out) return fail(KK_ERR_INVALID_ARG, "NULL argument");
+  if (B < 1 || B > c->max_batch) return fail(KK_ERR_INVALID_ARG, "batch %d outside 1..%d", B, c->max_batch);
+  return plan_for(c, B, out);
+}
+
+kk_status kk_oproj_residual(kk_ctx* c, int32_t B, const void* x, const void* resid, float* h32,
+                            void* h_out, void* ws, kk_stream stream) {
+  try {
+    kk_status st = check_common(c, B, ws);
+    if (st != KK_OK) return st;
+    KK_PTR(x, "x");
+    KK_PTR(resid, "resid");
+    KK_PTR(h32, "h32");
+    if (h_out && misaligned(h_out)) return fail(KK_ERR_INVALID_ARG, "h_out is not 16-byte aligned");
+    kk_plan plan;
+    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    return enqueue_oproj(c, B, x, resid, h32, h_out, (hipStream_t)stream);
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_oproj_residual");
+  }
+}
+
+kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_idx,
+                         float* topk_gate, int32_t* expert_offsets, int32_t* perm, void* ws,
+                         kk_stream stream) {
+  try {
+    kk_status st = check_common(c, B, ws);
+    if (st != KK_OK) return st;
+    KK_PTR(h32, "h32");
+    KK_PTR(topk_idx, "topk_idx");
+    KK_PTR(topk_gate, "topk_gate");
+    KK_PTR(expert_offsets, "expert_offsets");
+    KK_PTR(perm, "perm");
+    kk_plan plan;
+    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    WsPtrs p = carve(c, ws);
+    kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
+    return enqueue_router(c, B, h32, rt, p.logit_part, (hipStream_t)stream);
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_router_topk");
+  }
+}
+
+kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* topk_idx,
+                        const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
+                        void* out, void* ws, kk_stream stream) {
+  try {
+    kk_status st = check_common(c, B, ws);
+    if (st != KK_OK) return st;
+    KK_PTR(h32, "h32");
+    KK_PTR(topk_idx, "topk_idx");
+    KK_PTR(topk_gate, "topk_gate");
+    KK_PTR(expert_offsets, "expert_offsets");
+    KK_PTR(perm, "perm");
+    KK_PTR(out, "out");
+    kk_plan plan;
+    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    WsPtrs p = carve(c, ws);
+    kk::Routing rt{(int32_t*)topk_idx, (float*)topk_gate, (int32_t*)expert_offsets,
+                   (int32_t*)perm, p.inv_perm, p.act, p.n_act};
+    KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
+           "moe prep launch");
+    return enqueue_experts(c, B, h32, rt, p, out, s, true);
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_moe_decode");
+  }
+}
+
+kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid, void* out,
+                          int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
+                          uint32_t flags) {
+  try {
+    kk_status st = check_common(c, B, ws);
+    if (st != KK_OK) return st;
+    KK_PTR(x, "x");
+    KK_PTR(resid, "resid");
+    KK_PTR(out, "out");
+    if (topk_idx && misaligned(topk_idx)) return fail(KK_ERR_INVALID_ARG, "topk_idx misaligned");
+    if (topk_gate && misaligned(topk_gate)) return fail(KK_ERR_INVALID_ARG, "topk_gate misaligned");
+    if (flags & ~KK_GRAPH) return fail(KK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    kk_plan plan;
+    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!(flags & KK_GRAPH)) return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s);
+    if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
+    ++c->clock;
+    for (auto& g : c->graphs) {
+      if (g.B == B && g.x == x && g.r == resid && g.out == out && g.idx == topk_idx &&
+          g.gate == topk_gate && g.ws == ws && g.stream == s) {
+        g.uses = c->clock;
+        KK_HIP(hipGraphLaunch(g.exec, s), "graph launch");
+        return KK_OK;
+      }
+    }
+    if (c->graphs.size() >= 16) {  // evict the least recently used graph
+      size_t lru = 0;
+      for (size_t i = 1; i < c->graphs.size(); ++i)
+        if (c->graphs[i].uses < c->graphs[lru].uses) lru = i;
+      (void)hipGraphExecDestroy(c->graphs[lru].exec);
+      c->graphs.erase(c->graphs.begin() + lru);
+    }
+    KK_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
+    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s);
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &graph);
+    if (st != KK_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st;
+    }
+    if (e != hipSuccess) return hip_fail(e, "end capture");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+    c->graphs.push_back(GraphEntry{B, x, resid, out, topk_idx, topk_gate, ws, s, exec, c->clock});
+    KK_HIP(hipGraphLaunch(exec, s), "graph launch");
+    return KK_OK;
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_layer_decode");
+  }
+}
+
+kk_status kk_set_kernel_timing(kk_ctx* c, int32_t enable) {
+  if (!c) return fail(KK_ERR_INVALID_ARG, "context is NULL");
+  c->timing = enable != 0;
+  return KK_OK;
+}
+
+kk_status kk_read_kernel_timing(kk_ctx* c, const char** names, float* ms, int32_t cap,
+                                int32_t* count) {
+  if (!c || !count) return fail(KK_ERR_INVALID_ARG, "NULL argument");
+  int n = 0;
+  for (auto& r : c->trecs) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(KK_ERR_HIP, "timing event sync");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) t = -1.f;
+    if (n < cap) {
+      if (names) names[n] = kernel_names[r.name];
+      if (ms) ms[n] = t;
+    }
+    ++n;
+    c->tpool.push_back(r.a);
+    c->tpool.push_back(r.b);
+  }
+  c->trecs.clear();
+  *count = n;
+  return KK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+// Device helpers shared by the kernels of the decode-layer step (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kk {
+
+constexpr int kWave = 64;
+
+// One 16-byte chunk of a weight row (a native vector, so it loads as one dwordx4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element traits of the weight / activation storage type.  A "chunk" is 16 bytes.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bf16 bit patterns
+  static constexpr int EPC = 8;
+  __device__ static __forceinline__ void unpack(const u32x4& w, float (&f)[8]) {
+    f[0] = bf_lo(w.x);
+    f[1] = bf_hi(w.x);
+    f[2] = bf_lo(w.y);
+    f[3] = bf_hi(w.y);
+    f[4] = bf_lo(w.z);
+    f[5] = bf_hi(w.z);
+    f[6] = bf_lo(w.w);
+    f[7] = bf_hi(w.w);
+  }
+  __device__ static __forceinline__ float load(const uint16_t* p, size_t i) {
+    return __uint_as_float((uint32_t)p[i] << 16);
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int EPC = 4;
+  __device__ static __forceinline__ void unpack(const u32x4& w, float (&f)[4]) {
+    f[0] = __uint_as_float(w.x);
+    f[1] = __uint_as_float(w.y);
+    f[2] = __uint_as_float(w.z);
+    f[3] = __uint_as_float(w.w);
+  }
+  __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+};
+
+// Sum over the SEG lanes of each aligned lane segment (SEG a power of two <= 64).
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int off = SEG / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, SEG);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Weight-row geometry of a GEMV over rows of CPR 16-byte chunks.  A wave covers RPW rows
+// at once, SEG lanes per row (SEG = 64 for rows of >= 33 chunks); lane `sub` of a segment
+// holds chunks sub, sub + SEG, ... (CPL of them), so every wave-wide load instruction
+// reads whole rows' contiguous 16-byte pieces.
+template <typename T, int CPR>
+struct Geo {
+  static constexpr int EPC = Elem<T>::EPC;
+  static constexpr int SEG = CPR > 32 ? 64 : (CPR > 16 ? 32 : 16);
+  static constexpr int RPW = kWave / SEG;
+  static constexpr int CPL = (CPR + SEG - 1) / SEG;
+  static constexpr int K = CPR * EPC;  // elements per row
+  static constexpr bool EXACT = (CPR % SEG) == 0;
+};
+
+template <typename T, int CPR>
+__device__ __forceinline__ void load_row(const T* __restrict__ row, int sub,
+                                         u32x4 (&w)[Geo<T, CPR>::CPL]) {
+  using G = Geo<T, CPR>;
+  const u32x4* p = reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+  for (int i = 0; i < G::CPL; ++i) {
+    const int c = sub + G::SEG * i;
+    if (G::EXACT || c < CPR)
+      w[i] = __builtin_nontemporal_load(p + c);
+    else
+      w[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Lane-partial dot of the loaded row chunks with an fp32 activation row held in LDS.
+template <typename T, int CPR>
+__device__ __forceinline__ float dot_lane(const u32x4 (&w)[Geo<T, CPR>::CPL], const float* act,
+                                          int sub) {
+  using G = Geo<T, CPR>;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::CPL; ++i) {
+    const int c = sub + G::SEG * i;
+    if (G::EXACT || c < CPR) {
+      float f[G::EPC];
+      Elem<T>::unpack(w[i], f);
+      const float4* a = reinterpret_cast<const float4*>(act + c * G::EPC);
+#pragma unroll
+      for (int q = 0; q < G::EPC / 4; ++q) {
+        const float4 av = a[q];
+        acc = fmaf(f[4 * q + 0], av.x, acc);
+        acc = fmaf(f[4 * q + 1], av.y, acc);
+        acc = fmaf(f[4 * q + 2], av.z, acc);
+        acc = fmaf(f[4 * q + 3], av.w, acc);
+      }
+    }
+  }
+  return acc;
+}
+
+// Gate and up rows against the same activation row: each activation chunk is read from
+// LDS once and feeds both sums.
+template <typename T, int CPR>
+__device__ __forceinline__ void dot2_lane(const u32x4 (&wa)[Geo<T, CPR>::CPL],
+                                          const u32x4 (&wb)[Geo<T, CPR>::CPL], const float* act,
+                                          int sub, float& sa, float& sb) {
+  using G = Geo<T, CPR>;
+  float a0 = 0.f, b0 = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::CPL; ++i) {
+    const int c = sub + G::SEG * i;
+    if (G::EXACT || c < CPR) {
+      float fa[G::EPC], fb[G::EPC];
+      Elem<T>::unpack(wa[i], fa);
+      Elem<T>::unpack(wb[i], fb);
+      const float4* a = reinterpret_cast<const float4*>(act + c * G::EPC);
+#pragma unroll
+      for (int q = 0; q < G::EPC / 4; ++q) {
+        const float4 av = a[q];
+        a0 = fmaf(fa[4 * q + 0], av.x, a0);
+        b0 = fmaf(fb[4 * q + 0], av.x, b0);
+        a0 = fmaf(fa[4 * q + 1], av.y, a0);
+        b0 = fmaf(fb[4 * q + 1], av.y, b0);
+        a0 = fmaf(fa[4 * q + 2], av.z, a0);
+        b0 = fmaf(fb[4 * q + 2], av.z, b0);
+        a0 = fmaf(fa[4 * q + 3], av.w, a0);
+        b0 = fmaf(fb[4 * q + 3], av.w, b0);
+      }
+      // keep the LDS reads chunk by chunk: hoisting them all would double the live registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  sa = a0;
+  sb = b0;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace kk

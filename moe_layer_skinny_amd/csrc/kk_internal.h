@@ -1,0 +1,72 @@
+// Internal interface between the host API (kk_api.cpp) and the kernels (kk_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kk {
+
+struct Shape {
+  int H, Ko, E, k, I, Is;
+  int dtype;  // 0 fp32, 1 bf16
+  float routed_scale;
+};
+
+struct Weights {
+  const void* w_o;
+  const void* w_r;
+  const float* bias;
+  const void* w13;
+  const void* w2;
+  const void* ws13;
+  const void* ws2;
+};
+
+// Routing tables on the device.  topk_* and offsets/perm may be caller buffers.
+struct Routing {
+  int32_t* topk_idx;   // [B][k]
+  float* topk_gate;    // [B][k]
+  int32_t* offsets;    // [E+1]
+  int32_t* perm;       // [B*k]  position -> slot
+  int32_t* inv_perm;   // [B*k]  slot -> position
+  int32_t* act;        // [E]    active experts, ascending
+  int32_t* n_act;      // [1]
+};
+
+// Launch configuration facts gathered once per context.
+struct Device {
+  int num_cu;
+  int max_lds;  // bytes of LDS one block may use
+};
+
+// ---- GEMV path (batch 1..2) ----------------------------------------------------------
+// Each returns hipSuccess or the launch error.  `unsupported` is set when no kernel
+// instance exists for the shape (checked by kk_validate before any launch).
+bool gemv_supported(const Shape& s, int B);
+
+hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void* x, const void* r,
+                             const void* w_o, float* h32, void* h_out, hipStream_t st);
+
+// Router logits (split-K partials) + last-block top-k, gates and routing tables.
+hipError_t launch_router_gemv(const Shape& s, const Device& d, int B, const float* h32,
+                              const void* w_r, const float* bias, float* partials,
+                              unsigned* counter, const Routing& rt, hipStream_t st);
+int router_gemv_splits(const Shape& s);
+
+// Routed gate/up over the active experts (act/n_act) or the shared expert (shared=true):
+// A[position][i] = silu(W1[i] . u_t) * (W3[i] . u_t), t = token of the position.
+hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const float* u,
+                              const void* w13, bool shared, const Routing& rt, float* A,
+                              hipStream_t st);
+
+// out[t][n] = h32[t][n] + sum_positions gate * (W2_e[n] . A[p]) + Ws2[n] . As[t]
+hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
+                                    const float* As, const void* w2, const void* ws2,
+                                    const Routing& rt, const float* h32, void* out,
+                                    hipStream_t st);
+
+// act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
+hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
+
+}  // namespace kk

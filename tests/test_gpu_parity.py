@@ -1,0 +1,186 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Order follows "confirm the optimized path runs, then compare outputs and persistent state"
+("Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Deciding whether
+the work applies"): plan checks first, then per-op and whole-step parity, then replay
+determinism and weight checksums.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_common import (as_f64_out, assert_close, assert_routing_equal, gpu_layer, log,
+                              oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+GEMV_CASES = [("tiny_fp32", 1), ("full_b1", 1), ("tp_rank", 1), ("tp_rank", 2)]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bufs(cfg, B):
+    torch = _torch()
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    return {
+        "h32": torch.empty(B, cfg.hidden, dtype=torch.float32, device="cuda"),
+        "h_out": torch.empty(B, cfg.hidden, dtype=dt, device="cuda"),
+        "out": torch.empty(B, cfg.hidden, dtype=dt, device="cuda"),
+        "idx": torch.full((B, cfg.top_k), -1, dtype=torch.int32, device="cuda"),
+        "gate": torch.zeros(B, cfg.top_k, dtype=torch.float32, device="cuda"),
+        "offsets": torch.full((cfg.n_experts + 1,), -1, dtype=torch.int32, device="cuda"),
+        "perm": torch.full((B * cfg.top_k,), -1, dtype=torch.int32, device="cuda"),
+    }
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tp_rank", "full_b1"])
+def test_device_fill_matches_host_generator(name):
+    log(f"[fill] {name}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, w, _ = gpu_layer(name)
+    H, I = cfg.hidden, cfg.inter
+    checks = [("w_o", 0, 4096), ("w_r", 1000, 4096), ("ws2", 0, 2048)]
+    n13 = 2 * I * H
+    for e in (0, cfg.n_experts // 2, cfg.n_experts - 1):
+        checks.append(("w13", e * n13 + n13 - 4096, 4096))
+    for name_, first, count in checks:
+        _, tid, sigma = synth.weight_spec(cfg)[name_]
+        host = synth.host_stream(count, cfg.layer_seed, tid, sigma, cfg.dtype, first=first)
+        dev = sd.to_host_bits(w[name_].reshape(-1)[first:first + count])
+        assert np.array_equal(dev, host), name_
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,B", GEMV_CASES)
+def test_plan_is_gemv_and_visible(name, B):
+    log(f"[plan] {name} B={B}")
+    _, _, L = gpu_layer(name)
+    p = L.query_plan(B)
+    assert p["path_name"] == "gemv" and p["forced"] == 0
+    assert p["kernels_per_step"] == 5 and p["streams"] == 2
+
+
+@pytest.mark.parametrize("name,B", GEMV_CASES)
+def test_per_op_parity(name, B):
+    log(f"[ops] {name} B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(name)
+    ref = oracle_step(name, B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.oproj_residual(B, x, r, b["h32"], ws, h_out=b["h_out"], stream=s)
+        L.router_topk(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], ws, stream=s)
+        L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws, stream=s)
+    s.synchronize()
+    assert_close(b["h32"].cpu().numpy().astype(np.float64), ref["h"], "h32")
+    assert_close(as_f64_out(b["h_out"]), ref["h"], "h_out")
+    got = {"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy(),
+           "offsets": b["offsets"].cpu().numpy(), "perm": b["perm"].cpu().numpy()}
+    assert_routing_equal(got, ref, B, cfg.top_k, "router")
+    rep = assert_close(as_f64_out(b["out"]), ref["out"], "moe out")
+    log(f"[ops] {name} B={B} out: {rep}")
+
+
+@pytest.mark.parametrize("name,B", GEMV_CASES)
+def test_layer_parity_eager_and_graph(name, B):
+    log(f"[layer] {name} B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(name)
+    ref = oracle_step(name, B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s)
+    s.synchronize()
+    eager = b["out"].clone()
+    rep = assert_close(as_f64_out(eager), ref["out"], "layer out")
+    assert_routing_equal({"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy()},
+                         ref, B, cfg.top_k, "layer routing")
+    log(f"[layer] {name} B={B} eager out: {rep}")
+    for rep_i in range(3):
+        b["out"].zero_()
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s, graph=True)
+        s.synchronize()
+        assert torch.equal(b["out"], eager), f"graph replay {rep_i} differs from eager"
+    # routing outputs are optional
+    with torch.cuda.stream(s):
+        L.layer_decode(B, x, r, b["out"], ws, stream=s)
+    s.synchronize()
+    assert torch.equal(b["out"], eager)
+
+
+def test_batch_invariance_of_routing():
+    log("[batch-invariance] tp_rank")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer("tp_rank")
+    outs = {}
+    for B in (1, 2):
+        x, r, _, _ = sd.device_tokens(cfg, B)
+        b = _bufs(cfg, B)
+        ws = L.new_workspace()
+        L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"])
+        torch.cuda.synchronize()
+        outs[B] = (b["idx"].cpu().numpy(), as_f64_out(b["out"]))
+    np.testing.assert_array_equal(outs[1][0][0], outs[2][0][0])
+    np.testing.assert_allclose(outs[1][1][0], outs[2][1][0], rtol=2e-2, atol=1e-2)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tp_rank"])
+def test_weights_unchanged_after_steps(name):
+    log(f"[state] {name}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, w, L = gpu_layer(name)
+
+    def digest():
+        return {k: int(v.contiguous().view(torch.int16 if v.element_size() == 2 else torch.int32)
+                       .to(torch.int64).sum().item()) for k, v in w.items()}
+
+    before = digest()
+    B = cfg.max_batch if cfg.max_batch <= 2 else 2
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    for _ in range(20):
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, stream=s, graph=True)
+    s.synchronize()
+    assert digest() == before
+
+
+def test_device_side_argument_errors():
+    log("[errors] tp_rank")
+    torch = _torch()
+    from moe_layer_skinny_amd import kk
+    cfg, _, L = gpu_layer("tp_rank")
+    b = _bufs(cfg, 2)
+    ws = L.new_workspace()
+    x = torch.zeros(2, cfg.oproj_in, dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros(2, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kk.KKError) as e:
+        L.layer_decode(65, x, r, b["out"], ws)
+    assert e.value.status == kk.KK_ERR_INVALID_ARG
+    xm = torch.zeros(2 * cfg.oproj_in + 8, dtype=torch.bfloat16, device="cuda")[1:]
+    with pytest.raises(kk.KKError) as e:
+        L.layer_decode(1, xm, r, b["out"], ws)
+    assert e.value.status == kk.KK_ERR_INVALID_ARG
+    with pytest.raises(kk.KKError) as e:
+        L.layer_decode(1, x, r, b["out"], None)
+    assert e.value.status == kk.KK_ERR_WORKSPACE
+    with pytest.raises(kk.KKError) as e:
+        L.layer_decode(1, x, r, b["out"], ws, stream=0, graph=True)
+    assert e.value.status == kk.KK_ERR_INVALID_ARG
