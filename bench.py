@@ -1,15 +1,17 @@
 """Benchmark: one decode-layer step (o-proj + residual, router/top-k, routed experts || shared
-expert, combine) per timed step, on one MI355X, through the C ABI with a replayed HIP graph.
+expert, combine) per timed step, on one MI355X, through the C ABI.
 
 Prints ONE JSON line on stdout (everything else goes to stderr).  Default workload: the
 full-size layer (hidden 7168, 384 experts top-8, SwiGLU intermediate 2048, bf16 weights,
 ~34 GB of routed experts resident in HBM) at batch 1.
 
 Timing protocol: weights and inputs are resident in HBM before timing starts.  Each timed
-step is {flush the last-level cache by streaming a 1 GiB buffer; event A; graph launch;
-event B} on one stream, so every weight byte is fetched from HBM; value = median(B - A).
-The whole bracket (barrier + synchronize on both sides, flushes included) is reported as
-wall_ms_per_iter.  A "warm" figure (back-to-back steps, no flush) is reported separately and
+step is {flush the last-level cache by streaming a 1 GiB buffer; event A; the step's
+launches; event B} on one stream, so every weight byte is fetched from HBM; value = median(B - A).
+Steps are submitted as eager launches on one stream by default (on this GPU a replayed HIP
+graph costs more per kernel node than an eager launch); the graph-replay time is reported
+beside it.  The whole bracket (synchronize on both sides, flushes included) is reported as
+wall_ms_per_iter_incl_flush.  A "warm" figure (back-to-back steps, no flush) is reported separately and
 never used for the roofline fraction.
 """
 from __future__ import annotations
@@ -88,6 +90,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=1)
     ap.add_argument("--no-timing-pass", action="store_true")
+    ap.add_argument("--mode", choices=["eager", "graph"], default="eager",
+                    help="how each timed step is submitted (eager: 4 launches on one stream)")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="shared expert's gate/up on the auxiliary stream")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,8 +125,9 @@ def main():
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
     s = torch.cuda.Stream(dev)
 
-    def step():
-        layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=True)
+    def step(mode=args.mode):
+        layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=(mode == "graph"),
+                           two_stream=args.two_stream)
 
     with torch.cuda.stream(s):
         for _ in range(args.warmup):
@@ -147,6 +154,22 @@ def main():
     med = statistics.median(us)
     p10, p90 = us[int(0.1 * (len(us) - 1))], us[int(0.9 * (len(us) - 1))]
 
+    # ---- the other submission mode, same protocol (reported, not the headline)
+    other = "graph" if args.mode == "eager" else "eager"
+    with torch.cuda.stream(s):
+        step(other)
+    s.synchronize()
+    oevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    with torch.cuda.stream(s):
+        for a, b in oevs:
+            flush.add_(1.0)
+            a.record(s)
+            step(other)
+            b.record(s)
+    s.synchronize()
+    other_us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in oevs)
+
     # ---- warm figure: back-to-back steps, no flush (cache-assisted; not the headline)
     wa, wb_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(s):
@@ -165,7 +188,8 @@ def main():
         with torch.cuda.stream(s):
             for _ in range(args.steps):
                 flush.add_(1.0)
-                layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=False)
+                layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=False,
+                                   two_stream=args.two_stream)
         s.synchronize()
         recs = layer.read_kernel_timing()
         layer.set_kernel_timing(False)
@@ -201,6 +225,8 @@ def main():
         "p10_us": round(p10, 3), "p90_us": round(p90, 3),
         "wall_ms_per_iter_incl_flush": round(wall * 1e3 / args.steps, 4),
         "warm_us_per_step_no_flush": round(warm_us, 3),
+        "submission": args.mode + ("+two_stream" if args.two_stream else ""),
+        f"{other}_us_per_step": round(other_us, 3),
         "kernel_us_eager": {k: round(v, 3) for k, v in kernels.items()},
         "roofline": roofline,
     }

@@ -68,7 +68,9 @@ typedef enum {
 } kk_path;
 
 /* kk_layer_decode flags */
-#define KK_GRAPH 1u /* capture the step once per (B, buffers, stream) and replay it */
+#define KK_GRAPH 1u      /* capture the step once per (B, buffers, stream, flags), replay it */
+#define KK_TWO_STREAM 2u /* shared expert's gate/up on the context's auxiliary stream instead
+                            of inside the router launch (kept for comparison) */
 
 typedef struct {
   int32_t hidden;       /* H  */
@@ -96,8 +98,8 @@ typedef struct {
   int32_t forced;           /* 1 if the KK_FORCE_PLAN environment variable chose it */
   int32_t oproj_splitk;     /* K splits of the o-proj (1 on the GEMV path) */
   int32_t router_splitk;    /* K splits of the router logits */
-  int32_t kernels_per_step; /* kernel launches of one kk_layer_decode step */
-  int32_t streams;          /* streams one step uses (2: main + shared expert) */
+  int32_t kernels_per_step; /* kernel launches of one default kk_layer_decode step */
+  int32_t streams;          /* streams the default step uses (1; 2 with KK_TWO_STREAM) */
 } kk_plan;
 
 typedef struct kk_ctx kk_ctx;
@@ -130,18 +132,19 @@ kk_status kk_router_topk(kk_ctx* ctx, int32_t B, const float* h32, int32_t* topk
                          float* topk_gate, int32_t* expert_offsets, int32_t* perm, void* ws,
                          kk_stream stream);
 
-/* Routed experts (each selected expert's weights read once) on `stream`, the shared expert
- * on the context's auxiliary stream, and the combine out = h32 + sum g y + y_shared (RNE to
- * the config dtype).  Routing tables as written by kk_router_topk.
+/* Routed experts (each selected expert's weights read once), the shared expert, and the
+ * combine out = h32 + sum g y + y_shared (RNE to the config dtype), all on `stream`.
+ * Routing tables as written by kk_router_topk for the same B; tables that are not a valid
+ * routing leave the routed part out (no out-of-bounds access) -- undefined output.
  * "Recovering time between operators": selected experts; shared expert on another stream. */
 kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t* topk_idx,
                         const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
                         void* out, void* ws, kk_stream stream);
 
-/* The whole step: o-proj + residual, router, routed experts || shared expert, combine.
- * topk_idx / topk_gate are optional copies of the routing (nullable).  With KK_GRAPH the
- * step is captured into a HIP graph on first use for these (B, pointers, stream) and
- * replayed afterwards (one host->device submission per step). */
+/* The whole step: o-proj + residual, router || shared expert gate/up, routed experts,
+ * down-projection + combine (four launches on `stream`).  topk_idx / topk_gate are optional
+ * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
+ * first use for these (B, pointers, stream, flags) and replayed afterwards. */
 kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,
                           int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
                           uint32_t flags);

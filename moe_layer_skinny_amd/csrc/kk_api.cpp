@@ -119,9 +119,10 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
   return KK_OK;
 }
 
-const char* kernel_names[] = {"oproj_gemv", "router_gemv", "gateup_gemv_shared",
-                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep"};
-enum KName { K_OPROJ, K_ROUTER, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP };
+const char* kernel_names[] = {"oproj_gemv",         "router_gemv",       "gateup_gemv_shared",
+                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep",
+                              "router_shared_gemv"};
+enum KName { K_OPROJ, K_ROUTER, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_ROUTER_SHARED };
 
 struct TimingRec {
   int name;
@@ -130,6 +131,7 @@ struct TimingRec {
 
 struct GraphEntry {
   int B;
+  uint32_t flags;
   const void *x, *r, *out, *idx, *gate, *ws;
   hipStream_t stream;
   hipGraphExec_t exec;
@@ -148,7 +150,7 @@ struct kk_ctx {
   Layout L;
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  unsigned* counter = nullptr;  // router last-block ticket, self-resetting
+  unsigned* counter = nullptr;  // arrival counters (kk::kArriveCounters words), self-resetting
   std::vector<GraphEntry> graphs;
   unsigned long long clock = 0;
   bool timing = false;
@@ -182,7 +184,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
     p->router_splitk = kk::router_gemv_splits(c->shape);
-    p->kernels_per_step = 5;  // oproj, router, shared gate/up, routed gate/up, down+combine
+    // oproj, router || shared gate/up, routed gate/up, down + combine -- one stream
+    p->kernels_per_step = 4;
+    p->streams = 1;
     return KK_OK;
   }
   return fail(KK_ERR_UNSUPPORTED, "the split-K MFMA path (batch %d) is not built in this library",
@@ -277,36 +281,34 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
 }
 
 kk_status enqueue_router(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
-                         float* logit_part, hipStream_t s) {
-  KK_HIP(timed(c, K_ROUTER, s,
+                         float* logit_part, const void* ws13, float* As, hipStream_t s) {
+  KK_HIP(timed(c, ws13 ? K_ROUTER_SHARED : K_ROUTER, s,
                [&] {
                  return kk::launch_router_gemv(c->shape, c->dev, B, h32, c->w.w_r, c->w.bias,
-                                               logit_part, c->counter, rt, s);
+                                               logit_part, c->counter, rt, ws13, As, s);
                }),
          "router launch");
   return KK_OK;
 }
 
-// Routed experts on s, shared expert on the auxiliary stream, combine on s.
-kk_status enqueue_experts(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
-                          const WsPtrs& p, void* out, hipStream_t s, bool fork_here) {
-  if (fork_here) {
-    KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
-    KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
-    KK_HIP(timed(c, K_GU_SHARED, c->aux,
-                 [&] {
-                   return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt,
-                                                 p.As, c->aux);
-                 }),
-           "shared gate/up launch");
-    KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
-  }
+kk_status enqueue_shared_gateup(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                                float* As, hipStream_t s) {
+  KK_HIP(timed(c, K_GU_SHARED, s,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt, As, s);
+               }),
+         "shared gate/up launch");
+  return KK_OK;
+}
+
+// Routed gate/up then the fused routed + shared down-projection and combine, on s.
+kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                                     const WsPtrs& p, void* out, hipStream_t s) {
   KK_HIP(timed(c, K_GU_ROUTED, s,
                [&] {
                  return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A, s);
                }),
          "routed gate/up launch");
-  KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
   KK_HIP(timed(c, K_DOWN, s,
                [&] {
                  return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
@@ -317,25 +319,39 @@ kk_status enqueue_experts(kk_ctx* c, int B, const float* h32, const kk::Routing&
 }
 
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
-                        float* gate, void* ws, hipStream_t s) {
+                        float* gate, void* ws, hipStream_t s, bool two_stream) {
   WsPtrs p = carve(c, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act};
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, s);
   if (st != KK_OK) return st;
-  // shared expert forks right after the o-proj and overlaps the router + routed experts
+  if (!two_stream) {
+    // shared expert's gate/up streams inside the router launch, overlapping the top-k
+    st = enqueue_router(c, B, p.h32, rt, p.logit_part, c->w.ws13, p.As, s);
+    if (st != KK_OK) return st;
+    return enqueue_routed_and_combine(c, B, p.h32, rt, p, out, s);
+  }
+  // shared expert's gate/up on the auxiliary stream, joined before the down-projection
   KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
   KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
-  KK_HIP(timed(c, K_GU_SHARED, c->aux,
-               [&] {
-                 return kk::launch_gateup_gemv(c->shape, c->dev, B, p.h32, c->w.ws13, true, rt,
-                                               p.As, c->aux);
-               }),
-         "shared gate/up launch");
-  KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
-  st = enqueue_router(c, B, p.h32, rt, p.logit_part, s);
+  st = enqueue_shared_gateup(c, B, p.h32, rt, p.As, c->aux);
   if (st != KK_OK) return st;
-  return enqueue_experts(c, B, p.h32, rt, p, out, s, false);
+  KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
+  st = enqueue_router(c, B, p.h32, rt, p.logit_part, nullptr, nullptr, s);
+  if (st != KK_OK) return st;
+  KK_HIP(timed(c, K_GU_ROUTED, s,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, p.h32, c->w.w13, false, rt, p.A, s);
+               }),
+         "routed gate/up launch");
+  KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
+  KK_HIP(timed(c, K_DOWN, s,
+               [&] {
+                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
+                                                     c->w.ws2, rt, p.h32, out, s);
+               }),
+         "down+combine launch");
+  return KK_OK;
 }
 
 void destroy_graphs(kk_ctx* c) {
@@ -411,9 +427,9 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     if (e != hipSuccess) return bail(e, "fork event");
     e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "join event");
-    e = hipMalloc((void**)&c->counter, 256);
+    e = hipMalloc((void**)&c->counter, kk::kArriveCounters * sizeof(unsigned));
     if (e != hipSuccess) return bail(e, "counter buffer");
-    e = hipMemset(c->counter, 0, 256);
+    e = hipMemset(c->counter, 0, kk::kArriveCounters * sizeof(unsigned));
     if (e != hipSuccess) return bail(e, "counter clear");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return bail(e, "create sync");
@@ -479,7 +495,7 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     WsPtrs p = carve(c, ws);
     kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
-    return enqueue_router(c, B, h32, rt, p.logit_part, (hipStream_t)stream);
+    return enqueue_router(c, B, h32, rt, p.logit_part, nullptr, nullptr, (hipStream_t)stream);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_router_topk");
   }
@@ -505,7 +521,9 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
                    (int32_t*)perm, p.inv_perm, p.act, p.n_act};
     KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
            "moe prep launch");
-    return enqueue_experts(c, B, h32, rt, p, out, s, true);
+    st = enqueue_shared_gateup(c, B, h32, rt, p.As, s);
+    if (st != KK_OK) return st;
+    return enqueue_routed_and_combine(c, B, h32, rt, p, out, s);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_moe_decode");
   }
@@ -522,15 +540,17 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     KK_PTR(out, "out");
     if (topk_idx && misaligned(topk_idx)) return fail(KK_ERR_INVALID_ARG, "topk_idx misaligned");
     if (topk_gate && misaligned(topk_gate)) return fail(KK_ERR_INVALID_ARG, "topk_gate misaligned");
-    if (flags & ~KK_GRAPH) return fail(KK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    if (flags & ~(KK_GRAPH | KK_TWO_STREAM))
+      return fail(KK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    const bool two = (flags & KK_TWO_STREAM) != 0;
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!(flags & KK_GRAPH)) return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s);
+    if (!(flags & KK_GRAPH)) return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two);
     if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
     ++c->clock;
     for (auto& g : c->graphs) {
-      if (g.B == B && g.x == x && g.r == resid && g.out == out && g.idx == topk_idx &&
+      if (g.B == B && g.flags == flags && g.x == x && g.r == resid && g.out == out && g.idx == topk_idx &&
           g.gate == topk_gate && g.ws == ws && g.stream == s) {
         g.uses = c->clock;
         KK_HIP(hipGraphLaunch(g.exec, s), "graph launch");
@@ -545,7 +565,7 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
       c->graphs.erase(c->graphs.begin() + lru);
     }
     KK_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
-    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s);
+    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two);
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(s, &graph);
     if (st != KK_OK) {
@@ -557,7 +577,8 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "graph instantiate");
-    c->graphs.push_back(GraphEntry{B, x, resid, out, topk_idx, topk_gate, ws, s, exec, c->clock});
+    c->graphs.push_back(
+        GraphEntry{B, flags, x, resid, out, topk_idx, topk_gate, ws, s, exec, c->clock});
     KK_HIP(hipGraphLaunch(exec, s), "graph launch");
     return KK_OK;
   } catch (...) {

@@ -127,6 +127,40 @@ __device__ __forceinline__ float dot_lane(const u32x4 (&w)[Geo<T, CPR>::CPL], co
   return acc;
 }
 
+// Lane-partial dot of loaded row chunks with an activation row held in registers as raw
+// chunks of the same element type (the lane's own chunk positions).
+template <typename T, int CPR>
+__device__ __forceinline__ float dot_rr(const u32x4 (&w)[Geo<T, CPR>::CPL],
+                                        const u32x4 (&x)[Geo<T, CPR>::CPL], int sub) {
+  using G = Geo<T, CPR>;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::CPL; ++i) {
+    const int c = sub + G::SEG * i;
+    if (G::EXACT || c < CPR) {
+      float f[G::EPC], a[G::EPC];
+      Elem<T>::unpack(w[i], f);
+      Elem<T>::unpack(x[i], a);
+#pragma unroll
+      for (int q = 0; q < G::EPC; ++q) acc = fmaf(f[q], a[q], acc);
+    }
+  }
+  return acc;
+}
+
+// The lane's chunks of one activation row (plain loads: activations are read many times).
+template <typename T, int CPR>
+__device__ __forceinline__ void load_act_chunks(const T* __restrict__ row, int sub,
+                                                u32x4 (&x)[Geo<T, CPR>::CPL]) {
+  using G = Geo<T, CPR>;
+  const u32x4* p = reinterpret_cast<const u32x4*>(row);
+#pragma unroll
+  for (int i = 0; i < G::CPL; ++i) {
+    const int c = sub + G::SEG * i;
+    x[i] = (G::EXACT || c < CPR) ? p[c] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 // Gate and up rows against the same activation row: each activation chunk is read from
 // LDS once and feeds both sums.
 template <typename T, int CPR>
@@ -161,6 +195,38 @@ __device__ __forceinline__ void dot2_lane(const u32x4 (&wa)[Geo<T, CPR>::CPL],
   }
   sa = a0;
   sb = b0;
+}
+
+// Arrival of this block at a one-shot rendezvous of all gridDim.x blocks; returns true in
+// exactly one block, the last to arrive, after which every other block's prior writes are
+// visible to it.  Two levels (8 sub-counters by blockIdx % 8, one per XCD under round-robin
+// dispatch, then a top counter) keep single-address atomic traffic to ~gridDim/8 + 8
+// operations.  Each counter is reset by its last arriver, so the words are zero again when
+// the kernel ends.  ctrs: 9 counters 16 words apart.
+__device__ inline bool last_block_arrive(unsigned* ctrs) {
+  __shared__ int s_last;
+  __threadfence();  // every wave releases its own writes before the block arrives
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int nb = gridDim.x;
+    const int sub = blockIdx.x & 7;
+    const unsigned n_sub = (unsigned)((nb - sub + 7) / 8);
+    const unsigned n_top = (unsigned)(nb < 8 ? nb : 8);
+    int last = 0;
+    if (atomicAdd(&ctrs[16 * (1 + sub)], 1u) == n_sub - 1) {
+      atomicExch(&ctrs[16 * (1 + sub)], 0u);
+      __threadfence();  // carry the sub-group's writes on to the top counter
+      if (atomicAdd(&ctrs[0], 1u) == n_top - 1) {
+        atomicExch(&ctrs[0], 0u);
+        last = 1;
+      }
+    }
+    s_last = last;
+  }
+  __syncthreads();
+  const bool last = s_last != 0;
+  if (last) __threadfence();  // acquire
+  return last;
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }

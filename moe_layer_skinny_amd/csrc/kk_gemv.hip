@@ -1,10 +1,16 @@
 // GEMV path of the decode-layer step (batch 1-2): every weight row is streamed from HBM
-// once with 128-bit non-temporal loads; activations sit in LDS as fp32; each row's dot
-// product is finished with a wavefront shuffle reduction.
+// once with 128-bit non-temporal loads, each row's dot product finished with a wavefront
+// shuffle reduction.  One stream, four launches per step:
+//   1. o-proj + residual                     (activations held in registers)
+//   2. router logits -> top-k/gates/tables   (last block to arrive)  ||  shared gate/up
+//   3. routed gate/up over the active experts
+//   4. routed + shared down-projection fused with the weighted combine
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
-// time between operators": small-matrix projection kernels at batch 1-2, o-proj fused with
-// the residual, router scores, selected experts, shared expert on another stream.
+// time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
+// the residual; the shared expert overlapping routing; fewer launches.  On this GPU a
+// cross-stream fork/join and replayed graph nodes each cost more than a kernel boundary on
+// one stream, so the shared expert's overlap with routing happens inside launch 2.
 #include "kk_common.cuh"
 #include "kk_internal.h"
 #include "kk_topk.cuh"
@@ -12,29 +18,26 @@
 namespace kk {
 namespace {
 
-constexpr int kGemvThreads = 512;  // 8 waves; one persistent block per CU
-constexpr int kGemvWaves = kGemvThreads / kWave;
-
-// Copy n floats (or bf16 -> fp32) from global to LDS with the whole block.
-template <typename T>
-__device__ __forceinline__ void stage_f32(float* dst, const T* __restrict__ src, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = Elem<T>::load(src, i);
-}
+constexpr int kGemvThreads = 512;  // up to 8 waves; persistent blocks
 
 // ------------------------------------------------------------------------------ o-proj
 // h32[t][n] = r[t][n] + sum_k W_o[n][k] x[t][k]; optional h_out = RNE(h32).
+// When they fit (NT * CPL <= 14 chunks) each lane keeps its own chunks of x in registers --
+// the same chunk positions for every row, no LDS and no barrier before the first weight
+// loads; otherwise x is staged in LDS as fp32 while the first rows are in flight.
 template <typename T, int CPR, int NT, int R>
 __global__ __launch_bounds__(kGemvThreads) void oproj_gemv_kernel(
     const T* __restrict__ x, const T* __restrict__ r, const T* __restrict__ w_o,
-    float* __restrict__ h32, T* __restrict__ h_out, int H, int B) {
+    float* __restrict__ h32, T* __restrict__ h_out, int H) {
   using G = Geo<T, CPR>;
-  extern __shared__ float lds[];  // x as fp32 [B][Ko]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr bool kRegs = NT * G::CPL <= 14;
+  extern __shared__ float lds[];  // x as fp32 [NT][Ko] when not in registers
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int sub = lane % G::SEG, seg = lane / G::SEG;
   const int rows_per_unit = G::RPW * R;
   const int units = (H + rows_per_unit - 1) / rows_per_unit;
-  const int stride = gridDim.x * kGemvWaves;
-  int unit = blockIdx.x * kGemvWaves + wave;
+  const int stride = gridDim.x * wpb;
+  int unit = blockIdx.x * wpb + wave;
 
   u32x4 w[R][G::CPL];
   auto issue = [&](int u) {
@@ -48,71 +51,137 @@ __global__ __launch_bounds__(kGemvThreads) void oproj_gemv_kernel(
         for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  stage_f32<T>(lds, x, B * G::K);
-  __syncthreads();
-
-  for (; unit < units; unit += stride) {
+  u32x4 xa[kRegs ? NT : 1][G::CPL];
+  if constexpr (kRegs) {
+    if (unit >= units) return;
     issue(unit);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) load_act_chunks<T, CPR>(x + (size_t)t * G::K, sub, xa[t]);
+  } else {
+    if (unit < units) issue(unit);
+    for (int i = threadIdx.x; i < NT * G::K; i += blockDim.x) lds[i] = Elem<T>::load(x, i);
+    __syncthreads();
+    if (unit >= units) return;
+  }
+
+  while (true) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
       const int n = unit * rows_per_unit + seg + G::RPW * q;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (t < B) {
-          float acc = seg_sum<G::SEG>(dot_lane<T, CPR>(w[q], lds + t * G::K, sub));
-          if (sub == 0 && n < H) {
-            const size_t o = (size_t)t * H + n;
-            const float hv = Elem<T>::load(r, o) + acc;
-            h32[o] = hv;
-            if (h_out) Elem<T>::store(h_out, o, hv);
-          }
+        float part;
+        if constexpr (kRegs)
+          part = dot_rr<T, CPR>(w[q], xa[t], sub);
+        else
+          part = dot_lane<T, CPR>(w[q], lds + t * G::K, sub);
+        const float acc = seg_sum<G::SEG>(part);
+        if (sub == 0 && n < H) {
+          const size_t o = (size_t)t * H + n;
+          const float hv = Elem<T>::load(r, o) + acc;
+          h32[o] = hv;
+          if (h_out) Elem<T>::store(h_out, o, hv);
         }
       }
+    }
+    unit += stride;
+    if (unit >= units) break;
+    __builtin_amdgcn_sched_barrier(0);
+    issue(unit);
+  }
+}
+
+// ------------------------------------------------------------------------------ gate / up
+// One gate/up row pair of one expert for the positions [p0, p1) of that expert:
+// A[p][i] = silu(W1[i] . u_t) * (W3[i] . u_t), u_t an fp32 row in LDS.
+template <typename T, int CPR, int NT>
+__device__ __forceinline__ void gateup_unit(const u32x4 (&wg)[Geo<T, CPR>::CPL],
+                                            const u32x4 (&wu)[Geo<T, CPR>::CPL],
+                                            const float* lds_u, int p0, int p1, int i, int I,
+                                            int k, bool identity_tokens, const Routing& rt,
+                                            float* __restrict__ A, int lane) {
+  using G = Geo<T, CPR>;
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const int p = p0 + q;
+    if (p < p1) {
+      const int t = identity_tokens ? p : rt.perm[p] / k;
+      float z1, z3;
+      dot2_lane<T, CPR>(wg, wu, lds_u + t * G::K, lane, z1, z3);
+      z1 = seg_sum<64>(z1);
+      z3 = seg_sum<64>(z3);
+      if (lane == 0) A[(size_t)p * I + i] = silu_f32(z1) * z3;
     }
   }
 }
 
+template <typename T, int CPR>
+__device__ __forceinline__ void load_pair(const T* __restrict__ w13, int e, int i, int I,
+                                          u32x4 (&wg)[Geo<T, CPR>::CPL],
+                                          u32x4 (&wu)[Geo<T, CPR>::CPL], int lane) {
+  using G = Geo<T, CPR>;
+  const T* g_row = w13 + ((size_t)e * 2 * I + i) * G::K;
+  load_row<T, CPR>(g_row, lane, wg);
+  load_row<T, CPR>(g_row + (size_t)I * G::K, lane, wu);
+}
+
+__device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restrict__ src, int n) {
+  for (int i = threadIdx.x; i < n / 4; i += blockDim.x)
+    reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(src)[i];
+}
+
 // ------------------------------------------------------------------------------ router
-// Logit partials over `splits` K-slices, then the last block to finish runs top-k, gates
-// and the routing tables.  Each wave takes one (expert, slice) unit; h32 is read from L2.
-template <typename T, int CPS, int NT>
-__global__ __launch_bounds__(256) void router_gemv_kernel(
+// Phase 1: logit partials part[s][t][e] over `splits` K-slices (h32 read from L2).
+// Arrival: the last block runs top-k, gates and the routing tables.
+// Phase 2 (ws13 != nullptr): the shared expert's gate/up over all B tokens; each wave's
+// first row pair is requested before phase 1 so HBM streams while the router works.
+template <typename T, int CPS, int CPRH, int NT>
+__global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(
     const float* __restrict__ h32, const T* __restrict__ w_r, const float* __restrict__ bias,
     int H, int E, int k, int B, int splits, float routed_scale, float* __restrict__ part,
-    unsigned* __restrict__ counter, Routing rt) {
+    unsigned* __restrict__ ctrs, Routing rt, const T* __restrict__ ws13, int Is,
+    float* __restrict__ As) {
   using G = Geo<T, CPS>;
+  using GH = Geo<T, CPRH>;
   __shared__ TopkScratch sm;
-  __shared__ int s_last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wpb = blockDim.x >> 6;
+  extern __shared__ float lds[];  // u [B][H] for phase 2
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
+  const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
+  const bool shared = ws13 != nullptr;
+
+  u32x4 wg[GH::CPL], wu[GH::CPL];
+  int su = gw;
+  if (shared && su < Is) load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
+
   const int units = E * splits;
-  for (int unit = blockIdx.x * wpb + wave; unit < units; unit += gridDim.x * wpb) {
+  for (int unit = gw; unit < units; unit += nw) {
     const int e = unit / splits, s = unit - e * splits;
     u32x4 w[G::CPL];
     load_row<T, CPS>(w_r + (size_t)e * H + (size_t)s * G::K, lane, w);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t < B) {
-        const float acc =
-            seg_sum<64>(dot_lane<T, CPS>(w, h32 + (size_t)t * H + (size_t)s * G::K, lane));
-        if (lane == 0) part[((size_t)s * B + t) * E + e] = acc;
-      }
+      const float acc =
+          seg_sum<64>(dot_lane<T, CPS>(w, h32 + (size_t)t * H + (size_t)s * G::K, lane));
+      if (lane == 0) part[((size_t)s * B + t) * E + e] = acc;
     }
   }
-  // Publish the partials, then elect the last block (device-scope release/acquire).
-  __threadfence();
+  if (last_block_arrive(ctrs)) topk_tables(part, splits, bias, B, E, k, routed_scale, rt, sm);
+  if (!shared) return;
+
+  stage_rows_f32(lds, h32, B * GH::K);
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(counter, 1u) == gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  topk_tables(part, splits, bias, B, E, k, routed_scale, rt, sm);
-  if (threadIdx.x == 0) atomicExch(counter, 0u);  // ready for the next launch
+  if (su >= Is) return;
+  while (true) {
+    gateup_unit<T, CPRH, NT>(wg, wu, lds, 0, B, su, Is, k, true, rt, As, lane);
+    su += nw;
+    if (su >= Is) break;
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
+  }
 }
 
 // ------------------------------------------------------------------------------ gate / up
-// A[p][i] = silu(W1_e[i] . u_t) * (W3_e[i] . u_t) for every position p of expert e (token
-// t = perm[p] / k), or for the shared expert (positions = tokens 0..B-1).
+// Routed experts (act / n_act / offsets / perm) or the shared expert (positions = tokens).
 template <typename T, int CPR, int NT>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     const float* __restrict__ u, const T* __restrict__ w13, int I, int k, int B, int shared,
@@ -120,46 +189,31 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   using G = Geo<T, CPR>;
   static_assert(G::SEG == 64, "gate/up rows must span the wave");
   extern __shared__ float lds[];  // u [B][H]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int n = shared ? 1 : *rt.n_act;
   const int units = n * I;
-  const int stride = gridDim.x * kGemvWaves;
-  int unit = blockIdx.x * kGemvWaves + wave;
+  const int stride = gridDim.x * wpb;
+  int unit = blockIdx.x * wpb + wave;
 
   u32x4 wg[G::CPL], wu[G::CPL];
-  auto issue = [&](int un) {
-    const int a = un / I, i = un - a * I;
-    const int e = shared ? 0 : rt.act[a];
-    const T* g_row = w13 + ((size_t)e * 2 * I + i) * G::K;
-    load_row<T, CPR>(g_row, lane, wg);
-    load_row<T, CPR>(g_row + (size_t)I * G::K, lane, wu);
-  };
-  for (int i = threadIdx.x; i < B * G::K / 4; i += blockDim.x)
-    reinterpret_cast<float4*>(lds)[i] = reinterpret_cast<const float4*>(u)[i];
+  auto expert_of = [&](int un) { return shared ? 0 : rt.act[un / I]; };
+  if (unit < units) load_pair<T, CPR>(w13, expert_of(unit), unit % I, I, wg, wu, lane);
+  stage_rows_f32(lds, u, B * G::K);
   __syncthreads();
-
-  for (; unit < units; unit += stride) {
-    issue(unit);
-    const int a = unit / I, i = unit - a * I;
+  if (unit >= units) return;
+  while (true) {
+    const int i = unit % I;
     int p0 = 0, p1 = B;
     if (!shared) {
-      const int e = rt.act[a];
+      const int e = rt.act[unit / I];
       p0 = rt.offsets[e];
       p1 = rt.offsets[e + 1];
     }
-#pragma unroll
-    for (int q = 0; q < NT; ++q) {
-      const int p = p0 + q;
-      if (p < p1) {
-        const int t = shared ? p : rt.perm[p] / k;
-        const float* ut = lds + t * G::K;
-        float z1, z3;
-        dot2_lane<T, CPR>(wg, wu, ut, lane, z1, z3);
-        z1 = seg_sum<64>(z1);
-        z3 = seg_sum<64>(z3);
-        if (lane == 0) A[(size_t)p * I + i] = silu_f32(z1) * z3;
-      }
-    }
+    gateup_unit<T, CPR, NT>(wg, wu, lds, p0, p1, i, I, k, shared != 0, rt, A, lane);
+    unit += stride;
+    if (unit >= units) break;
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair<T, CPR>(w13, expert_of(unit), unit % I, I, wg, wu, lane);
   }
 }
 
@@ -167,7 +221,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
 // out[t][n] = RNE(h32[t][n] + sum_{e active} sum_{p of e, token t} g_p (W2_e[n] . A[p])
 //                 + Ws2[n] . As[t]).  Each routed W2 row is read once for all its tokens.
 // Lane partials are accumulated over experts (ascending) then the shared expert, and
-// reduced across the row's lanes once per token.
+// reduced across the row's lanes once per token.  EB experts' rows are requested at once.
 template <typename T, int CPR, int NT, int EB>
 __global__ __launch_bounds__(kGemvThreads) void down_combine_gemv_kernel(
     const float* __restrict__ A, const float* __restrict__ As, const T* __restrict__ w2,
@@ -177,36 +231,49 @@ __global__ __launch_bounds__(kGemvThreads) void down_combine_gemv_kernel(
   extern __shared__ float lds[];  // A [B*k][I], As [B][I]
   float* sA = lds;
   float* sAs = lds + (size_t)B * k * G::K;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int sub = lane % G::SEG, seg = lane / G::SEG;
-  for (int i = threadIdx.x; i < B * k * G::K / 4; i += blockDim.x)
-    reinterpret_cast<float4*>(sA)[i] = reinterpret_cast<const float4*>(A)[i];
-  for (int i = threadIdx.x; i < B * G::K / 4; i += blockDim.x)
-    reinterpret_cast<float4*>(sAs)[i] = reinterpret_cast<const float4*>(As)[i];
-  __syncthreads();
   const int n_act = *rt.n_act;
-  const int stride = gridDim.x * kGemvWaves * G::RPW;
+  const int stride = gridDim.x * wpb * G::RPW;
+  int base = (blockIdx.x * wpb + wave) * G::RPW;
 
-  for (int base = (blockIdx.x * kGemvWaves + wave) * G::RPW; base < H; base += stride) {
-    const int row = base + seg;
+  u32x4 w[EB][G::CPL], ws[G::CPL];
+  int eid[EB];
+  auto issue = [&](int row, int a0) {
     const bool rv = row < H;
+#pragma unroll
+    for (int q = 0; q < EB; ++q) {
+      const int a = a0 + q;
+      eid[q] = a < n_act ? rt.act[a] : -1;
+      if (eid[q] >= 0 && rv)
+        load_row<T, CPR>(w2 + ((size_t)eid[q] * H + row) * G::K, sub, w[q]);
+      else
+#pragma unroll
+        for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto issue_shared = [&](int row) {
+    if (row < H)
+      load_row<T, CPR>(ws2 + (size_t)row * G::K, sub, ws);
+    else
+#pragma unroll
+      for (int i = 0; i < G::CPL; ++i) ws[i] = u32x4{0u, 0u, 0u, 0u};
+  };
+  if (base < H) {
+    issue(base + seg, 0);
+    issue_shared(base + seg);
+  }
+  stage_rows_f32(sA, A, B * k * G::K);
+  stage_rows_f32(sAs, As, B * G::K);
+  __syncthreads();
+  if (base >= H) return;
+
+  while (true) {
+    const int row = base + seg;
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-
-    for (int a0 = 0; a0 < n_act; a0 += EB) {
-      u32x4 w[EB][G::CPL];
-      int eid[EB];
-#pragma unroll
-      for (int q = 0; q < EB; ++q) {
-        const int a = a0 + q;
-        eid[q] = a < n_act ? rt.act[a] : -1;
-        if (eid[q] >= 0 && rv)
-          load_row<T, CPR>(w2 + ((size_t)eid[q] * H + row) * G::K, sub, w[q]);
-        else
-#pragma unroll
-          for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int a0 = 0;;) {
 #pragma unroll
       for (int q = 0; q < EB; ++q) {
         if (eid[q] < 0) continue;
@@ -225,23 +292,24 @@ __global__ __launch_bounds__(kGemvThreads) void down_combine_gemv_kernel(
           }
         }
       }
+      a0 += EB;
+      if (a0 >= n_act) break;
+      __builtin_amdgcn_sched_barrier(0);
+      issue(row, a0);
     }
-    u32x4 ws[G::CPL];
-    if (rv)
-      load_row<T, CPR>(ws2 + (size_t)row * G::K, sub, ws);
-    else
-#pragma unroll
-      for (int i = 0; i < G::CPL; ++i) ws[i] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t < B) {
-        const float v = seg_sum<G::SEG>(acc[t] + dot_lane<T, CPR>(ws, sAs + t * G::K, sub));
-        if (sub == 0 && rv) {
-          const size_t o = (size_t)t * H + row;
-          Elem<T>::store(out, o, h32[o] + v);
-        }
+      const float v = seg_sum<G::SEG>(acc[t] + dot_lane<T, CPR>(ws, sAs + t * G::K, sub));
+      if (sub == 0 && row < H) {
+        const size_t o = (size_t)t * H + row;
+        Elem<T>::store(out, o, h32[o] + v);
       }
     }
+    base += stride;
+    if (base >= H) break;
+    __builtin_amdgcn_sched_barrier(0);
+    issue(base + seg, 0);
+    issue_shared(base + seg);
   }
 }
 
@@ -298,32 +366,47 @@ void allow_lds(K kernel, size_t bytes) {
   if (n_done < 64) done[n_done++] = (const void*)kernel;
 }
 
+// Persistent launch shape: blocks <= num_cu, 4..8 waves each, preferring a total wave count
+// that divides the work evenly (no half-empty last round).
+struct LaunchShape {
+  int blocks, threads;
+};
+LaunchShape balanced(const Device& d, int units) {
+  for (int wpb = 8; wpb >= 4; --wpb) {
+    const int waves = d.num_cu * wpb;
+    if (units % waves == 0) return {d.num_cu, wpb * 64};
+  }
+  const int waves = d.num_cu * 8;
+  if (units < waves) return {(units + 7) / 8, 512};
+  return {d.num_cu, 512};
+}
+
 template <typename T, int CPR, int R>
 hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const void* r,
                    const void* w, float* h32, void* h_out, hipStream_t st) {
-  const size_t lds = (size_t)B * Geo<T, CPR>::K * sizeof(float);
-  auto kern = B == 1 ? oproj_gemv_kernel<T, CPR, 1, R> : oproj_gemv_kernel<T, CPR, 2, R>;
-  allow_lds(kern, lds);
-  const int rows_per_unit = Geo<T, CPR>::RPW * R;
+  // two tokens' activations share the register budget with half as many rows in flight
+  constexpr int R2 = (R > 1 && Geo<T, CPR>::CPL > 4) ? R / 2 : R;
+  const int rows_per_unit = Geo<T, CPR>::RPW * (B == 1 ? R : R2);
   const int units = (s.H + rows_per_unit - 1) / rows_per_unit;
-  int grid = d.num_cu;
-  if (grid * kGemvWaves > units) grid = (units + kGemvWaves - 1) / kGemvWaves;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), lds, st, (const T*)x, (const T*)r,
-                     (const T*)w, h32, (T*)h_out, s.H, B);
+  const LaunchShape ls = balanced(d, units);
+  auto kern = B == 1 ? oproj_gemv_kernel<T, CPR, 1, R> : oproj_gemv_kernel<T, CPR, 2, R2>;
+  const size_t lds = 2 * Geo<T, CPR>::CPL > 14 && B == 2 ? 2 * Geo<T, CPR>::K * sizeof(float) : 0;
+  hipLaunchKernelGGL(kern, dim3(ls.blocks), dim3(ls.threads), lds, st, (const T*)x, (const T*)r,
+                     (const T*)w, h32, (T*)h_out, s.H);
   return hipGetLastError();
 }
 
-template <typename T, int CPS>
+template <typename T, int CPS, int CPRH>
 hipError_t router_t(const Shape& s, const Device& d, int B, const float* h32, const void* w_r,
-                    const float* bias, float* part, unsigned* counter, const Routing& rt,
-                    hipStream_t st) {
+                    const float* bias, float* part, unsigned* ctrs, const Routing& rt,
+                    const void* ws13, float* As, hipStream_t st) {
   const int splits = s.H / Geo<T, CPS>::K;
-  const int units = s.E * splits;
-  const int grid = (units + 3) / 4;
-  auto kern = B == 1 ? router_gemv_kernel<T, CPS, 1> : router_gemv_kernel<T, CPS, 2>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, st, h32,
-                     (const T*)w_r, bias, s.H, s.E, s.k, B, splits, s.routed_scale, part, counter,
-                     rt);
+  const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
+  auto kern = B == 1 ? router_gemv_kernel<T, CPS, CPRH, 1> : router_gemv_kernel<T, CPS, CPRH, 2>;
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, bias,
+                     s.H, s.E, s.k, B, splits, s.routed_scale, part, ctrs, rt, (const T*)ws13, s.Is,
+                     As);
   return hipGetLastError();
 }
 
@@ -334,12 +417,8 @@ hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, cons
   auto kern = B == 1 ? gateup_gemv_kernel<T, CPR, 1> : gateup_gemv_kernel<T, CPR, 2>;
   allow_lds(kern, lds);
   const int inter = shared ? s.Is : s.I;
-  const int max_act = shared ? 1 : (s.E < B * s.k ? s.E : B * s.k);
-  const int units = max_act * inter;
-  int grid = d.num_cu;
-  if (grid * kGemvWaves > units) grid = (units + kGemvWaves - 1) / kGemvWaves;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), lds, st, u, (const T*)w13, inter, s.k,
-                     B, shared ? 1 : 0, rt, A);
+  hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, u, (const T*)w13, inter,
+                     s.k, B, shared ? 1 : 0, rt, A);
   return hipGetLastError();
 }
 
@@ -349,12 +428,13 @@ hipError_t down_t(const Shape& s, const Device& d, int B, const float* A, const 
                   hipStream_t st) {
   using G = Geo<T, CPR>;
   const size_t lds = (size_t)(B * s.k + B) * G::K * sizeof(float);
-  auto kern = B == 1 ? down_combine_gemv_kernel<T, CPR, 1, 4> : down_combine_gemv_kernel<T, CPR, 2, 4>;
+  // experts whose rows are requested together: ~16 chunks per lane in flight
+  constexpr int EB = G::CPL >= 4 ? 4 : 8;
+  auto kern = B == 1 ? down_combine_gemv_kernel<T, CPR, 1, EB> : down_combine_gemv_kernel<T, CPR, 2, EB>;
   allow_lds(kern, lds);
   const int units = (s.H + G::RPW - 1) / G::RPW;
-  int grid = d.num_cu;
-  if (grid * kGemvWaves > units) grid = (units + kGemvWaves - 1) / kGemvWaves;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemvThreads), lds, st, A, As, (const T*)w2,
+  const LaunchShape ls = balanced(d, units);
+  hipLaunchKernelGGL(kern, dim3(ls.blocks), dim3(ls.threads), lds, st, A, As, (const T*)w2,
                      (const T*)ws2, s.H, s.k, B, rt, h32, (T*)out);
   return hipGetLastError();
 }
@@ -387,12 +467,12 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 }
 
 hipError_t launch_router_gemv(const Shape& s, const Device& d, int B, const float* h32,
-                              const void* w_r, const float* bias, float* part, unsigned* counter,
-                              const Routing& rt, hipStream_t st) {
+                              const void* w_r, const float* bias, float* part, unsigned* ctrs,
+                              const Routing& rt, const void* ws13, float* As, hipStream_t st) {
   if (s.dtype == 1 && s.H == 7168)
-    return router_t<uint16_t, 128>(s, d, B, h32, w_r, bias, part, counter, rt, st);
+    return router_t<uint16_t, 128, 896>(s, d, B, h32, w_r, bias, part, ctrs, rt, ws13, As, st);
   if (s.dtype == 0 && s.H == 256)
-    return router_t<float, 64>(s, d, B, h32, w_r, bias, part, counter, rt, st);
+    return router_t<float, 64, 64>(s, d, B, h32, w_r, bias, part, ctrs, rt, ws13, As, st);
   return hipErrorInvalidValue;
 }
 

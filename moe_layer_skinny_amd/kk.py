@@ -18,6 +18,7 @@ KK_OK, KK_ERR_INVALID_ARG, KK_ERR_UNSUPPORTED, KK_ERR_WORKSPACE, KK_ERR_HIP = ra
 KK_F32, KK_BF16 = 0, 1
 KK_PATH_GEMV, KK_PATH_SPLITK_MFMA = 0, 1
 KK_GRAPH = 1
+KK_TWO_STREAM = 2
 PATH_NAMES = {KK_PATH_GEMV: "gemv", KK_PATH_SPLITK_MFMA: "splitk_mfma"}
 
 
@@ -174,10 +175,10 @@ class Layer:
                                    _stream(stream)))
 
     def layer_decode(self, B, x, resid, out, ws, topk_idx=None, topk_gate=None, stream=None,
-                     graph=False):
+                     graph=False, two_stream=False):
+        flags = (KK_GRAPH if graph else 0) | (KK_TWO_STREAM if two_stream else 0)
         _check(lib().kk_layer_decode(self._h, B, _ptr(x), _ptr(resid), _ptr(out), _ptr(topk_idx),
-                                     _ptr(topk_gate), _ptr(ws), _stream(stream),
-                                     KK_GRAPH if graph else 0))
+                                     _ptr(topk_gate), _ptr(ws), _stream(stream), flags))
 
     def set_kernel_timing(self, enable: bool):
         _check(lib().kk_set_kernel_timing(self._h, 1 if enable else 0))
