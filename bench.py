@@ -91,7 +91,7 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=1)
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--mode", choices=["eager", "graph"], default="eager",
-                    help="how each timed step is submitted (eager: 4 launches on one stream)")
+                    help="how each timed step is submitted (eager: one launch per kernel on one stream)")
     ap.add_argument("--two-stream", action="store_true",
                     help="shared expert's gate/up on the auxiliary stream")
     args = ap.parse_args()

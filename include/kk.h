@@ -29,12 +29,11 @@
  *
  * Ownership: the caller owns every buffer (weights, activations, outputs, workspace).
  * Weights passed to kk_create must stay alive and unchanged until kk_destroy.  The
- * context owns an auxiliary HIP stream, events, a small counter buffer and cached HIP
- * graphs.  Every device pointer must be 16-byte aligned; ws must be 256-byte aligned.
+ * context owns an auxiliary HIP stream, events and cached HIP graphs.  Every device pointer must be 16-byte aligned; ws must be 256-byte aligned.
  *
  * Concurrency: every op is asynchronous on the caller's stream; no host synchronisation.
  * One host thread and one stream at a time per context (the ops share the context's
- * counters and auxiliary stream).
+ * auxiliary stream and events).
  *
  * Errors: arguments are validated on the host before anything is enqueued; a failure
  * returns a status and sets kk_last_error() (thread-local text).  A shape outside the
@@ -70,7 +69,7 @@ typedef enum {
 /* kk_layer_decode flags */
 #define KK_GRAPH 1u      /* capture the step once per (B, buffers, stream, flags), replay it */
 #define KK_TWO_STREAM 2u /* shared expert's gate/up on the context's auxiliary stream instead
-                            of inside the router launch (kept for comparison) */
+                            of inside the top-k launch (kept for comparison) */
 
 typedef struct {
   int32_t hidden;       /* H  */
@@ -141,8 +140,8 @@ kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t*
                         const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
                         void* out, void* ws, kk_stream stream);
 
-/* The whole step: o-proj + residual, router || shared expert gate/up, routed experts,
- * down-projection + combine (four launches on `stream`).  topk_idx / topk_gate are optional
+/* The whole step: o-proj + residual, router logits, top-k || shared expert gate/up, routed
+ * experts, down-projection + combine (five launches on `stream`).  topk_idx / topk_gate are optional
  * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
  * first use for these (B, pointers, stream, flags) and replayed afterwards. */
 kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,

@@ -119,10 +119,10 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
   return KK_OK;
 }
 
-const char* kernel_names[] = {"oproj_gemv",         "router_gemv",       "gateup_gemv_shared",
+const char* kernel_names[] = {"oproj_gemv",         "router_logits",     "gateup_gemv_shared",
                               "gateup_gemv_routed", "down_combine_gemv", "moe_prep",
-                              "router_shared_gemv"};
-enum KName { K_OPROJ, K_ROUTER, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_ROUTER_SHARED };
+                              "topk_shared",        "topk"};
+enum KName { K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK };
 
 struct TimingRec {
   int name;
@@ -150,7 +150,6 @@ struct kk_ctx {
   Layout L;
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
-  unsigned* counter = nullptr;  // arrival counters (kk::kArriveCounters words), self-resetting
   std::vector<GraphEntry> graphs;
   unsigned long long clock = 0;
   bool timing = false;
@@ -184,8 +183,8 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
     p->router_splitk = kk::router_gemv_splits(c->shape);
-    // oproj, router || shared gate/up, routed gate/up, down + combine -- one stream
-    p->kernels_per_step = 4;
+    // oproj, router logits, top-k || shared gate/up, routed gate/up, down + combine
+    p->kernels_per_step = 5;
     p->streams = 1;
     return KK_OK;
   }
@@ -280,14 +279,20 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
   return KK_OK;
 }
 
+// Router logits, then top-k / tables (+ the shared expert's gate/up when ws13 is given).
 kk_status enqueue_router(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                          float* logit_part, const void* ws13, float* As, hipStream_t s) {
-  KK_HIP(timed(c, ws13 ? K_ROUTER_SHARED : K_ROUTER, s,
+  KK_HIP(timed(c, K_LOGITS, s,
                [&] {
-                 return kk::launch_router_gemv(c->shape, c->dev, B, h32, c->w.w_r, c->w.bias,
-                                               logit_part, c->counter, rt, ws13, As, s);
+                 return kk::launch_router_logits(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s);
                }),
-         "router launch");
+         "router logits launch");
+  KK_HIP(timed(c, ws13 ? K_TOPK_SHARED : K_TOPK, s,
+               [&] {
+                 return kk::launch_topk_shared(c->shape, c->dev, B, logit_part, c->w.bias, rt, ws13,
+                                               h32, As, s);
+               }),
+         "top-k launch");
   return KK_OK;
 }
 
@@ -326,7 +331,7 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, s);
   if (st != KK_OK) return st;
   if (!two_stream) {
-    // shared expert's gate/up streams inside the router launch, overlapping the top-k
+    // the shared expert's gate/up streams inside the top-k launch
     st = enqueue_router(c, B, p.h32, rt, p.logit_part, c->w.ws13, p.As, s);
     if (st != KK_OK) return st;
     return enqueue_routed_and_combine(c, B, p.h32, rt, p, out, s);
@@ -427,10 +432,6 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     if (e != hipSuccess) return bail(e, "fork event");
     e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "join event");
-    e = hipMalloc((void**)&c->counter, kk::kArriveCounters * sizeof(unsigned));
-    if (e != hipSuccess) return bail(e, "counter buffer");
-    e = hipMemset(c->counter, 0, kk::kArriveCounters * sizeof(unsigned));
-    if (e != hipSuccess) return bail(e, "counter clear");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return bail(e, "create sync");
     *out = c;
@@ -449,7 +450,6 @@ kk_status kk_destroy(kk_ctx* c) {
     (void)hipEventDestroy(r.b);
   }
   for (auto ev : c->tpool) (void)hipEventDestroy(ev);
-  if (c->counter) (void)hipFree(c->counter);
   if (c->ev_fork) (void)hipEventDestroy(c->ev_fork);
   if (c->ev_join) (void)hipEventDestroy(c->ev_join);
   if (c->aux) (void)hipStreamDestroy(c->aux);

@@ -197,38 +197,6 @@ __device__ __forceinline__ void dot2_lane(const u32x4 (&wa)[Geo<T, CPR>::CPL],
   sb = b0;
 }
 
-// Arrival of this block at a one-shot rendezvous of all gridDim.x blocks; returns true in
-// exactly one block, the last to arrive, after which every other block's prior writes are
-// visible to it.  Two levels (8 sub-counters by blockIdx % 8, one per XCD under round-robin
-// dispatch, then a top counter) keep single-address atomic traffic to ~gridDim/8 + 8
-// operations.  Each counter is reset by its last arriver, so the words are zero again when
-// the kernel ends.  ctrs: 9 counters 16 words apart.
-__device__ inline bool last_block_arrive(unsigned* ctrs) {
-  __shared__ int s_last;
-  __threadfence();  // every wave releases its own writes before the block arrives
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int nb = gridDim.x;
-    const int sub = blockIdx.x & 7;
-    const unsigned n_sub = (unsigned)((nb - sub + 7) / 8);
-    const unsigned n_top = (unsigned)(nb < 8 ? nb : 8);
-    int last = 0;
-    if (atomicAdd(&ctrs[16 * (1 + sub)], 1u) == n_sub - 1) {
-      atomicExch(&ctrs[16 * (1 + sub)], 0u);
-      __threadfence();  // carry the sub-group's writes on to the top counter
-      if (atomicAdd(&ctrs[0], 1u) == n_top - 1) {
-        atomicExch(&ctrs[0], 0u);
-        last = 1;
-      }
-    }
-    s_last = last;
-  }
-  __syncthreads();
-  const bool last = s_last != 0;
-  if (last) __threadfence();  // acquire
-  return last;
-}
-
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
 }  // namespace kk

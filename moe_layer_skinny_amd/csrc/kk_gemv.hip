@@ -1,16 +1,19 @@
 // GEMV path of the decode-layer step (batch 1-2): every weight row is streamed from HBM
 // once with 128-bit non-temporal loads, each row's dot product finished with a wavefront
-// shuffle reduction.  One stream, four launches per step:
+// shuffle reduction.  One stream, five launches per step:
 //   1. o-proj + residual                     (activations held in registers)
-//   2. router logits -> top-k/gates/tables   (last block to arrive)  ||  shared gate/up
-//   3. routed gate/up over the active experts
-//   4. routed + shared down-projection fused with the weighted combine
+//   2. router logits (split-K partials)
+//   3. top-k / gates / routing tables (block 0)  ||  shared expert gate/up (other blocks)
+//   4. routed gate/up over the active experts
+//   5. routed + shared down-projection fused with the weighted combine
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
 // time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
 // the residual; the shared expert overlapping routing; fewer launches.  On this GPU a
 // cross-stream fork/join and replayed graph nodes each cost more than a kernel boundary on
-// one stream, so the shared expert's overlap with routing happens inside launch 2.
+// one stream, and a device-scope fence per wave for an in-kernel cross-block handoff costs
+// more still, so the shared expert overlaps the serial top-k inside launch 3 with no
+// communication between its blocks.
 #include "kk_common.cuh"
 #include "kk_internal.h"
 #include "kk_topk.cuh"
@@ -131,30 +134,16 @@ __device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restri
 }
 
 // ------------------------------------------------------------------------------ router
-// Phase 1: logit partials part[s][t][e] over `splits` K-slices (h32 read from L2).
-// Arrival: the last block runs top-k, gates and the routing tables.
-// Phase 2 (ws13 != nullptr): the shared expert's gate/up over all B tokens; each wave's
-// first row pair is requested before phase 1 so HBM streams while the router works.
-template <typename T, int CPS, int CPRH, int NT>
-__global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(
-    const float* __restrict__ h32, const T* __restrict__ w_r, const float* __restrict__ bias,
-    int H, int E, int k, int B, int splits, float routed_scale, float* __restrict__ part,
-    unsigned* __restrict__ ctrs, Routing rt, const T* __restrict__ ws13, int Is,
-    float* __restrict__ As) {
+// Logit partials part[s][t][e] over `splits` K-slices; one (expert, slice) unit per wave,
+// h32 read from L2.
+template <typename T, int CPS, int NT>
+__global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
+    const float* __restrict__ h32, const T* __restrict__ w_r, int H, int E, int B, int splits,
+    float* __restrict__ part) {
   using G = Geo<T, CPS>;
-  using GH = Geo<T, CPRH>;
-  __shared__ TopkScratch sm;
-  extern __shared__ float lds[];  // u [B][H] for phase 2
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
-  const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
-  const bool shared = ws13 != nullptr;
-
-  u32x4 wg[GH::CPL], wu[GH::CPL];
-  int su = gw;
-  if (shared && su < Is) load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
-
   const int units = E * splits;
-  for (int unit = gw; unit < units; unit += nw) {
+  for (int unit = blockIdx.x * wpb + wave; unit < units; unit += gridDim.x * wpb) {
     const int e = unit / splits, s = unit - e * splits;
     u32x4 w[G::CPL];
     load_row<T, CPS>(w_r + (size_t)e * H + (size_t)s * G::K, lane, w);
@@ -165,9 +154,28 @@ __global__ __launch_bounds__(kGemvThreads) void router_gemv_kernel(
       if (lane == 0) part[((size_t)s * B + t) * E + e] = acc;
     }
   }
-  if (last_block_arrive(ctrs)) topk_tables(part, splits, bias, B, E, k, routed_scale, rt, sm);
-  if (!shared) return;
+}
 
+// Block 0: top-k, gates and routing tables from the logit partials.  Blocks 1..: the shared
+// expert's gate/up over all B tokens (ws13 != nullptr), so its weight stream overlaps the
+// serial top-k without any cross-block communication.
+template <typename T, int CPRH, int NT>
+__global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
+    const float* __restrict__ part, int splits, const float* __restrict__ bias, int E, int k,
+    int B, float routed_scale, Routing rt, const T* __restrict__ ws13, int Is,
+    const float* __restrict__ h32, float* __restrict__ As) {
+  using GH = Geo<T, CPRH>;
+  extern __shared__ float lds[];  // blocks >= 1: u [B][H]
+  if (blockIdx.x == 0) {
+    __shared__ TopkScratch sm;
+    topk_tables(part, splits, bias, B, E, k, routed_scale, rt, sm);
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
+  const int nw = (gridDim.x - 1) * wpb;
+  int su = (blockIdx.x - 1) * wpb + wave;
+  u32x4 wg[GH::CPL], wu[GH::CPL];
+  if (su < Is) load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
   stage_rows_f32(lds, h32, B * GH::K);
   __syncthreads();
   if (su >= Is) return;
@@ -396,17 +404,29 @@ hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const 
   return hipGetLastError();
 }
 
+template <typename T, int CPS>
+hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* h32,
+                           const void* w_r, float* part, hipStream_t st) {
+  const int splits = s.H / Geo<T, CPS>::K;
+  const int units = s.E * splits;
+  const int blocks = (units + 7) / 8;
+  auto kern = B == 1 ? router_logits_kernel<T, CPS, 1> : router_logits_kernel<T, CPS, 2>;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), 0, st, h32, (const T*)w_r, s.H, s.E,
+                     B, splits, part);
+  return hipGetLastError();
+}
+
 template <typename T, int CPS, int CPRH>
-hipError_t router_t(const Shape& s, const Device& d, int B, const float* h32, const void* w_r,
-                    const float* bias, float* part, unsigned* ctrs, const Routing& rt,
-                    const void* ws13, float* As, hipStream_t st) {
+hipError_t topk_shared_t(const Shape& s, const Device& d, int B, const float* part,
+                         const float* bias, const Routing& rt, const void* ws13,
+                         const float* h32, float* As, hipStream_t st) {
   const int splits = s.H / Geo<T, CPS>::K;
   const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
-  auto kern = B == 1 ? router_gemv_kernel<T, CPS, CPRH, 1> : router_gemv_kernel<T, CPS, CPRH, 2>;
+  auto kern = B == 1 ? topk_shared_kernel<T, CPRH, 1> : topk_shared_kernel<T, CPRH, 2>;
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, bias,
-                     s.H, s.E, s.k, B, splits, s.routed_scale, part, ctrs, rt, (const T*)ws13, s.Is,
-                     As);
+  const int blocks = ws13 ? 1 + d.num_cu : 1;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, part, splits, bias, s.E, s.k,
+                     B, s.routed_scale, rt, (const T*)ws13, s.Is, h32, As);
   return hipGetLastError();
 }
 
@@ -466,13 +486,20 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_router_gemv(const Shape& s, const Device& d, int B, const float* h32,
-                              const void* w_r, const float* bias, float* part, unsigned* ctrs,
-                              const Routing& rt, const void* ws13, float* As, hipStream_t st) {
+hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
+                                const void* w_r, float* part, hipStream_t st) {
+  if (s.dtype == 1 && s.H == 7168) return router_logits_t<uint16_t, 128>(s, d, B, h32, w_r, part, st);
+  if (s.dtype == 0 && s.H == 256) return router_logits_t<float, 64>(s, d, B, h32, w_r, part, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_shared(const Shape& s, const Device& d, int B, const float* part,
+                              const float* bias, const Routing& rt, const void* ws13,
+                              const float* h32, float* As, hipStream_t st) {
   if (s.dtype == 1 && s.H == 7168)
-    return router_t<uint16_t, 128, 896>(s, d, B, h32, w_r, bias, part, ctrs, rt, ws13, As, st);
+    return topk_shared_t<uint16_t, 128, 896>(s, d, B, part, bias, rt, ws13, h32, As, st);
   if (s.dtype == 0 && s.H == 256)
-    return router_t<float, 64, 64>(s, d, B, h32, w_r, bias, part, ctrs, rt, ws13, As, st);
+    return topk_shared_t<float, 64, 64>(s, d, B, part, bias, rt, ws13, h32, As, st);
   return hipErrorInvalidValue;
 }
 

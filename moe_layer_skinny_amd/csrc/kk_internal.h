@@ -34,10 +34,6 @@ struct Routing {
   int32_t* n_act;      // [1]
 };
 
-// Words of the arrival-counter buffer (9 counters, 64 bytes apart), zeroed at creation and
-// left zeroed by every kernel that uses them.
-constexpr int kArriveCounters = 9 * 16;
-
 // Launch configuration facts gathered once per context.
 struct Device {
   int num_cu;
@@ -52,14 +48,15 @@ bool gemv_supported(const Shape& s, int B);
 hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void* x, const void* r,
                              const void* w_o, float* h32, void* h_out, hipStream_t st);
 
-// Router logits (split-K partials) + top-k, gates and routing tables by the last block to
-// arrive.  With ws13 != nullptr the same launch also computes the shared expert's gate/up
-// (As[t][i] = silu(Ws1[i].u_t) * (Ws3[i].u_t)) after the logit phase, so the shared expert's
-// weight stream overlaps the serial top-k.  counters: kArriveCounters zeroed words.
-hipError_t launch_router_gemv(const Shape& s, const Device& d, int B, const float* h32,
-                              const void* w_r, const float* bias, float* partials,
-                              unsigned* counters, const Routing& rt, const void* ws13, float* As,
-                              hipStream_t st);
+// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s].
+hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
+                                const void* w_r, float* partials, hipStream_t st);
+// Top-k, gates and routing tables from the partials (one block); with ws13 != nullptr the
+// same launch computes the shared expert's gate/up in its other blocks:
+// As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).
+hipError_t launch_topk_shared(const Shape& s, const Device& d, int B, const float* partials,
+                              const float* bias, const Routing& rt, const void* ws13,
+                              const float* h32, float* As, hipStream_t st);
 int router_gemv_splits(const Shape& s);
 
 // Routed gate/up over the active experts (act/n_act) or the shared expert (shared=true):
