@@ -43,7 +43,7 @@ def unique_bytes(cfg, n_act: int) -> dict:
         "router": wb * E * H + 4 * E,
         "shared_gateup": wb * 2 * Is * H,
         "routed_gateup": wb * n_act * 2 * I * H,
-        "down_combine": wb * (n_act * H * I + H * Is),
+        "down": wb * (n_act * H * I + H * Is),
     }
     parts["total"] = sum(parts.values())
     return parts

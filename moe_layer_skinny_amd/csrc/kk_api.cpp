@@ -119,10 +119,12 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
   return KK_OK;
 }
 
-const char* kernel_names[] = {"oproj_gemv",         "router_logits",     "gateup_gemv_shared",
-                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep",
-                              "topk_shared",        "topk"};
-enum KName { K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK };
+const char* kernel_names[] = {"oproj_gemv", "router_logits", "gateup_gemv_shared",
+                              "gateup_gemv_routed", "down_gemv", "moe_prep", "topk_shared",
+                              "topk", "combine"};
+enum KName {
+  K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK, K_COMBINE
+};
 
 struct TimingRec {
   int name;
@@ -183,8 +185,8 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
     p->router_splitk = kk::router_gemv_splits(c->shape);
-    // oproj, router logits, top-k || shared gate/up, routed gate/up, down + combine
-    p->kernels_per_step = 5;
+    // oproj, router logits, top-k || shared gate/up, routed gate/up, down, combine
+    p->kernels_per_step = 6;
     p->streams = 1;
     return KK_OK;
   }
@@ -233,6 +235,8 @@ struct WsPtrs {
   int32_t* n_act;
   float* A;
   float* As;
+  float* Y;
+  float* ys;
 };
 
 WsPtrs carve(const kk_ctx* c, void* ws) {
@@ -241,7 +245,8 @@ WsPtrs carve(const kk_ctx* c, void* ws) {
   return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
                 (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
                 (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
-                (float*)(b + L.A),         (float*)(b + L.As)};
+                (float*)(b + L.A),         (float*)(b + L.As),         (float*)(b + L.Y),
+                (float*)(b + L.ys)};
 }
 
 kk_status check_common(const kk_ctx* c, int B, void* ws) {
@@ -306,7 +311,21 @@ kk_status enqueue_shared_gateup(kk_ctx* c, int B, const float* h32, const kk::Ro
   return KK_OK;
 }
 
-// Routed gate/up then the fused routed + shared down-projection and combine, on s.
+kk_status enqueue_down_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                               const WsPtrs& p, void* out, hipStream_t s) {
+  KK_HIP(timed(c, K_DOWN, s,
+               [&] {
+                 return kk::launch_down_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
+                                             p.Y, p.ys, s);
+               }),
+         "down launch");
+  KK_HIP(timed(c, K_COMBINE, s,
+               [&] { return kk::launch_combine(c->shape, B, h32, p.Y, p.ys, rt, out, s); }),
+         "combine launch");
+  return KK_OK;
+}
+
+// Routed gate/up, then the routed + shared down-projection and the combine, on s.
 kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                                      const WsPtrs& p, void* out, hipStream_t s) {
   KK_HIP(timed(c, K_GU_ROUTED, s,
@@ -314,13 +333,7 @@ kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const k
                  return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A, s);
                }),
          "routed gate/up launch");
-  KK_HIP(timed(c, K_DOWN, s,
-               [&] {
-                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
-                                                     c->w.ws2, rt, h32, out, s);
-               }),
-         "down+combine launch");
-  return KK_OK;
+  return enqueue_down_combine(c, B, h32, rt, p, out, s);
 }
 
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
@@ -350,13 +363,7 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
                }),
          "routed gate/up launch");
   KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
-  KK_HIP(timed(c, K_DOWN, s,
-               [&] {
-                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
-                                                     c->w.ws2, rt, p.h32, out, s);
-               }),
-         "down+combine launch");
-  return KK_OK;
+  return enqueue_down_combine(c, B, p.h32, rt, p, out, s);
 }
 
 void destroy_graphs(kk_ctx* c) {

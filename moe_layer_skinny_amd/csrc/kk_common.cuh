@@ -161,6 +161,73 @@ __device__ __forceinline__ void load_act_chunks(const T* __restrict__ row, int s
   }
 }
 
+// ---- wavefront reductions with DPP lane moves (VALU latency instead of the LDS crossbar).
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror =
+// 0x141, row_mirror = 0x140, row_bcast15 = 0x142 (rows 1, 3), row_bcast31 = 0x143 (rows
+// 2, 3), row_shr:n = 0x110 + n.  After the six combining steps lane 63 holds the result.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>((uint32_t)v);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum of v over the 64 lanes, returned to every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));
+  v = max_u64(v, dpp_u64<0x4E>(v));
+  v = max_u64(v, dpp_u64<0x141>(v));
+  v = max_u64(v, dpp_u64<0x140>(v));
+  v = max_u64(v, dpp_u64<0x142, 0xA>(v));
+  v = max_u64(v, dpp_u64<0x143, 0xC>(v));
+  return readlane_u64(v, 63);
+}
+
+// Sum of v over the 64 lanes in a fixed combining order, returned to every lane.
+__device__ __forceinline__ double wave_sum_f64_dpp(double v) {
+  auto step = [](double x, uint64_t moved) { return x + __longlong_as_double((long long)moved); };
+  v = step(v, dpp_u64<0xB1>((uint64_t)__double_as_longlong(v)));
+  v = step(v, dpp_u64<0x4E>((uint64_t)__double_as_longlong(v)));
+  v = step(v, dpp_u64<0x141>((uint64_t)__double_as_longlong(v)));
+  v = step(v, dpp_u64<0x140>((uint64_t)__double_as_longlong(v)));
+  // rows 1 and 3 add their left neighbour row's total; rows 0 and 2 add nothing
+  {
+    const uint64_t bits = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)bits, 0x142, 0xA, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(bits >> 32), 0x142, 0xA, 0xF, false);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  {
+    const uint64_t bits = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)bits, 0x143, 0xC, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(bits >> 32), 0x143, 0xC, 0xF, false);
+    v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+  return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), 63));
+}
+
+// Inclusive prefix sum of v over lanes 0..63 (Hillis-Steele within rows of 16, then the
+// row totals carried across rows).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
 // Gate and up rows against the same activation row: each activation chunk is read from
 // LDS once and feeds both sums.
 template <typename T, int CPR>

@@ -1,11 +1,12 @@
 // GEMV path of the decode-layer step (batch 1-2): every weight row is streamed from HBM
 // once with 128-bit non-temporal loads, each row's dot product finished with a wavefront
-// shuffle reduction.  One stream, five launches per step:
+// shuffle reduction.  One stream, six launches per step:
 //   1. o-proj + residual                     (activations held in registers)
 //   2. router logits (split-K partials)
 //   3. top-k / gates / routing tables (block 0)  ||  shared expert gate/up (other blocks)
 //   4. routed gate/up over the active experts
-//   5. routed + shared down-projection fused with the weighted combine
+//   5. routed + shared down-projection, one contiguous run of one expert's rows per unit
+//   6. weighted combine into the residual
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
 // time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
@@ -225,16 +226,16 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   }
 }
 
-// ------------------------------------------------------------------------------ down + combine
-// out[t][n] = RNE(h32[t][n] + sum_{e active} sum_{p of e, token t} g_p (W2_e[n] . A[p])
-//                 + Ws2[n] . As[t]).  Each routed W2 row is read once for all its tokens.
-// Lane partials are accumulated over experts (ascending) then the shared expert, and
-// reduced across the row's lanes once per token.  EB experts' rows are requested at once.
-template <typename T, int CPR, int NT, int EB>
-__global__ __launch_bounds__(kGemvThreads) void down_combine_gemv_kernel(
+// ------------------------------------------------------------------------------ down (per expert)
+// Y[p][n] = W2_e[n] . A[p] for every position p of active expert e, and ys[t][n] = Ws2[n] .
+// As[t] for the shared expert (unit index n_act).  A unit is R consecutive row groups of
+// one expert, so each wave streams a contiguous run of that expert's W2 and consecutive
+// waves continue it; the weighted combine is a separate small launch.
+template <typename T, int CPR, int NT, int R>
+__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(
     const float* __restrict__ A, const float* __restrict__ As, const T* __restrict__ w2,
-    const T* __restrict__ ws2, int H, int k, int B, Routing rt, const float* __restrict__ h32,
-    T* __restrict__ out) {
+    const T* __restrict__ ws2, int H, int k, int B, Routing rt, float* __restrict__ Y,
+    float* __restrict__ ys) {
   using G = Geo<T, CPR>;
   extern __shared__ float lds[];  // A [B*k][I], As [B][I]
   float* sA = lds;
@@ -242,83 +243,86 @@ __global__ __launch_bounds__(kGemvThreads) void down_combine_gemv_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int sub = lane % G::SEG, seg = lane / G::SEG;
   const int n_act = *rt.n_act;
-  const int stride = gridDim.x * wpb * G::RPW;
-  int base = (blockIdx.x * wpb + wave) * G::RPW;
+  const int rows_per_unit = G::RPW * R;
+  const int rb_per_expert = (H + rows_per_unit - 1) / rows_per_unit;
+  const int units = (n_act + 1) * rb_per_expert;
+  const int stride = gridDim.x * wpb;
+  int unit = blockIdx.x * wpb + wave;
 
-  u32x4 w[EB][G::CPL], ws[G::CPL];
-  int eid[EB];
-  auto issue = [&](int row, int a0) {
-    const bool rv = row < H;
+  u32x4 w[R][G::CPL];
+  auto issue = [&](int u) {
+    const int a = u / rb_per_expert, rb = u - a * rb_per_expert;
+    const T* base = a < n_act ? w2 + (size_t)rt.act[a] * H * G::K : ws2;
 #pragma unroll
-    for (int q = 0; q < EB; ++q) {
-      const int a = a0 + q;
-      eid[q] = a < n_act ? rt.act[a] : -1;
-      if (eid[q] >= 0 && rv)
-        load_row<T, CPR>(w2 + ((size_t)eid[q] * H + row) * G::K, sub, w[q]);
+    for (int q = 0; q < R; ++q) {
+      const int n = rb * rows_per_unit + seg + G::RPW * q;
+      if (n < H)
+        load_row<T, CPR>(base + (size_t)n * G::K, sub, w[q]);
       else
 #pragma unroll
         for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto issue_shared = [&](int row) {
-    if (row < H)
-      load_row<T, CPR>(ws2 + (size_t)row * G::K, sub, ws);
-    else
-#pragma unroll
-      for (int i = 0; i < G::CPL; ++i) ws[i] = u32x4{0u, 0u, 0u, 0u};
-  };
-  if (base < H) {
-    issue(base + seg, 0);
-    issue_shared(base + seg);
-  }
+  if (unit < units) issue(unit);
   stage_rows_f32(sA, A, B * k * G::K);
   stage_rows_f32(sAs, As, B * G::K);
   __syncthreads();
-  if (base >= H) return;
-
+  if (unit >= units) return;
   while (true) {
-    const int row = base + seg;
-    float acc[NT];
+    const int a = unit / rb_per_expert, rb = unit - a * rb_per_expert;
+    int p0 = 0, p1 = B;
+    const bool routed = a < n_act;
+    if (routed) {
+      const int e = rt.act[a];
+      p0 = rt.offsets[e];
+      p1 = rt.offsets[e + 1];
+    }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = 0.f;
-    for (int a0 = 0;;) {
+    for (int q = 0; q < R; ++q) {
+      const int n = rb * rows_per_unit + seg + G::RPW * q;
 #pragma unroll
-      for (int q = 0; q < EB; ++q) {
-        if (eid[q] < 0) continue;
-        const int p0 = rt.offsets[eid[q]], p1 = rt.offsets[eid[q] + 1];
-#pragma unroll
-        for (int qq = 0; qq < NT; ++qq) {
-          const int p = p0 + qq;
-          if (p < p1) {
-            const int slot = rt.perm[p];
-            const int t = slot / k;
-            const float g = rt.topk_gate[slot];
-            const float d = dot_lane<T, CPR>(w[q], sA + (size_t)p * G::K, sub);
-#pragma unroll
-            for (int tt = 0; tt < NT; ++tt)
-              if (tt == t) acc[tt] = fmaf(g, d, acc[tt]);
-          }
+      for (int qq = 0; qq < NT; ++qq) {
+        const int p = p0 + qq;
+        if (p < p1) {
+          const float* act = routed ? sA + (size_t)p * G::K : sAs + (size_t)p * G::K;
+          const float v = seg_sum<G::SEG>(dot_lane<T, CPR>(w[q], act, sub));
+          if (sub == 0 && n < H) (routed ? Y : ys)[(size_t)p * H + n] = v;
         }
       }
-      a0 += EB;
-      if (a0 >= n_act) break;
-      __builtin_amdgcn_sched_barrier(0);
-      issue(row, a0);
     }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v = seg_sum<G::SEG>(acc[t] + dot_lane<T, CPR>(ws, sAs + t * G::K, sub));
-      if (sub == 0 && row < H) {
-        const size_t o = (size_t)t * H + row;
-        Elem<T>::store(out, o, h32[o] + v);
-      }
-    }
-    base += stride;
-    if (base >= H) break;
+    unit += stride;
+    if (unit >= units) break;
     __builtin_amdgcn_sched_barrier(0);
-    issue(base + seg, 0);
-    issue_shared(base + seg);
+    issue(unit);
   }
+}
+
+// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] * Y[inv_perm[t*k+j]][n] + ys[t][n]), j in
+// ascending expert order.  KMAX >= k; every load is issued before the sum (clamped indices,
+// zero gates past k) so the launch costs one memory latency.
+template <typename T, int KMAX>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ h32,
+                                                      const float* __restrict__ Y,
+                                                      const float* __restrict__ ys, Routing rt,
+                                                      int H, int k, int B, T* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * H) return;
+  const int t = i / H, n = i - t * H;
+  float g[KMAX];
+  int q[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int slot = t * k + min(j, k - 1);
+    g[j] = j < k ? rt.topk_gate[slot] : 0.f;
+    q[j] = rt.inv_perm[slot];
+  }
+  float y[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) y[j] = Y[(size_t)q[j] * H + n];
+  float acc = h32[i];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) acc = fmaf(g[j], y[j], acc);
+  Elem<T>::store(out, i, acc + ys[i]);
 }
 
 // ------------------------------------------------------------------------------ prep
@@ -444,18 +448,27 @@ hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, cons
 
 template <typename T, int CPR>
 hipError_t down_t(const Shape& s, const Device& d, int B, const float* A, const float* As,
-                  const void* w2, const void* ws2, const Routing& rt, const float* h32, void* out,
+                  const void* w2, const void* ws2, const Routing& rt, float* Y, float* ys,
                   hipStream_t st) {
   using G = Geo<T, CPR>;
+  constexpr int R = G::CPL >= 4 ? 2 : 4;  // rows per unit: 8 KB runs at I = 2048
   const size_t lds = (size_t)(B * s.k + B) * G::K * sizeof(float);
-  // experts whose rows are requested together: ~16 chunks per lane in flight
-  constexpr int EB = G::CPL >= 4 ? 4 : 8;
-  auto kern = B == 1 ? down_combine_gemv_kernel<T, CPR, 1, EB> : down_combine_gemv_kernel<T, CPR, 2, EB>;
+  auto kern = B == 1 ? down_gemv_kernel<T, CPR, 1, R> : down_gemv_kernel<T, CPR, 2, R>;
   allow_lds(kern, lds);
-  const int units = (s.H + G::RPW - 1) / G::RPW;
-  const LaunchShape ls = balanced(d, units);
-  hipLaunchKernelGGL(kern, dim3(ls.blocks), dim3(ls.threads), lds, st, A, As, (const T*)w2,
-                     (const T*)ws2, s.H, s.k, B, rt, h32, (T*)out);
+  int bpc = (int)((size_t)d.max_lds / (lds ? lds : 1));
+  bpc = bpc < 1 ? 1 : (bpc > 2 ? 2 : bpc);
+  hipLaunchKernelGGL(kern, dim3(d.num_cu * bpc), dim3(kGemvThreads), lds, st, A, As, (const T*)w2,
+                     (const T*)ws2, s.H, s.k, B, rt, Y, ys);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t combine_t(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
+                     const Routing& rt, void* out, hipStream_t st) {
+  const int n = B * s.H;
+  auto kern = s.k <= 8 ? combine_kernel<T, 8> : combine_kernel<T, 16>;
+  hipLaunchKernelGGL(kern, dim3((n + 255) / 256), dim3(256), 0, st, h32, Y, ys, rt, s.H, s.k, B,
+                     (T*)out);
   return hipGetLastError();
 }
 
@@ -512,18 +525,23 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
-                                    const float* As, const void* w2, const void* ws2,
-                                    const Routing& rt, const float* h32, void* out,
-                                    hipStream_t st) {
+hipError_t launch_down_gemv(const Shape& s, const Device& d, int B, const float* A,
+                            const float* As, const void* w2, const void* ws2, const Routing& rt,
+                            float* Y, float* ys, hipStream_t st) {
   const int c = cpr_of(s.I, s.dtype);
   if (s.dtype == 1) {
-    if (c == 256) return down_t<uint16_t, 256>(s, d, B, A, As, w2, ws2, rt, h32, out, st);
-    if (c == 16) return down_t<uint16_t, 16>(s, d, B, A, As, w2, ws2, rt, h32, out, st);
+    if (c == 256) return down_t<uint16_t, 256>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
+    if (c == 16) return down_t<uint16_t, 16>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
   } else if (c == 32) {
-    return down_t<float, 32>(s, d, B, A, As, w2, ws2, rt, h32, out, st);
+    return down_t<float, 32>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
+                          const Routing& rt, void* out, hipStream_t st) {
+  if (s.dtype == 1) return combine_t<uint16_t>(s, B, h32, Y, ys, rt, out, st);
+  return combine_t<float>(s, B, h32, Y, ys, rt, out, st);
 }
 
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st) {

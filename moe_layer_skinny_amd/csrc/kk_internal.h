@@ -65,11 +65,15 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
                               const void* w13, bool shared, const Routing& rt, float* A,
                               hipStream_t st);
 
-// out[t][n] = h32[t][n] + sum_positions gate * (W2_e[n] . A[p]) + Ws2[n] . As[t]
-hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
-                                    const float* As, const void* w2, const void* ws2,
-                                    const Routing& rt, const float* h32, void* out,
-                                    hipStream_t st);
+// Y[p][n] = W2_e[n] . A[p] for every position p of each active expert, ys[t][n] =
+// Ws2[n] . As[t] for the shared expert.
+hipError_t launch_down_gemv(const Shape& s, const Device& d, int B, const float* A,
+                            const float* As, const void* w2, const void* ws2, const Routing& rt,
+                            float* Y, float* ys, hipStream_t st);
+
+// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] + ys[t][n]).
+hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
+                          const Routing& rt, void* out, hipStream_t st);
 
 // act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);

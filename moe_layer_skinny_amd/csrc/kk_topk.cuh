@@ -1,10 +1,11 @@
 // Router tail shared by both paths: logits (sum of K-slice partials) -> sigmoid scores ->
-// fp64 selection keys -> top-k by wavefront arg-max rounds -> renormalised gates ->
+// fp64 selection keys -> top-k by wavefront arg-max rounds (DPP) -> renormalised gates ->
 // token->expert permutation and expert offsets by prefix sum.  Runs in one block.
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering time
 // between operators" (router scores in MoE preparation).  Reading of the unstated math:
-// sigmoid scores, selection on score + per-expert bias (lower index first on equal keys),
+// sigmoid scores, selection on score + per-expert bias (lower index first on equal keys;
+// keys are ranked on their fp64 value truncated to 43 mantissa bits),
 // gates = selected unbiased scores / their sum * routed_scale, experts of a token listed in
 // ascending index; perm orders slots (t*k + j) by (expert, token).
 #pragma once
@@ -23,66 +24,71 @@ struct TopkScratch {
   int start[kMaxExperts];                  // exclusive prefix sum of counts
 };
 
-// part: [splits][B][E] fp32 logit partials, summed in slice order.  blockDim.x >= 64.
+// Order-preserving 64-bit image of a double (larger key -> larger integer), with the low 9
+// bits replaced by (511 - e) so that one integer maximum picks the largest key and, among
+// keys equal to 43 mantissa bits, the lowest expert index.
+__device__ __forceinline__ uint64_t rank_key(double key, int e) {
+  uint64_t u = (uint64_t)__double_as_longlong(key);
+  u = (u >> 63) ? ~u : (u | (1ull << 63));
+  return (u & ~0x1FFull) | (uint64_t)(511 - e);
+}
+
+// part: [splits][B][E] fp32 logit partials (splits <= kMaxTopkSplits), summed in slice
+// order.  blockDim.x >= 64.  All global loads of a token are issued before any is used
+// (addresses clamped instead of branched around, so nothing waits on a join).
+constexpr int kMaxTopkSplits = 8;
 __device__ inline void topk_tables(const float* part, int splits, const float* __restrict__ bias,
                                    int B, int E, int k, float routed_scale, const Routing& rt,
                                    TopkScratch& sm) {
   constexpr int MAXM = kMaxExperts / 64;
+  constexpr int MAXS = kMaxTopkSplits;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const double kNegInf = -__builtin_huge_val();
   for (int e = threadIdx.x; e < E; e += blockDim.x) sm.mask[e] = 0ull;
 
   for (int t = wave; t < B; t += nw) {
-    double key[MAXM], sc[MAXM];
-    bool sel[MAXM];
+    float pv[MAXM][MAXS], bv[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+      const int ec = min(lane + 64 * m, E - 1);
+      bv[m] = bias[ec];
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s)
+        pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
+    }
+    double sc[MAXM];
+    uint64_t rk[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
       const int e = lane + 64 * m;
-      sel[m] = false;
-      key[m] = kNegInf;
-      sc[m] = 0.0;
-      if (e < E) {
-        float l = 0.f;
-        for (int s = 0; s < splits; ++s) l += part[((size_t)s * B + t) * E + e];
-        const double sv = 1.0 / (1.0 + exp(-(double)l));
-        sc[m] = sv;
-        key[m] = sv + (double)bias[e];
-      }
+      float l = 0.f;
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
+      const double sv = 1.0 / (1.0 + exp(-(double)l));
+      sc[m] = sv;
+      rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
     }
+    // k rounds of wave arg-max on the packed keys; the winner's entry drops out
+    uint32_t selmask = 0;
     for (int r = 0; r < k; ++r) {
-      double bk = kNegInf;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m) {  // ascending index: strict > keeps the lower one
-        const int e = lane + 64 * m;
-        if (e < E && !sel[m] && key[m] > bk) {
-          bk = key[m];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double ok = __shfl_xor(bk, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ok > bk || (ok == bk && oi < bi)) {
-          bk = ok;
-          bi = oi;
-        }
-      }
+      uint64_t best = 0;
 #pragma unroll
       for (int m = 0; m < MAXM; ++m)
-        if (lane + 64 * m == bi) sel[m] = true;
+        if (!((selmask >> m) & 1u)) best = max_u64(best, rk[m]);
+      best = wave_max_u64(best);
+      const int win = 511 - (int)(best & 0x1FFull);
+      if ((win & 63) == lane) selmask |= 1u << (win >> 6);
     }
     double ssum = 0.0;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
-      if (sel[m]) ssum += sc[m];
-    ssum = wave_sum_f64(ssum);
+      if ((selmask >> m) & 1u) ssum += sc[m];
+    ssum = wave_sum_f64_dpp(ssum);
     int base = 0;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) {
-      const unsigned long long bal = __ballot(sel[m]);
-      if (sel[m]) {
+      const bool on = (selmask >> m) & 1u;
+      const unsigned long long bal = __ballot(on);
+      if (on) {
         const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
         const int e = lane + 64 * m;
         rt.topk_idx[t * k + pos] = e;
@@ -97,39 +103,32 @@ __device__ inline void topk_tables(const float* part, int splits, const float* _
     atomicOr(&sm.mask[sm.sel[i]], 1ull << (i / k));
   __syncthreads();
   if (wave == 0) {
+    // lane l owns experts l*per .. l*per+per-1; counts (<= 64) and active flags are scanned
+    // together as (count | flag << 16)
     const int per = (E + 63) / 64;
-    int lc = 0, lf = 0;
+    uint32_t loc = 0;
     for (int q = 0; q < per; ++q) {
       const int e = lane * per + q;
       if (e < E) {
-        const int c = __popcll(sm.mask[e]);
-        lc += c;
-        lf += c > 0;
+        const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
+        loc += c | ((c > 0 ? 1u : 0u) << 16);
       }
     }
-    int ic = lc, jf = lf;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int vc = __shfl_up(ic, off, 64);
-      const int vf = __shfl_up(jf, off, 64);
-      if (lane >= off) {
-        ic += vc;
-        jf += vf;
-      }
-    }
-    int ec = ic - lc, ef = jf - lf;
+    const uint32_t inc = wave_incl_scan_u32(loc);
+    uint32_t ec = (inc - loc) & 0xFFFFu, ef = (inc - loc) >> 16;
     for (int q = 0; q < per; ++q) {
       const int e = lane * per + q;
       if (e < E) {
-        const int c = __popcll(sm.mask[e]);
-        sm.start[e] = ec;
-        rt.offsets[e] = ec;
+        const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
+        sm.start[e] = (int)ec;
+        rt.offsets[e] = (int)ec;
         if (c > 0) rt.act[ef++] = e;
         ec += c;
       }
     }
     if (lane == 63) {
-      rt.offsets[E] = ic;
-      *rt.n_act = jf;
+      rt.offsets[E] = (int)(inc & 0xFFFFu);
+      *rt.n_act = (int)(inc >> 16);
     }
   }
   __syncthreads();
