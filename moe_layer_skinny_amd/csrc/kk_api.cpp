@@ -284,12 +284,14 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
   return KK_OK;
 }
 
-// Router logits, then top-k / tables (+ the shared expert's gate/up when ws13 is given).
+// Router logits, then top-k / tables; with ws13 the shared expert's gate/up is split over
+// both launches.
 kk_status enqueue_router(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                          float* logit_part, const void* ws13, float* As, hipStream_t s) {
   KK_HIP(timed(c, K_LOGITS, s,
                [&] {
-                 return kk::launch_router_logits(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s);
+                 return kk::launch_router_logits(c->shape, c->dev, B, h32, c->w.w_r, logit_part,
+                                                 ws13, rt, As, s);
                }),
          "router logits launch");
   KK_HIP(timed(c, ws13 ? K_TOPK_SHARED : K_TOPK, s,

@@ -2,8 +2,8 @@
 // once with 128-bit non-temporal loads, each row's dot product finished with a wavefront
 // shuffle reduction.  One stream, six launches per step:
 //   1. o-proj + residual                     (activations held in registers)
-//   2. router logits (split-K partials)
-//   3. top-k / gates / routing tables (block 0)  ||  shared expert gate/up (other blocks)
+//   2. router logits (split-K partials)         ||  shared expert gate/up, first half
+//   3. top-k / gates / routing tables (block 0)  ||  shared expert gate/up, second half
 //   4. routed gate/up over the active experts
 //   5. routed + shared down-projection, one contiguous run of one expert's rows per unit
 //   6. weighted combine into the residual
@@ -135,16 +135,44 @@ __device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restri
 }
 
 // ------------------------------------------------------------------------------ router
-// Logit partials part[s][t][e] over `splits` K-slices; one (expert, slice) unit per wave,
-// h32 read from L2.
-template <typename T, int CPS, int NT>
+// Shared expert gate/up rows [i0, i1) over all B tokens, spread over `nw` workers (waves),
+// worker `gw`; wg/wu already hold the worker's first row pair when `primed`.  u rows are
+// staged in LDS by the caller.
+template <typename T, int CPRH, int NT>
+__device__ __forceinline__ void shared_rows(const T* __restrict__ ws13, int Is, int i0, int i1,
+                                            int gw, int nw, u32x4 (&wg)[Geo<T, CPRH>::CPL],
+                                            u32x4 (&wu)[Geo<T, CPRH>::CPL], const float* lds_u,
+                                            int k, int B, const Routing& rt, float* As, int lane) {
+  int su = i0 + gw;
+  if (su >= i1) return;
+  while (true) {
+    gateup_unit<T, CPRH, NT>(wg, wu, lds_u, 0, B, su, Is, k, true, rt, As, lane);
+    su += nw;
+    if (su >= i1) break;
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
+  }
+}
+
+// Logit partials part[s][t][e] over `splits` K-slices (one (expert, slice) unit per wave,
+// h32 read from L2); with ws13 != nullptr the launch also streams the shared expert's
+// gate/up rows [0, i_split), each wave's first row pair requested before the logit work so
+// HBM stays busy through this latency-bound phase.
+template <typename T, int CPS, int CPRH, int NT>
 __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
     const float* __restrict__ h32, const T* __restrict__ w_r, int H, int E, int B, int splits,
-    float* __restrict__ part) {
+    float* __restrict__ part, const T* __restrict__ ws13, int Is, int i_split, int k, Routing rt,
+    float* __restrict__ As) {
   using G = Geo<T, CPS>;
+  using GH = Geo<T, CPRH>;
+  extern __shared__ float lds[];  // u [B][H] when the shared rows are streamed here
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
+  const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
+  const bool shared = ws13 != nullptr;
+  u32x4 wg[GH::CPL], wu[GH::CPL];
+  if (shared && gw < i_split) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
   const int units = E * splits;
-  for (int unit = blockIdx.x * wpb + wave; unit < units; unit += gridDim.x * wpb) {
+  for (int unit = gw; unit < units; unit += nw) {
     const int e = unit / splits, s = unit - e * splits;
     u32x4 w[G::CPL];
     load_row<T, CPS>(w_r + (size_t)e * H + (size_t)s * G::K, lane, w);
@@ -155,15 +183,19 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
       if (lane == 0) part[((size_t)s * B + t) * E + e] = acc;
     }
   }
+  if (!shared) return;
+  stage_rows_f32(lds, h32, B * GH::K);
+  __syncthreads();
+  shared_rows<T, CPRH, NT>(ws13, Is, 0, i_split, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
 
 // Block 0: top-k, gates and routing tables from the logit partials.  Blocks 1..: the shared
-// expert's gate/up over all B tokens (ws13 != nullptr), so its weight stream overlaps the
-// serial top-k without any cross-block communication.
+// expert's gate/up rows [i_split, Is) over all B tokens (ws13 != nullptr), so its weight
+// stream overlaps the serial top-k without any cross-block communication.
 template <typename T, int CPRH, int NT>
 __global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
     const float* __restrict__ part, int splits, const float* __restrict__ bias, int E, int k,
-    int B, float routed_scale, Routing rt, const T* __restrict__ ws13, int Is,
+    int B, float routed_scale, Routing rt, const T* __restrict__ ws13, int Is, int i_split,
     const float* __restrict__ h32, float* __restrict__ As) {
   using GH = Geo<T, CPRH>;
   extern __shared__ float lds[];  // blocks >= 1: u [B][H]
@@ -174,19 +206,12 @@ __global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
   const int nw = (gridDim.x - 1) * wpb;
-  int su = (blockIdx.x - 1) * wpb + wave;
+  const int gw = (blockIdx.x - 1) * wpb + wave;
   u32x4 wg[GH::CPL], wu[GH::CPL];
-  if (su < Is) load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
+  if (i_split + gw < Is) load_pair<T, CPRH>(ws13, 0, i_split + gw, Is, wg, wu, lane);
   stage_rows_f32(lds, h32, B * GH::K);
   __syncthreads();
-  if (su >= Is) return;
-  while (true) {
-    gateup_unit<T, CPRH, NT>(wg, wu, lds, 0, B, su, Is, k, true, rt, As, lane);
-    su += nw;
-    if (su >= Is) break;
-    __builtin_amdgcn_sched_barrier(0);
-    load_pair<T, CPRH>(ws13, 0, su, Is, wg, wu, lane);
-  }
+  shared_rows<T, CPRH, NT>(ws13, Is, i_split, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
 
 // ------------------------------------------------------------------------------ gate / up
@@ -408,15 +433,22 @@ hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const 
   return hipGetLastError();
 }
 
-template <typename T, int CPS>
+// Shared expert rows streamed by the logits launch (the rest go with the top-k launch).
+inline int shared_split(const Shape& s) { return s.Is / 2; }
+
+template <typename T, int CPS, int CPRH>
 hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* h32,
-                           const void* w_r, float* part, hipStream_t st) {
+                           const void* w_r, float* part, const void* ws13, const Routing& rt,
+                           float* As, hipStream_t st) {
   const int splits = s.H / Geo<T, CPS>::K;
   const int units = s.E * splits;
-  const int blocks = (units + 7) / 8;
-  auto kern = B == 1 ? router_logits_kernel<T, CPS, 1> : router_logits_kernel<T, CPS, 2>;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), 0, st, h32, (const T*)w_r, s.H, s.E,
-                     B, splits, part);
+  const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
+  auto kern = B == 1 ? router_logits_kernel<T, CPS, CPRH, 1> : router_logits_kernel<T, CPS, CPRH, 2>;
+  allow_lds(kern, lds);
+  int blocks = (units + 7) / 8;
+  if (ws13 && blocks < d.num_cu) blocks = d.num_cu;
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, s.H, s.E,
+                     B, splits, part, (const T*)ws13, s.Is, ws13 ? shared_split(s) : 0, s.k, rt, As);
   return hipGetLastError();
 }
 
@@ -430,7 +462,8 @@ hipError_t topk_shared_t(const Shape& s, const Device& d, int B, const float* pa
   allow_lds(kern, lds);
   const int blocks = ws13 ? 1 + d.num_cu : 1;
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, part, splits, bias, s.E, s.k,
-                     B, s.routed_scale, rt, (const T*)ws13, s.Is, h32, As);
+                     B, s.routed_scale, rt, (const T*)ws13, s.Is, ws13 ? shared_split(s) : s.Is,
+                     h32, As);
   return hipGetLastError();
 }
 
@@ -500,9 +533,12 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 }
 
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
-                                const void* w_r, float* part, hipStream_t st) {
-  if (s.dtype == 1 && s.H == 7168) return router_logits_t<uint16_t, 128>(s, d, B, h32, w_r, part, st);
-  if (s.dtype == 0 && s.H == 256) return router_logits_t<float, 64>(s, d, B, h32, w_r, part, st);
+                                const void* w_r, float* part, const void* ws13, const Routing& rt,
+                                float* As, hipStream_t st) {
+  if (s.dtype == 1 && s.H == 7168)
+    return router_logits_t<uint16_t, 128, 896>(s, d, B, h32, w_r, part, ws13, rt, As, st);
+  if (s.dtype == 0 && s.H == 256)
+    return router_logits_t<float, 64, 64>(s, d, B, h32, w_r, part, ws13, rt, As, st);
   return hipErrorInvalidValue;
 }
 

@@ -48,12 +48,14 @@ bool gemv_supported(const Shape& s, int B);
 hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void* x, const void* r,
                              const void* w_o, float* h32, void* h_out, hipStream_t st);
 
-// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s].
+// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s].  With ws13 !=
+// nullptr the same launch computes the first half of the shared expert's gate/up rows,
+// As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t); launch_topk_shared does the rest.
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
-                                const void* w_r, float* partials, hipStream_t st);
+                                const void* w_r, float* partials, const void* ws13,
+                                const Routing& rt, float* As, hipStream_t st);
 // Top-k, gates and routing tables from the partials (one block); with ws13 != nullptr the
-// same launch computes the shared expert's gate/up in its other blocks:
-// As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).
+// same launch computes the second half of the shared expert's gate/up in its other blocks.
 hipError_t launch_topk_shared(const Shape& s, const Device& d, int B, const float* partials,
                               const float* bias, const Routing& rt, const void* ws13,
                               const float* h32, float* As, hipStream_t st);
