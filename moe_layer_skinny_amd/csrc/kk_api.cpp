@@ -119,11 +119,13 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
   return KK_OK;
 }
 
-const char* kernel_names[] = {"oproj_gemv", "router_logits", "gateup_gemv_shared",
+const char* kernel_names[] = {"oproj_gemv",  "router_logits", "gateup_gemv_shared",
                               "gateup_gemv_routed", "down_gemv", "moe_prep", "topk_shared",
-                              "topk", "combine"};
+                              "topk",        "combine",       "oproj_mfma", "oproj_reduce",
+                              "router_mfma", "gateup_mfma",   "down_mfma"};
 enum KName {
-  K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK, K_COMBINE
+  K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK, K_COMBINE,
+  K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA
 };
 
 struct TimingRec {
@@ -175,7 +177,7 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   if (f == -2) return fail(KK_ERR_INVALID_ARG, "KK_FORCE_PLAN must be 'gemv' or 'mfma'");
   p->forced = f >= 0;
   p->path = f >= 0 ? f : (B <= 2 ? KK_PATH_GEMV : KK_PATH_SPLITK_MFMA);
-  p->streams = 2;
+  p->streams = 1;
   if (p->path == KK_PATH_GEMV) {
     if (!kk::gemv_supported(c->shape, B))
       return fail(KK_ERR_UNSUPPORTED, "GEMV path has no kernels for batch %d of this shape", B);
@@ -187,11 +189,16 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
     p->router_splitk = kk::router_gemv_splits(c->shape);
     // oproj, router logits, top-k || shared gate/up, routed gate/up, down, combine
     p->kernels_per_step = 6;
-    p->streams = 1;
     return KK_OK;
   }
-  return fail(KK_ERR_UNSUPPORTED, "the split-K MFMA path (batch %d) is not built in this library",
-              B);
+  if (!kk::mfma_supported(c->shape, B))
+    return fail(KK_ERR_UNSUPPORTED, "split-K MFMA path has no kernels for batch %d of this shape",
+                B);
+  p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
+  p->router_splitk = kk::mfma_router_splits(c->shape);
+  // oproj, reduce, router logits, top-k, grouped gate/up, grouped down, combine
+  p->kernels_per_step = 7;
+  return KK_OK;
 }
 
 hipEvent_t pool_event(kk_ctx* c) {
@@ -237,6 +244,7 @@ struct WsPtrs {
   float* As;
   float* Y;
   float* ys;
+  float* oproj_part;
 };
 
 WsPtrs carve(const kk_ctx* c, void* ws) {
@@ -246,7 +254,7 @@ WsPtrs carve(const kk_ctx* c, void* ws) {
                 (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
                 (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
                 (float*)(b + L.A),         (float*)(b + L.As),         (float*)(b + L.Y),
-                (float*)(b + L.ys)};
+                (float*)(b + L.ys),         (float*)(b + L.oproj_part)};
 }
 
 kk_status check_common(const kk_ctx* c, int B, void* ws) {
@@ -275,12 +283,59 @@ kk_status check_common(const kk_ctx* c, int B, void* ws) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-// ---- step pieces (GEMV path) ----------------------------------------------------------
+// ---- step pieces ------------------------------------------------------------------------
 kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h32, void* h_out,
-                        hipStream_t s) {
-  KK_HIP(timed(c, K_OPROJ, s,
-               [&] { return kk::launch_oproj_gemv(c->shape, c->dev, B, x, r, c->w.w_o, h32, h_out, s); }),
+                        float* part, int path, hipStream_t s) {
+  if (path == KK_PATH_GEMV) {
+    KK_HIP(timed(c, K_OPROJ, s,
+                 [&] {
+                   return kk::launch_oproj_gemv(c->shape, c->dev, B, x, r, c->w.w_o, h32, h_out, s);
+                 }),
+           "oproj launch");
+    return KK_OK;
+  }
+  KK_HIP(timed(c, K_OPROJ_MFMA, s,
+               [&] { return kk::launch_oproj_mfma(c->shape, c->dev, B, x, part, c->w.w_o, s); }),
          "oproj launch");
+  KK_HIP(timed(c, K_OPROJ_REDUCE, s,
+               [&] { return kk::launch_oproj_reduce(c->shape, B, part, r, h32, h_out, s); }),
+         "oproj reduce launch");
+  return KK_OK;
+}
+
+// MFMA path: router logits, top-k / tables (one block).
+kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                              float* logit_part, hipStream_t s) {
+  KK_HIP(timed(c, K_ROUTER_MFMA, s,
+               [&] { return kk::launch_router_mfma(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s); }),
+         "router logits launch");
+  KK_HIP(timed(c, K_TOPK, s,
+               [&] {
+                 return kk::launch_topk_shared(c->shape, c->dev, B, logit_part, c->w.bias, rt,
+                                               nullptr, h32, nullptr, s);
+               }),
+         "top-k launch");
+  return KK_OK;
+}
+
+// MFMA path: grouped gate/up and down over the active experts plus the shared one, combine.
+kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                               const WsPtrs& p, void* out, hipStream_t s) {
+  KK_HIP(timed(c, K_GU_MFMA, s,
+               [&] {
+                 return kk::launch_gateup_mfma(c->shape, c->dev, B, h32, c->w.w13, c->w.ws13, rt,
+                                               p.A, p.As, s);
+               }),
+         "gate/up launch");
+  KK_HIP(timed(c, K_DOWN_MFMA, s,
+               [&] {
+                 return kk::launch_down_mfma(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
+                                             p.Y, p.ys, s);
+               }),
+         "down launch");
+  KK_HIP(timed(c, K_COMBINE, s,
+               [&] { return kk::launch_combine(c->shape, B, h32, p.Y, p.ys, rt, out, s); }),
+         "combine launch");
   return KK_OK;
 }
 
@@ -339,12 +394,17 @@ kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const k
 }
 
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
-                        float* gate, void* ws, hipStream_t s, bool two_stream) {
+                        float* gate, void* ws, hipStream_t s, bool two_stream, int path) {
   WsPtrs p = carve(c, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act};
-  kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, s);
+  kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, path, s);
   if (st != KK_OK) return st;
+  if (path == KK_PATH_SPLITK_MFMA) {
+    st = enqueue_router_mfma(c, B, p.h32, rt, p.logit_part, s);
+    if (st != KK_OK) return st;
+    return enqueue_experts_mfma(c, B, p.h32, rt, p, out, s);
+  }
   if (!two_stream) {
     // the shared expert's gate/up streams inside the top-k launch
     st = enqueue_router(c, B, p.h32, rt, p.logit_part, c->w.ws13, p.As, s);
@@ -483,7 +543,8 @@ kk_status kk_oproj_residual(kk_ctx* c, int32_t B, const void* x, const void* res
     if (h_out && misaligned(h_out)) return fail(KK_ERR_INVALID_ARG, "h_out is not 16-byte aligned");
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
-    return enqueue_oproj(c, B, x, resid, h32, h_out, (hipStream_t)stream);
+    WsPtrs p = carve(c, ws);
+    return enqueue_oproj(c, B, x, resid, h32, h_out, p.oproj_part, plan.path, (hipStream_t)stream);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_oproj_residual");
   }
@@ -504,6 +565,8 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     WsPtrs p = carve(c, ws);
     kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
+    if (plan.path == KK_PATH_SPLITK_MFMA)
+      return enqueue_router_mfma(c, B, h32, rt, p.logit_part, (hipStream_t)stream);
     return enqueue_router(c, B, h32, rt, p.logit_part, nullptr, nullptr, (hipStream_t)stream);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_router_topk");
@@ -530,6 +593,7 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
                    (int32_t*)perm, p.inv_perm, p.act, p.n_act};
     KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
            "moe prep launch");
+    if (plan.path == KK_PATH_SPLITK_MFMA) return enqueue_experts_mfma(c, B, h32, rt, p, out, s);
     st = enqueue_shared_gateup(c, B, h32, rt, p.As, s);
     if (st != KK_OK) return st;
     return enqueue_routed_and_combine(c, B, h32, rt, p, out, s);
@@ -552,10 +616,13 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     if (flags & ~(KK_GRAPH | KK_TWO_STREAM))
       return fail(KK_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     const bool two = (flags & KK_TWO_STREAM) != 0;
-    kk_plan plan;
-    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    kk_plan plan0;
+    if ((st = plan_for(c, B, &plan0)) != KK_OK) return st;
+    if (two && plan0.path != KK_PATH_GEMV)
+      return fail(KK_ERR_UNSUPPORTED, "KK_TWO_STREAM applies to the GEMV path (batch 1-2)");
     hipStream_t s = (hipStream_t)stream;
-    if (!(flags & KK_GRAPH)) return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two);
+    if (!(flags & KK_GRAPH))
+      return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two, plan0.path);
     if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
     ++c->clock;
     for (auto& g : c->graphs) {
@@ -574,7 +641,7 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
       c->graphs.erase(c->graphs.begin() + lru);
     }
     KK_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
-    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two);
+    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two, plan0.path);
     hipGraph_t graph = nullptr;
     hipError_t e = hipStreamEndCapture(s, &graph);
     if (st != KK_OK) {

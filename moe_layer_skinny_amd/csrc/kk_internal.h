@@ -80,4 +80,25 @@ hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* 
 // act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
 
+// ---- split-K MFMA path (batch 3..64) ---------------------------------------------------
+bool mfma_supported(const Shape& s, int B);
+int mfma_oproj_splits(const Shape& s);
+int mfma_router_splits(const Shape& s);
+// o-proj partials part[sp][t][n] over the K slices, then h32 = r + sum (and h_out).
+hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x, float* part,
+                             const void* w_o, hipStream_t st);
+hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const void* r,
+                               float* h32, void* h_out, hipStream_t st);
+// Router logit partials from h32 (three bf16 terms per fp32 value).
+hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const float* h32,
+                              const void* w_r, float* part, hipStream_t st);
+// Grouped gate/up (routed experts and the shared expert) -> A, As.
+hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
+                              const void* w13, const void* ws13, const Routing& rt, float* A,
+                              float* As, hipStream_t st);
+// Grouped down-projection -> Y (per position), ys (shared).
+hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
+                            const float* As, const void* w2, const void* ws2, const Routing& rt,
+                            float* Y, float* ys, hipStream_t st);
+
 }  // namespace kk

@@ -1,0 +1,164 @@
+"""GPU parity of the split-K MFMA path (batch 3-64) against the fp64 oracle.
+
+Routing tables are compared for every token; outputs are compared on every token except at
+full size and batch 64, where the oracle evaluates sampled tokens only (routing is still
+computed for all 64, and those tokens' experts are regenerated on the host).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from tests.gpu_common import (as_f64_out, assert_close, assert_routing_equal, gpu_layer, log,
+                              oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+MFMA_CASES = [("tp_rank", 8), ("tp_rank", 64), ("full_b8", 8), ("full_b64", 64)]
+SAMPLE = {("full_b64", 64): (0, 21, 42, 63)}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bufs(cfg, B):
+    torch = _torch()
+    return {
+        "h32": torch.empty(B, cfg.hidden, dtype=torch.float32, device="cuda"),
+        "h_out": torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda"),
+        "out": torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda"),
+        "idx": torch.full((B, cfg.top_k), -1, dtype=torch.int32, device="cuda"),
+        "gate": torch.zeros(B, cfg.top_k, dtype=torch.float32, device="cuda"),
+        "offsets": torch.full((cfg.n_experts + 1,), -1, dtype=torch.int32, device="cuda"),
+        "perm": torch.full((B * cfg.top_k,), -1, dtype=torch.int32, device="cuda"),
+    }
+
+
+def _ref(name, B):
+    toks = SAMPLE.get((name, B))
+    return oracle_step(name, B, toks), (list(range(B)) if toks is None else list(toks))
+
+
+@pytest.mark.parametrize("name,B", MFMA_CASES)
+def test_plan_is_mfma(name, B):
+    log(f"[plan-mfma] {name} B={B}")
+    _, _, L = gpu_layer(name)
+    p = L.query_plan(B)
+    assert p["path_name"] == "splitk_mfma" and p["forced"] == 0
+    assert p["kernels_per_step"] == 7 and p["oproj_splitk"] == 7
+
+
+@pytest.mark.parametrize("name,B", MFMA_CASES)
+def test_per_op_parity_mfma(name, B):
+    log(f"[ops-mfma] {name} B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(name)
+    ref, toks = _ref(name, B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.oproj_residual(B, x, r, b["h32"], ws, h_out=b["h_out"], stream=s)
+        L.router_topk(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], ws, stream=s)
+        L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws, stream=s)
+    s.synchronize()
+    assert_close(b["h32"].cpu().numpy().astype(np.float64), ref["h"], "h32")
+    assert_close(as_f64_out(b["h_out"]), ref["h"], "h_out")
+    got = {"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy(),
+           "offsets": b["offsets"].cpu().numpy(), "perm": b["perm"].cpu().numpy()}
+    assert_routing_equal(got, ref, B, cfg.top_k, "router")
+    rep = assert_close(as_f64_out(b["out"])[toks], ref["out"][toks], "moe out")
+    log(f"[ops-mfma] {name} B={B} out: {rep}")
+
+
+@pytest.mark.parametrize("name,B", MFMA_CASES)
+def test_layer_parity_mfma(name, B):
+    log(f"[layer-mfma] {name} B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(name)
+    ref, toks = _ref(name, B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s)
+    s.synchronize()
+    eager = b["out"].clone()
+    rep = assert_close(as_f64_out(eager)[toks], ref["out"][toks], "layer out")
+    assert_routing_equal({"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy()},
+                         ref, B, cfg.top_k, "layer routing")
+    log(f"[layer-mfma] {name} B={B} out: {rep}")
+    for rep_i in range(3):
+        b["out"].zero_()
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s, graph=rep_i > 0)
+        s.synchronize()
+        assert torch.equal(b["out"], eager), f"replay {rep_i} differs (bitwise)"
+
+
+@pytest.mark.parametrize("B", [3, 5])
+def test_odd_batches_mfma(B):
+    log(f"[odd-mfma] tp_rank B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer("tp_rank")
+    ref = oracle_step("tp_rank", B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    assert L.query_plan(B)["path_name"] == "splitk_mfma"
+    L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"])
+    torch.cuda.synchronize()
+    assert_close(as_f64_out(b["out"]), ref["out"], "layer out")
+    np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["topk_idx"])
+
+
+def test_forced_plans_are_visible_and_agree():
+    log("[forced] tp_rank B=2 mfma, B=8 gemv")
+    torch = _torch()
+    import synth.device as sd
+    from moe_layer_skinny_amd import kk
+    cfg, _, L = gpu_layer("tp_rank")
+    ref = oracle_step("tp_rank", 2)
+    x, r, _, _ = sd.device_tokens(cfg, 2)
+    b = _bufs(cfg, 2)
+    ws = L.new_workspace()
+    os.environ["KK_FORCE_PLAN"] = "mfma"
+    try:
+        p = L.query_plan(2)
+        assert p["path_name"] == "splitk_mfma" and p["forced"] == 1
+        L.layer_decode(2, x, r, b["out"], ws, b["idx"], b["gate"])
+        torch.cuda.synchronize()
+        assert_close(as_f64_out(b["out"]), ref["out"], "forced mfma out")
+        np.testing.assert_array_equal(b["idx"].cpu().numpy(), ref["topk_idx"])
+        os.environ["KK_FORCE_PLAN"] = "gemv"
+        with pytest.raises(kk.KKError) as e:
+            L.query_plan(8)
+        assert e.value.status == kk.KK_ERR_UNSUPPORTED
+        os.environ["KK_FORCE_PLAN"] = "bogus"
+        with pytest.raises(kk.KKError) as e:
+            L.query_plan(1)
+        assert e.value.status == kk.KK_ERR_INVALID_ARG
+    finally:
+        del os.environ["KK_FORCE_PLAN"]
+    assert L.query_plan(2)["forced"] == 0
+
+
+def test_two_stream_flag_rejected_on_mfma_path():
+    log("[two-stream-mfma] tp_rank B=8")
+    torch = _torch()
+    from moe_layer_skinny_amd import kk
+    cfg, _, L = gpu_layer("tp_rank")
+    b = _bufs(cfg, 8)
+    ws = L.new_workspace()
+    x = torch.zeros(8, cfg.oproj_in, dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros(8, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kk.KKError) as e:
+        L.layer_decode(8, x, r, b["out"], ws, two_stream=True)
+    assert e.value.status == kk.KK_ERR_UNSUPPORTED
