@@ -2,21 +2,20 @@
 //
 // Every product is weights (A operand: 16 rows x 32 k) times activations (B operand: 32 k x
 // 16 tokens) into fp32 accumulators (D: 16 rows x 16 tokens).  Lane l of a wave holds row
-// (or token) l % 16 and k = 8 * (l / 16) + e of each operand.  Within a run of S MFMAs the
-// four lane groups take contiguous k sub-ranges, so each lane reads 16*S contiguous bytes of
-// its weight row per run (the same k mapping is used for both operands).
+// (or token) l % 16 and k = 8 * (l / 16) + e of each operand.  Operands are staged through
+// LDS: global loads stay row-contiguous (an operand read straight from HBM would touch 16
+// rows per quarter-wave), and the MFMA reads its 16-row layout out of LDS.
 //
 // fp32 activations (the residual stream h32 and the SwiGLU activations) enter the MFMA as
 // NTERM bf16 terms hi + lo (+ lo2) whose sum reproduces them (to 2^-17 relative with two
 // terms, exactly with three), so the products keep fp32-level accuracy; x is already bf16.
 //
 // Launches of one step:
-//   1. o-proj partials over 7 K-slices (one 16-row tile x one slice per wave)
-//   2. reduce: h32 = resid + sum of slices (fixed order), optional h_out
-//   3. router logit partials (three-term h32), then the shared top-k launch
-//   4. grouped gate/up over the active experts + the shared expert: the 8 waves of a block
-//      split K of one (expert, 16 gate rows, 16 up rows) unit and reduce through LDS;
-//      SwiGLU epilogue -> A (fp32, position-major)
+//   1. o-proj partials over 7 K chunks (32 rows x one chunk per block unit)
+//   2. reduce: h32 = resid + sum of chunks (fixed order), optional h_out
+//   3. router logit partials (three-term h32), then the top-k launch
+//   4. grouped gate/up over the active experts + the shared expert, one (expert, 16 gate
+//      rows, 16 up rows) unit per block over the whole K; SwiGLU epilogue -> A (fp32)
 //   5. grouped down-projection the same way -> Y (per position) and ys (shared)
 //   6. the combine launch shared with the GEMV path
 //
@@ -60,95 +59,6 @@ __device__ __forceinline__ void split_terms(const float (&x)[8], u32x4 (&out)[NT
   }
 }
 
-// One lane's B operand for k = kk .. kk+7 of an activation row (bf16 source: one term;
-// fp32 source: NTERM terms).  Invalid tokens read a valid row and are zeroed.
-template <int NTERM, bool BF16SRC>
-__device__ __forceinline__ void load_b(const void* row, int kk, bool valid, u32x4 (&out)[NTERM]) {
-  if constexpr (BF16SRC) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>((const uint16_t*)row + kk);
-    out[0] = valid ? v : u32x4{0u, 0u, 0u, 0u};
-  } else {
-    const float4* p = reinterpret_cast<const float4*>((const float*)row + kk);
-    const float4 a = p[0], b = p[1];
-    float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    if (!valid)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    split_terms<NTERM>(x, out);
-  }
-}
-
-// acc[r][tt] += W[rows of tile r][k_begin, k_end) . X[tokens of tile tt][k_begin, k_end).
-// wrow[r]: this lane's weight row of tile r; arow[tt]/aval[tt]: this lane's token row.
-template <int NR, int TT, int NTERM, bool BF16SRC, int S>
-__device__ __forceinline__ void mfma_span(const uint16_t* const (&wrow)[NR],
-                                          const void* const (&arow)[TT], const bool (&aval)[TT],
-                                          int ntt, int k_begin, int k_end, int g,
-                                          f32x4 (&acc)[NR][TT]) {
-  for (int k0 = k_begin; k0 < k_end; k0 += 32 * S) {
-    const int kl = k0 + g * 8 * S;
-    u32x4 wv[NR][S];
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int s = 0; s < S; ++s)
-        wv[r][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[r] + kl + 8 * s));
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        if (tt < ntt) {
-          u32x4 bv[NTERM];
-          load_b<NTERM, BF16SRC>(arow[tt], kl + 8 * s, aval[tt], bv);
-#pragma unroll
-          for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int q = 0; q < NTERM; ++q) acc[r][tt] = mfma(wv[r][s], bv[q], acc[r][tt]);
-        }
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------ split-K
-// part[sp][t][n] = W[n][slice sp] . X[t][slice sp] for N rows (one 16-row tile per wave unit).
-template <int TT, int NTERM, bool BF16SRC, int S>
-__global__ __launch_bounds__(256) void mfma_splitk_kernel(const uint16_t* __restrict__ W, int N,
-                                                          int K, const void* __restrict__ act,
-                                                          int B, int splits,
-                                                          float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int unit = blockIdx.x * (blockDim.x >> 6) + wave;
-  const int tiles = N / 16;
-  if (unit >= tiles * splits) return;
-  const int tile = unit / splits, sp = unit - tile * splits;
-  const int kspan = K / splits;
-  const int g = lane >> 4, c = lane & 15;
-  const uint16_t* wrow[1] = {W + (size_t)(tile * 16 + c) * K};
-  const void* arow[TT];
-  bool aval[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int j = tt * 16 + c;
-    aval[tt] = j < B;
-    const size_t off = (size_t)(aval[tt] ? j : 0) * K;
-    arow[tt] = BF16SRC ? (const void*)((const uint16_t*)act + off) : (const void*)((const float*)act + off);
-  }
-  const int ntt = (B + 15) / 16;
-  f32x4 acc[1][TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[0][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mfma_span<1, TT, NTERM, BF16SRC, S>(wrow, arow, aval, ntt, sp * kspan, (sp + 1) * kspan, g, acc);
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    const int j = tt * 16 + c;
-    if (tt < ntt && j < B) {
-      float4 v = {acc[0][tt][0], acc[0][tt][1], acc[0][tt][2], acc[0][tt][3]};
-      *reinterpret_cast<float4*>(part + ((size_t)sp * B + j) * N + tile * 16 + 4 * g) = v;
-    }
-  }
-}
-
 // h32[t][n] = r[t][n] + sum_sp part[sp][t][n] (slice order); h_out = RNE(h32) if given.
 template <typename T, int MAXS>
 __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restrict__ part,
@@ -168,145 +78,213 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restri
   if (h_out) Elem<T>::store(h_out, i, hv);
 }
 
-// ------------------------------------------------------------------------------ grouped experts
-// Group a < n_act: routed expert act[a] over its positions [offsets[e], offsets[e+1]);
-// group n_act: the shared expert over tokens 0..B-1.  A unit is (group, row tile pair); the
-// KW waves of a block each take K/KW of it and the partial tiles are summed through LDS in
-// wave order.
-//   MODE 0 (gate/up): rows i0+c of W1 and I+i0+c of W3 (K = H, activations h32 rows of the
-//                     tokens); epilogue A[p][i] = silu(gate) * up (As[t][i] for shared).
-//   MODE 1 (down):    rows n0+c and n0+16+c of W2 (K = I, activations A rows of the
-//                     positions / As rows); epilogue Y[p][n] (ys[t][n] for shared).
-struct ExpertArgs {
-  const uint16_t* w_routed;  // w13 or w2
-  const uint16_t* w_shared;  // ws13 or ws2
-  const float* act_routed;   // MODE 0: h32 [B][H]; MODE 1: A [B*k][I]
-  const float* act_shared;   // MODE 0: h32;        MODE 1: As [B][Is]
-  float* out_routed;         // MODE 0: A [B*k][I]; MODE 1: Y [B*k][H]
-  float* out_shared;         // MODE 0: As [B][Is]; MODE 1: ys [B][H]
+// Arguments of the grouped / split-K launches.
+struct UnitArgs {
+  const uint16_t* w_routed;  // MODE 0: w13; MODE 1: w2; MODE 2: the weight matrix [N][K]
+  const uint16_t* w_shared;  // MODE 0: ws13; MODE 1: ws2
+  const void* act_routed;    // MODE 0: h32 [B][H]; MODE 1: A [B*k][I]; MODE 2: X [B][K]
+  const float* act_shared;   // MODE 0: h32; MODE 1: As [B][Is]
+  float* out_routed;         // MODE 0: A; MODE 1: Y [B*k][H]; MODE 2: part [chunks][B][N]
+  float* out_shared;         // MODE 0: As; MODE 1: ys [B][H]
   int H, I, k, B;
+  int N, K, chunks;          // MODE 2
   Routing rt;
 };
 
-template <int MODE, int KW, int TT, int S>
-__global__ __launch_bounds__(KW * 64) void mfma_expert_kernel(ExpertArgs x) {
-  constexpr int NR = 2;
-  extern __shared__ f32x4 red[];  // [KW][NR][TT][64] when KW > 1
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// ------------------------------------------------------------------------------ LDS-staged
+// All MFMA launches share one kernel.  A unit is (group, pair of 16-row tiles, K chunk):
+//   MODE 0 (gate/up): group a < n_act is routed expert act[a] over its positions, group
+//     n_act the shared expert over tokens 0..B-1; tiles = W1 rows i0.. and W3 rows I+i0..;
+//     K = H in one chunk; epilogue A[p][i] = silu(gate) * up (As[t][i] for shared).
+//   MODE 1 (down): same groups; tiles = W2 rows n0.. and n0+16..; K = I in one chunk;
+//     epilogue Y[p][n] (ys[t][n] for shared).
+//   MODE 2 (split-K): one group, tokens 0..B-1; tiles = rows n0.. and n0+16.. of W [N][K];
+//     chunk c of K -> part[c][t][n].
+// The chunk is walked in stages of KS.  Each stage the 256 threads load the tile pair's 32
+// rows x KS (every quarter-wave reading 256 contiguous bytes of one row) and the group's
+// token rows x KS (bf16 as is, or fp32 split into NTERM bf16 terms on the way into LDS),
+// then the four waves multiply (k-step, token tile) pairs out of LDS while the next stage's
+// loads are in flight.  Each wave's partial tiles are summed through LDS in wave order at
+// the end of the unit.
+//   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
+//   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC>
+__global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
+  constexpr int K8 = KS / 8;
+  constexpr int WP = K8 + 1;
+  constexpr int NTOK = 16 * TT;
+  constexpr int W_CH = 32 * WP;
+  constexpr int WLD = (32 * K8 + 255) / 256;    // weight chunks per thread per stage
+  constexpr int ALD = (NTOK * K8 + 255) / 256;  // activation chunks (8 values) per thread
+  constexpr int KSTEPS = KS / 32;
+  constexpr int AW = BF16SRC ? 1 : 2;           // 16-byte words per activation chunk
+  extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
+  u32x4* lw = lds;
+  u32x4* la = lds + W_CH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n_act = *x.rt.n_act;
-  const int K = MODE == 0 ? x.H : x.I;
-  const int out_rows = MODE == 0 ? x.I : x.H;          // per group
-  const int tiles = MODE == 0 ? x.I / 16 : x.H / 32;    // units per group
+  const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
+  const int K = MODE == 0 ? x.H : (MODE == 1 ? x.I : x.K);
+  const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
+  const int tiles = MODE == 0 ? x.I / 16 : out_rows / 32;
+  const int chunks = MODE == 2 ? x.chunks : 1;
   const size_t wstride = MODE == 0 ? (size_t)2 * x.I * x.H : (size_t)x.H * x.I;
-  const int units = (n_act + 1) * tiles;
-  const int kspan = K / KW;
+  const int units = n_groups * tiles * chunks;
+  const int kchunk = K / chunks;
+  const int nst = kchunk / KS;
 
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int a = unit / tiles, tile = unit - a * tiles;
-    const bool shared = a == n_act;
+    const int a = unit / (tiles * chunks);
+    const int rem = unit - a * tiles * chunks;
+    const int tile = rem / chunks, chunk = rem - tile * chunks;
+    const bool shared = MODE != 2 && a == n_groups - 1;
     int p0 = 0, cnt = x.B;
-    const uint16_t* wbase = x.w_shared;
-    if (!shared) {
+    const uint16_t* wbase = shared ? x.w_shared : x.w_routed;
+    if (MODE != 2 && !shared) {
       const int e = x.rt.act[a];
       p0 = x.rt.offsets[e];
       cnt = x.rt.offsets[e + 1] - p0;
       wbase = x.w_routed + (size_t)e * wstride;
     }
     const int ntt = (cnt + 15) / 16;
-    const uint16_t* wrow[NR];
-    int row0;
-    if (MODE == 0) {
-      row0 = tile * 16;
-      wrow[0] = wbase + (size_t)(row0 + c) * K;
-      wrow[1] = wbase + (size_t)(x.I + row0 + c) * K;
-    } else {
-      row0 = tile * 32;
-      wrow[0] = wbase + (size_t)(row0 + c) * K;
-      wrow[1] = wbase + (size_t)(row0 + 16 + c) * K;
-    }
-    const void* arow[TT];
-    bool aval[TT];
+    const int row0 = MODE == 0 ? tile * 16 : tile * 32;
+    const int kbase = chunk * kchunk;
+    // this thread's weight chunks: q = tid + 256 i -> (row q / K8, chunk q % K8)
+    const uint16_t* wsrc[WLD];
 #pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int j = tt * 16 + c;
-      aval[tt] = j < cnt;
-      const int jj = aval[tt] ? j : 0;
-      int src;  // activation row
+    for (int i = 0; i < WLD; ++i) {
+      const int q = min(tid + 256 * i, 32 * K8 - 1), rr = q / K8, ch = q - rr * K8;
+      const int wr = MODE == 0 ? (rr < 16 ? row0 + rr : x.I + row0 + rr - 16) : row0 + rr;
+      wsrc[i] = wbase + (size_t)wr * K + kbase + ch * 8;
+    }
+    // this thread's activation chunks: q = tid + 256 i -> (token slot q / K8, chunk q % K8)
+    const void* asrc[ALD];
+    bool aok[ALD];
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      const int q = min(tid + 256 * i, NTOK * K8 - 1), j = q / K8, ch = q - j * K8;
+      aok[i] = j < cnt;
+      const int jj = aok[i] ? j : 0;
+      int src;
       if (MODE == 0)
-        src = shared ? jj : x.rt.perm[p0 + jj] / x.k;  // token rows of h32
+        src = shared ? jj : x.rt.perm[p0 + jj] / x.k;
+      else if (MODE == 1)
+        src = shared ? jj : p0 + jj;
       else
-        src = shared ? jj : p0 + jj;                   // position rows of A / token rows of As
-      const float* base = MODE == 0 ? x.act_routed : (shared ? x.act_shared : x.act_routed);
-      arow[tt] = base + (size_t)src * K;
+        src = jj;
+      const void* base = (MODE == 1 && shared) ? (const void*)x.act_shared : x.act_routed;
+      const size_t off = (size_t)src * K + kbase + ch * 8;
+      asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
     }
-    f32x4 acc[NR][TT];
+    u32x4 wreg[WLD], areg[ALD][AW];
+    auto load_stage = [&](int st) {
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
+      for (int i = 0; i < WLD; ++i)
+        wreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + st * KS));
+#pragma unroll
+      for (int i = 0; i < ALD; ++i) {
+        const u32x4* p = BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
+                                 : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
+#pragma unroll
+        for (int w = 0; w < AW; ++w) areg[i][w] = p[w];
+      }
+    };
+    f32x4 acc[2][TT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mfma_span<NR, TT, 2, false, S>(wrow, arow, aval, ntt, wave * kspan, (wave + 1) * kspan, g, acc);
 
-    float* outp = shared ? x.out_shared : x.out_routed;
-    const int pbase = shared ? 0 : p0;
-    if constexpr (KW == 1) {
+    load_stage(0);
+    for (int st = 0; st < nst; ++st) {
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int j = tt * 16 + c;
-        if (tt < ntt && j < cnt) {
-          float* o = outp + (size_t)(pbase + j) * out_rows + row0 + 4 * g;
-          if (MODE == 0) {
-            float4 v;
-            v.x = silu_f32(acc[0][tt][0]) * acc[1][tt][0];
-            v.y = silu_f32(acc[0][tt][1]) * acc[1][tt][1];
-            v.z = silu_f32(acc[0][tt][2]) * acc[1][tt][2];
-            v.w = silu_f32(acc[0][tt][3]) * acc[1][tt][3];
-            *reinterpret_cast<float4*>(o) = v;
+      for (int i = 0; i < WLD; ++i) {
+        const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+        if (q < 32 * K8) lw[rr * WP + ch] = wreg[i];
+      }
+#pragma unroll
+      for (int i = 0; i < ALD; ++i) {
+        const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
+        if (q < NTOK * K8) {
+          if constexpr (BF16SRC) {
+            la[ch * NTOK + j] = aok[i] ? areg[i][0] : u32x4{0u, 0u, 0u, 0u};
           } else {
-            *reinterpret_cast<float4*>(o) = float4{acc[0][tt][0], acc[0][tt][1], acc[0][tt][2], acc[0][tt][3]};
-            *reinterpret_cast<float4*>(o + 16) = float4{acc[1][tt][0], acc[1][tt][1], acc[1][tt][2], acc[1][tt][3]};
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = aok[i] ? __uint_as_float(areg[i][0][e]) : 0.f;
+              v[4 + e] = aok[i] ? __uint_as_float(areg[i][1][e]) : 0.f;
+            }
+            u32x4 terms[NTERM];
+            split_terms<NTERM>(v, terms);
+#pragma unroll
+            for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
           }
         }
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt) red[((wave * NR + r) * TT + tt) * 64 + lane] = acc[r][tt];
       __syncthreads();
-      // one thread per (tile slot tt, lane) sums the KW partial tiles in wave order
-      for (int idx = threadIdx.x; idx < TT * 64; idx += blockDim.x) {
-        const int tt = idx >> 6, ln = idx & 63;
-        const int j = tt * 16 + (ln & 15), gg = ln >> 4;
-        if (tt < ntt && j < cnt) {
-          f32x4 s0 = red[((0 * NR + 0) * TT + tt) * 64 + ln];
-          f32x4 s1 = red[((0 * NR + 1) * TT + tt) * 64 + ln];
-          for (int w = 1; w < KW; ++w) {
-            s0 += red[((w * NR + 0) * TT + tt) * 64 + ln];
-            s1 += red[((w * NR + 1) * TT + tt) * 64 + ln];
-          }
-          float* o = outp + (size_t)(pbase + j) * out_rows + row0 + 4 * gg;
-          if (MODE == 0) {
-            float4 v;
-            v.x = silu_f32(s0[0]) * s1[0];
-            v.y = silu_f32(s0[1]) * s1[1];
-            v.z = silu_f32(s0[2]) * s1[2];
-            v.w = silu_f32(s0[3]) * s1[3];
-            *reinterpret_cast<float4*>(o) = v;
-          } else {
-            *reinterpret_cast<float4*>(o) = float4{s0[0], s0[1], s0[2], s0[3]};
-            *reinterpret_cast<float4*>(o + 16) = float4{s1[0], s1[1], s1[2], s1[3]};
+      if (st + 1 < nst) load_stage(st + 1);
+      for (int pr = wave; pr < KSTEPS * ntt; pr += 4) {
+        const int ks = pr % KSTEPS, tt = pr / KSTEPS;
+        const u32x4 a0 = lw[c * WP + ks * 4 + g];
+        const u32x4 a1 = lw[(16 + c) * WP + ks * 4 + g];
+        u32x4 bq[NTERM];
+#pragma unroll
+        for (int q2 = 0; q2 < NTERM; ++q2) bq[q2] = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
+#pragma unroll
+        for (int t2 = 0; t2 < TT; ++t2) {
+          if (t2 == tt) {
+#pragma unroll
+            for (int q2 = 0; q2 < NTERM; ++q2) {
+              acc[0][t2] = mfma(a0, bq[q2], acc[0][t2]);
+              acc[1][t2] = mfma(a1, bq[q2], acc[1][t2]);
+            }
           }
         }
       }
       __syncthreads();
     }
+    // sum the four waves' partial tiles in wave order, then the epilogue
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) red[((wave * 2 + r) * TT + tt) * 64 + lane] = acc[r][tt];
+    __syncthreads();
+    float* outp = shared ? x.out_shared : x.out_routed;
+    for (int idx = tid; idx < TT * 64; idx += 256) {
+      const int tt = idx >> 6, ln = idx & 63;
+      const int j = tt * 16 + (ln & 15), gg = ln >> 4;
+      if (tt < ntt && j < cnt) {
+        f32x4 s0 = red[((0 * 2 + 0) * TT + tt) * 64 + ln];
+        f32x4 s1 = red[((0 * 2 + 1) * TT + tt) * 64 + ln];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+          s0 += red[((w * 2 + 0) * TT + tt) * 64 + ln];
+          s1 += red[((w * 2 + 1) * TT + tt) * 64 + ln];
+        }
+        float* o;
+        if (MODE == 2)
+          o = outp + ((size_t)chunk * x.B + j) * out_rows + row0 + 4 * gg;
+        else
+          o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
+        if (MODE == 0) {
+          *reinterpret_cast<float4*>(o) =
+              float4{silu_f32(s0[0]) * s1[0], silu_f32(s0[1]) * s1[1], silu_f32(s0[2]) * s1[2],
+                     silu_f32(s0[3]) * s1[3]};
+        } else {
+          *reinterpret_cast<float4*>(o) = float4{s0[0], s0[1], s0[2], s0[3]};
+          *reinterpret_cast<float4*>(o + 16) = float4{s1[0], s1[1], s1[2], s1[3]};
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename K>
-void allow_lds_mfma(K kernel) {
+template <typename Kern>
+void allow_lds_mfma(Kern kernel) {
   static thread_local const void* done[64];
   static thread_local int n_done = 0;
   for (int i = 0; i < n_done; ++i)
@@ -318,43 +296,34 @@ void allow_lds_mfma(K kernel) {
 
 inline int token_tiles(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
-template <int TT, int NTERM, bool BF16SRC, int S>
-hipError_t splitk_t(const uint16_t* W, int N, int K, const void* act, int B, int splits,
-                    float* part, hipStream_t st) {
-  const int units = (N / 16) * splits;
-  hipLaunchKernelGGL((mfma_splitk_kernel<TT, NTERM, BF16SRC, S>), dim3((units + 3) / 4), dim3(256),
-                     0, st, W, N, K, act, B, splits, part);
-  return hipGetLastError();
-}
-
-template <int NTERM, bool BF16SRC, int S>
-hipError_t splitk_dispatch(const uint16_t* W, int N, int K, const void* act, int B, int splits,
-                           float* part, hipStream_t st) {
-  switch (token_tiles(B)) {
-    case 1: return splitk_t<1, NTERM, BF16SRC, S>(W, N, K, act, B, splits, part, st);
-    case 2: return splitk_t<2, NTERM, BF16SRC, S>(W, N, K, act, B, splits, part, st);
-    default: return splitk_t<4, NTERM, BF16SRC, S>(W, N, K, act, B, splits, part, st);
-  }
-}
-
-template <int MODE, int KW, int TT, int S>
-hipError_t expert_t(const Device& d, const ExpertArgs& x, hipStream_t st) {
-  auto kern = mfma_expert_kernel<MODE, KW, TT, S>;
-  const size_t lds = KW > 1 ? (size_t)KW * 2 * TT * 64 * sizeof(f32x4) : 0;
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC>
+hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
+  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC>;
+  constexpr size_t lds_main = (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
+  constexpr size_t lds_red = (size_t)4 * 2 * TT * 64 * 16;
+  constexpr size_t lds = lds_main > lds_red ? lds_main : lds_red;
   if (lds > 64 * 1024) allow_lds_mfma(kern);
-  int bpc = KW >= 8 ? 2 : 16 / KW;
-  if (lds && (size_t)bpc * lds > 160 * 1024) bpc = (int)((160 * 1024) / lds);
-  if (bpc < 1) bpc = 1;
-  hipLaunchKernelGGL(kern, dim3(d.num_cu * bpc), dim3(KW * 64), lds, st, x);
+  // persistent grid: as many blocks as are resident at once (registers and LDS permitting)
+  static thread_local int bpc = 0;
+  if (bpc == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, lds) != hipSuccess || n < 1) n = 1;
+    bpc = n;
+  }
+  int grid = d.num_cu * bpc;
+  if (grid > max_units) grid = max_units;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x);
   return hipGetLastError();
 }
 
-template <int MODE, int KW, int S>
-hipError_t expert_dispatch(const Device& d, const ExpertArgs& x, hipStream_t st) {
+// Stage depth by token tiles: 256 k (1 tile), 128 (2), 64 (4); KMAX caps it (K = 448).
+template <int MODE, int NTERM, bool BF16SRC, int KMAX = 256>
+hipError_t staged_dispatch(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
+  constexpr int K1 = KMAX < 256 ? KMAX : 256, K2 = KMAX < 128 ? KMAX : 128;
   switch (token_tiles(x.B)) {
-    case 1: return expert_t<MODE, KW, 1, S>(d, x, st);
-    case 2: return expert_t<MODE, KW, 2, S>(d, x, st);
-    default: return expert_t<MODE, KW, 4, S>(d, x, st);
+    case 1: return staged_t<MODE, 1, K1, NTERM, BF16SRC>(d, x, max_units, st);
+    case 2: return staged_t<MODE, 2, K2, NTERM, BF16SRC>(d, x, max_units, st);
+    default: return staged_t<MODE, 4, 64, NTERM, BF16SRC>(d, x, max_units, st);
   }
 }
 
@@ -362,21 +331,28 @@ hipError_t expert_dispatch(const Device& d, const ExpertArgs& x, hipStream_t st)
 
 bool mfma_supported(const Shape& s, int B) {
   if (B < 1 || B > 64 || s.dtype != 1 || s.I != s.Is) return false;
-  if (s.H != 7168 || s.E % 16 != 0) return false;
+  if (s.H != 7168 || s.E % 32 != 0) return false;
   if (!(s.Ko == 7168 || s.Ko == 448)) return false;
   return s.I == 2048 || s.I == 128;
 }
 
-int mfma_oproj_splits(const Shape& s) { return 7; }
+// K chunks of the split-K launches (the partials the reduce / top-k launches sum).
+int mfma_oproj_splits(const Shape& s) { return s.Ko == 7168 ? 7 : 1; }
 int mfma_router_splits(const Shape& s) { return 7; }
 
 hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x,
                              float* part, const void* w_o, hipStream_t st) {
-  const int splits = mfma_oproj_splits(s);
-  if (s.Ko == 7168)
-    return splitk_dispatch<1, true, 4>((const uint16_t*)w_o, s.H, s.Ko, x, B, splits, part, st);
-  if (s.Ko == 448)
-    return splitk_dispatch<1, true, 2>((const uint16_t*)w_o, s.H, s.Ko, x, B, splits, part, st);
+  UnitArgs a{};
+  a.w_routed = (const uint16_t*)w_o;
+  a.act_routed = x;
+  a.out_routed = part;
+  a.B = B;
+  a.N = s.H;
+  a.K = s.Ko;
+  a.chunks = mfma_oproj_splits(s);
+  const int units = (s.H / 32) * a.chunks;
+  if (s.Ko == 7168) return staged_dispatch<2, 1, true>(d, a, units, st);     // 7 x 1024 k
+  if (s.Ko == 448) return staged_dispatch<2, 1, true, 64>(d, a, units, st);  // 448 = 7 x 64
   return hipErrorInvalidValue;
 }
 
@@ -390,23 +366,54 @@ hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const v
 
 hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w_r, float* part, hipStream_t st) {
-  return splitk_dispatch<3, false, 4>((const uint16_t*)w_r, s.E, s.H, h32, B,
-                                      mfma_router_splits(s), part, st);
+  UnitArgs a{};
+  a.w_routed = (const uint16_t*)w_r;
+  a.act_routed = h32;
+  a.out_routed = part;
+  a.B = B;
+  a.N = s.E;
+  a.K = s.H;
+  a.chunks = mfma_router_splits(s);  // 7 x 1024 k
+  return staged_dispatch<2, 3, false>(d, a, (s.E / 32) * a.chunks, st);
 }
 
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
                               float* As, hipStream_t st) {
-  ExpertArgs x{(const uint16_t*)w13, (const uint16_t*)ws13, h32, h32, A, As, s.H, s.I, s.k, B, rt};
-  return expert_dispatch<0, 8, 4>(d, x, st);  // K = H = 7168: 896 per wave
+  UnitArgs a{};
+  a.w_routed = (const uint16_t*)w13;
+  a.w_shared = (const uint16_t*)ws13;
+  a.act_routed = h32;
+  a.act_shared = h32;
+  a.out_routed = A;
+  a.out_shared = As;
+  a.H = s.H;
+  a.I = s.I;
+  a.k = s.k;
+  a.B = B;
+  a.rt = rt;
+  const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.I / 16);
+  return staged_dispatch<0, 2, false>(d, a, max_units, st);
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,
                             float* Y, float* ys, hipStream_t st) {
-  ExpertArgs x{(const uint16_t*)w2, (const uint16_t*)ws2, A, As, Y, ys, s.H, s.I, s.k, B, rt};
-  if (s.I == 2048) return expert_dispatch<1, 8, 4>(d, x, st);  // 256 per wave
-  if (s.I == 128) return expert_dispatch<1, 1, 4>(d, x, st);   // one 128-k run per unit
+  UnitArgs a{};
+  a.w_routed = (const uint16_t*)w2;
+  a.w_shared = (const uint16_t*)ws2;
+  a.act_routed = A;
+  a.act_shared = As;
+  a.out_routed = Y;
+  a.out_shared = ys;
+  a.H = s.H;
+  a.I = s.I;
+  a.k = s.k;
+  a.B = B;
+  a.rt = rt;
+  const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.H / 32);
+  if (s.I == 2048) return staged_dispatch<1, 2, false>(d, a, max_units, st);
+  if (s.I == 128) return staged_dispatch<1, 2, false, 128>(d, a, max_units, st);
   return hipErrorInvalidValue;
 }
 

@@ -9,6 +9,8 @@ import os
 import numpy as np
 import pytest
 
+import synth
+
 from tests.gpu_common import (as_f64_out, assert_close, assert_routing_equal, gpu_layer, log,
                               oracle_step)
 
@@ -47,7 +49,9 @@ def test_plan_is_mfma(name, B):
     _, _, L = gpu_layer(name)
     p = L.query_plan(B)
     assert p["path_name"] == "splitk_mfma" and p["forced"] == 0
-    assert p["kernels_per_step"] == 7 and p["oproj_splitk"] == 7
+    assert p["kernels_per_step"] == 7
+    assert p["oproj_splitk"] == (7 if synth.CONFIGS[name].oproj_in == 7168 else 1)
+    assert p["router_splitk"] == 7
 
 
 @pytest.mark.parametrize("name,B", MFMA_CASES)
