@@ -122,10 +122,11 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
 const char* kernel_names[] = {"oproj_gemv",  "router_logits", "gateup_gemv_shared",
                               "gateup_gemv_routed", "down_gemv", "moe_prep", "topk_shared",
                               "topk",        "combine",       "oproj_mfma", "oproj_reduce",
-                              "router_mfma", "gateup_mfma",   "down_mfma"};
+                              "router_mfma", "gateup_mfma",   "down_mfma",  "topk_rows",
+                              "tables"};
 enum KName {
   K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK, K_COMBINE,
-  K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA
+  K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS, K_TABLES
 };
 
 struct TimingRec {
@@ -196,8 +197,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                 B);
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
-  // oproj, reduce, router logits, top-k, grouped gate/up, grouped down, combine
-  p->kernels_per_step = 7;
+  // oproj, reduce, router logits, top-k rows, tables, gate/up, down, combine; B > 16 adds
+  // a second gate/up and down launch for groups of more than 16 tokens
+  p->kernels_per_step = B > 16 ? 10 : 8;
   return KK_OK;
 }
 
@@ -303,18 +305,20 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
   return KK_OK;
 }
 
-// MFMA path: router logits, top-k / tables (one block).
+// MFMA path: router logits, top-k rows (one wave per token), routing tables (one block).
 kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                               float* logit_part, hipStream_t s) {
   KK_HIP(timed(c, K_ROUTER_MFMA, s,
                [&] { return kk::launch_router_mfma(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s); }),
          "router logits launch");
-  KK_HIP(timed(c, K_TOPK, s,
+  KK_HIP(timed(c, K_TOPK_ROWS, s,
                [&] {
-                 return kk::launch_topk_shared(c->shape, c->dev, B, logit_part, c->w.bias, rt,
-                                               nullptr, h32, nullptr, s);
+                 return kk::launch_topk_rows(c->shape, B, logit_part,
+                                             kk::mfma_router_splits(c->shape), c->w.bias, rt, s);
                }),
          "top-k launch");
+  KK_HIP(timed(c, K_TABLES, s, [&] { return kk::launch_tables(c->shape, B, rt, s); }),
+         "routing tables launch");
   return KK_OK;
 }
 

@@ -214,6 +214,23 @@ __global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
   shared_rows<T, CPRH, NT>(ws13, Is, i_split, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
 
+// ------------------------------------------------------------------------------ top-k, large batch
+// One wave per token (grid = B): topk_idx / topk_gate rows.
+__global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ part, int splits,
+                                                       const float* __restrict__ bias, int E,
+                                                       int k, int B, float routed_scale,
+                                                       Routing rt) {
+  topk_row(part, splits, bias, B, E, k, routed_scale, blockIdx.x, rt, nullptr);
+}
+
+// One block: routing tables from the topk_idx rows of all B tokens.
+__global__ __launch_bounds__(256) void tables_kernel(int E, int k, int B, Routing rt) {
+  __shared__ TopkScratch sm;
+  for (int i = threadIdx.x; i < B * k; i += blockDim.x) sm.sel[i] = rt.topk_idx[i];
+  __syncthreads();
+  build_tables(B, E, k, rt, sm);
+}
+
 // ------------------------------------------------------------------------------ gate / up
 // Routed experts (act / n_act / offsets / perm) or the shared expert (positions = tokens).
 template <typename T, int CPR, int NT>
@@ -578,6 +595,18 @@ hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* 
                           const Routing& rt, void* out, hipStream_t st) {
   if (s.dtype == 1) return combine_t<uint16_t>(s, B, h32, Y, ys, rt, out, st);
   return combine_t<float>(s, B, h32, Y, ys, rt, out, st);
+}
+
+hipError_t launch_topk_rows(const Shape& s, int B, const float* part, int splits,
+                            const float* bias, const Routing& rt, hipStream_t st) {
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(B), dim3(64), 0, st, part, splits, bias, s.E, s.k, B,
+                     s.routed_scale, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t st) {
+  hipLaunchKernelGGL(tables_kernel, dim3(1), dim3(256), 0, st, s.E, s.k, B, rt);
+  return hipGetLastError();
 }
 
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st) {

@@ -77,6 +77,12 @@ hipError_t launch_down_gemv(const Shape& s, const Device& d, int B, const float*
 hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
                           const Routing& rt, void* out, hipStream_t st);
 
+// Large-batch router tail: one wave per token writes its top-k row, then one block builds
+// the routing tables from all rows.
+hipError_t launch_topk_rows(const Shape& s, int B, const float* part, int splits,
+                            const float* bias, const Routing& rt, hipStream_t st);
+hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t st);
+
 // act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
 

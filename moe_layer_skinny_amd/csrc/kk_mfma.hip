@@ -108,7 +108,8 @@ struct UnitArgs {
 // the end of the unit.
 //   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
 //   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC>
+// GSEL picks the groups a launch covers: 0 all, 1 those with <= 16 tokens, 2 the others.
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   constexpr int K8 = KS / 8;
   constexpr int WP = K8 + 1;
@@ -146,6 +147,7 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
       cnt = x.rt.offsets[e + 1] - p0;
       wbase = x.w_routed + (size_t)e * wstride;
     }
+    if ((GSEL == 1 && cnt > 16) || (GSEL == 2 && cnt <= 16)) continue;  // block-uniform
     const int ntt = (cnt + 15) / 16;
     const int row0 = MODE == 0 ? tile * 16 : tile * 32;
     const int kbase = chunk * kchunk;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
         const u32x4* p = BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
                                  : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
 #pragma unroll
-        for (int w = 0; w < AW; ++w) areg[i][w] = p[w];
+        for (int w = 0; w < AW; ++w) areg[i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
       }
     };
     f32x4 acc[2][TT];
@@ -296,9 +298,9 @@ void allow_lds_mfma(Kern kernel) {
 
 inline int token_tiles(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0>
 hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
-  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC>;
+  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL>;
   constexpr size_t lds_main = (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
   constexpr size_t lds_red = (size_t)4 * 2 * TT * 64 * 16;
   constexpr size_t lds = lds_main > lds_red ? lds_main : lds_red;
@@ -316,15 +318,29 @@ hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream
   return hipGetLastError();
 }
 
-// Stage depth by token tiles: 256 k (1 tile), 128 (2), 64 (4); KMAX caps it (K = 448).
+// Split-K launches (one token group): stage depth 256 k for up to 32 tokens, 128 k for 64;
+// KMAX caps it (K = 448).
 template <int MODE, int NTERM, bool BF16SRC, int KMAX = 256>
 hipError_t staged_dispatch(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
-  constexpr int K1 = KMAX < 256 ? KMAX : 256, K2 = KMAX < 128 ? KMAX : 128;
+  constexpr int K1 = KMAX < 256 ? KMAX : 256, K4 = KMAX < 128 ? KMAX : 128;
   switch (token_tiles(x.B)) {
     case 1: return staged_t<MODE, 1, K1, NTERM, BF16SRC>(d, x, max_units, st);
-    case 2: return staged_t<MODE, 2, K2, NTERM, BF16SRC>(d, x, max_units, st);
-    default: return staged_t<MODE, 4, 64, NTERM, BF16SRC>(d, x, max_units, st);
+    case 2: return staged_t<MODE, 2, K1, NTERM, BF16SRC>(d, x, max_units, st);
+    default: return staged_t<MODE, 4, K4, NTERM, BF16SRC>(d, x, max_units, st);
   }
+}
+
+// Grouped launches: groups of up to 16 tokens (nearly all routed experts) go through the
+// one-tile kernel with 256-k stages; when B > 16 a second launch covers the shared expert
+// and any routed expert with more than 16 tokens.
+template <int MODE, int KMAX = 256>
+hipError_t grouped_dispatch(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
+  constexpr int K1 = KMAX < 256 ? KMAX : 256, K4 = KMAX < 128 ? KMAX : 128;
+  if (x.B <= 16) return staged_t<MODE, 1, K1, 2, false, 0>(d, x, max_units, st);
+  hipError_t e = staged_t<MODE, 1, K1, 2, false, 1>(d, x, max_units, st);
+  if (e != hipSuccess) return e;
+  if (x.B <= 32) return staged_t<MODE, 2, K1, 2, false, 2>(d, x, max_units, st);
+  return staged_t<MODE, 4, K4, 2, false, 2>(d, x, max_units, st);
 }
 
 }  // namespace
@@ -393,7 +409,7 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   a.B = B;
   a.rt = rt;
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.I / 16);
-  return staged_dispatch<0, 2, false>(d, a, max_units, st);
+  return grouped_dispatch<0>(d, a, max_units, st);
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
@@ -412,8 +428,8 @@ hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float*
   a.B = B;
   a.rt = rt;
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.H / 32);
-  if (s.I == 2048) return staged_dispatch<1, 2, false>(d, a, max_units, st);
-  if (s.I == 128) return staged_dispatch<1, 2, false, 128>(d, a, max_units, st);
+  if (s.I == 2048) return grouped_dispatch<1>(d, a, max_units, st);
+  if (s.I == 128) return grouped_dispatch<1, 128>(d, a, max_units, st);
   return hipErrorInvalidValue;
 }
 

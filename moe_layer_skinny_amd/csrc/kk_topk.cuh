@@ -33,71 +33,76 @@ __device__ __forceinline__ uint64_t rank_key(double key, int e) {
   return (u & ~0x1FFull) | (uint64_t)(511 - e);
 }
 
-// part: [splits][B][E] fp32 logit partials (splits <= kMaxTopkSplits), summed in slice
-// order.  blockDim.x >= 64.  All global loads of a token are issued before any is used
-// (addresses clamped instead of branched around, so nothing waits on a join).
+// One token's top-k on one wave: logits (partials summed in slice order), sigmoid scores,
+// fp64 keys, k rounds of wave arg-max, renormalised gates; topk_idx / topk_gate rows written
+// in ascending expert order, and the selected experts returned through sel (nullable).
+// part: [splits][B][E] (splits <= kMaxTopkSplits).  All global loads are issued before any
+// is used (addresses clamped instead of branched around, so nothing waits on a join).
 constexpr int kMaxTopkSplits = 8;
-__device__ inline void topk_tables(const float* part, int splits, const float* __restrict__ bias,
-                                   int B, int E, int k, float routed_scale, const Routing& rt,
-                                   TopkScratch& sm) {
+__device__ inline void topk_row(const float* part, int splits, const float* __restrict__ bias,
+                                int B, int E, int k, float routed_scale, int t, const Routing& rt,
+                                int* sel) {
   constexpr int MAXM = kMaxExperts / 64;
   constexpr int MAXS = kMaxTopkSplits;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) sm.mask[e] = 0ull;
-
-  for (int t = wave; t < B; t += nw) {
-    float pv[MAXM][MAXS], bv[MAXM];
+  const int lane = threadIdx.x & 63;
+  float pv[MAXM][MAXS], bv[MAXM];
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-      const int ec = min(lane + 64 * m, E - 1);
-      bv[m] = bias[ec];
+  for (int m = 0; m < MAXM; ++m) {
+    const int ec = min(lane + 64 * m, E - 1);
+    bv[m] = bias[ec];
 #pragma unroll
-      for (int s = 0; s < MAXS; ++s)
-        pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
-    }
-    double sc[MAXM];
-    uint64_t rk[MAXM];
+    for (int s = 0; s < MAXS; ++s) pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
+  }
+  double sc[MAXM];
+  uint64_t rk[MAXM];
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-      const int e = lane + 64 * m;
-      float l = 0.f;
+  for (int m = 0; m < MAXM; ++m) {
+    const int e = lane + 64 * m;
+    float l = 0.f;
 #pragma unroll
-      for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
-      const double sv = 1.0 / (1.0 + exp(-(double)l));
-      sc[m] = sv;
-      rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
-    }
-    // k rounds of wave arg-max on the packed keys; the winner's entry drops out
-    uint32_t selmask = 0;
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
-#pragma unroll
-      for (int m = 0; m < MAXM; ++m)
-        if (!((selmask >> m) & 1u)) best = max_u64(best, rk[m]);
-      best = wave_max_u64(best);
-      const int win = 511 - (int)(best & 0x1FFull);
-      if ((win & 63) == lane) selmask |= 1u << (win >> 6);
-    }
-    double ssum = 0.0;
+    for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
+    const double sv = 1.0 / (1.0 + exp(-(double)l));
+    sc[m] = sv;
+    rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
+  }
+  // k rounds of wave arg-max on the packed keys; the winner's entry drops out
+  uint32_t selmask = 0;
+  for (int r = 0; r < k; ++r) {
+    uint64_t best = 0;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m)
-      if ((selmask >> m) & 1u) ssum += sc[m];
-    ssum = wave_sum_f64_dpp(ssum);
-    int base = 0;
-#pragma unroll
-    for (int m = 0; m < MAXM; ++m) {
-      const bool on = (selmask >> m) & 1u;
-      const unsigned long long bal = __ballot(on);
-      if (on) {
-        const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
-        const int e = lane + 64 * m;
-        rt.topk_idx[t * k + pos] = e;
-        rt.topk_gate[t * k + pos] = (float)((double)routed_scale * sc[m] / ssum);
-        sm.sel[t * k + pos] = e;
-      }
-      base += __popcll(bal);
-    }
+      if (!((selmask >> m) & 1u)) best = max_u64(best, rk[m]);
+    best = wave_max_u64(best);
+    const int win = 511 - (int)(best & 0x1FFull);
+    if ((win & 63) == lane) selmask |= 1u << (win >> 6);
   }
+  double ssum = 0.0;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m)
+    if ((selmask >> m) & 1u) ssum += sc[m];
+  ssum = wave_sum_f64_dpp(ssum);
+  int base = 0;
+#pragma unroll
+  for (int m = 0; m < MAXM; ++m) {
+    const bool on = (selmask >> m) & 1u;
+    const unsigned long long bal = __ballot(on);
+    if (on) {
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      const int e = lane + 64 * m;
+      rt.topk_idx[t * k + pos] = e;
+      rt.topk_gate[t * k + pos] = (float)((double)routed_scale * sc[m] / ssum);
+      if (sel) sel[t * k + pos] = e;
+    }
+    base += __popcll(bal);
+  }
+}
+
+// Routing tables from the selected experts of all B tokens (sm.sel filled, block-wide):
+// per-expert token masks, counts, exclusive prefix sum -> offsets, active list, n_act, perm
+// (slots by (expert, token)) and its inverse.
+__device__ inline void build_tables(int B, int E, int k, const Routing& rt, TopkScratch& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sm.mask[e] = 0ull;
   __syncthreads();
   for (int i = threadIdx.x; i < B * k; i += blockDim.x)
     atomicOr(&sm.mask[sm.sel[i]], 1ull << (i / k));
@@ -138,6 +143,16 @@ __device__ inline void topk_tables(const float* part, int splits, const float* _
     rt.perm[p] = i;
     rt.inv_perm[i] = p;
   }
+}
+
+// Both steps in one block (blockDim.x >= 64): each wave takes tokens wave, wave + nw, ...
+__device__ inline void topk_tables(const float* part, int splits, const float* __restrict__ bias,
+                                   int B, int E, int k, float routed_scale, const Routing& rt,
+                                   TopkScratch& sm) {
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int t = wave; t < B; t += nw) topk_row(part, splits, bias, B, E, k, routed_scale, t, rt, sm.sel);
+  __syncthreads();
+  build_tables(B, E, k, rt, sm);
 }
 
 }  // namespace kk
