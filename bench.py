@@ -80,6 +80,68 @@ def cpu_baseline(cfg, B: int, reps: int) -> dict:
                       f"touched); fp64 numpy incl. bf16->fp64 upcasts; weights pre-generated"}
 
 
+def time_steps(layer, B, x, r, out, idx, gate, ws, s, flush, steps, warmup):
+    """Median us of `steps` flushed eager steps (same protocol as the headline)."""
+    import torch
+    with torch.cuda.stream(s):
+        for _ in range(warmup):
+            flush.add_(1.0)
+            layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s)
+    s.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    with torch.cuda.stream(s):
+        for a, b in evs:
+            flush.add_(1.0)
+            a.record(s)
+            layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s)
+            b.record(s)
+    s.synchronize()
+    return statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+
+
+def sweep(main_cfg, main_w, args, s, flush) -> dict:
+    """The other workloads: batch 8 / 64 of the full-size layer on the same resident weights
+    (only the router bias differs), and one TP rank's share at batch 1, 2, 8, 64."""
+    import torch
+
+    import synth
+    import synth.device as sd
+    from moe_layer_skinny_amd import kk
+
+    out = {}
+    plan = [("full_b8", 8), ("full_b64", 64)] + [("tp_rank", b) for b in (1, 2, 8, 64)]
+    weights = {}
+    for name, B in plan:
+        cfg = synth.CONFIGS[name]
+        same = (cfg.hidden, cfg.oproj_in, cfg.inter) == (main_cfg.hidden, main_cfg.oproj_in,
+                                                         main_cfg.inter)
+        if name not in weights:
+            share = main_w if same else next((v for k, v in weights.items()
+                                              if synth.CONFIGS[k].oproj_in == cfg.oproj_in), None)
+            log(f"[bench] sweep {name}: weights {'shared' if share is not None else 'filled'}")
+            weights[name] = sd.device_weights(cfg, share_from=share)
+        w = weights[name]
+        layer = kk.Layer(kk.make_config(cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.top_k,
+                                        cfg.inter, cfg.shared_inter, cfg.dtype), w, B)
+        x, r, _, _ = sd.device_tokens(cfg, B)
+        o = torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty(B, cfg.top_k, dtype=torch.int32, device="cuda")
+        gate = torch.empty(B, cfg.top_k, dtype=torch.float32, device="cuda")
+        ws = layer.new_workspace()
+        us = time_steps(layer, B, x, r, o, idx, gate, ws, s, flush, args.steps, max(2, args.warmup))
+        n_act = int(torch.unique(idx).numel())
+        by = unique_bytes(cfg, n_act)["total"]
+        gbs = by / (us * 1e-6) / 1e9
+        out[f"{name}@{B}"] = {"us_per_step": round(us, 3), "tokens_per_s": round(B / (us * 1e-6), 1),
+                              "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "n_act": n_act, "unique_bytes": by,
+                              "path": layer.query_plan(B)["path_name"]}
+        log(f"[bench] {name}@{B}: {out[f'{name}@{B}']}")
+        layer.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +156,8 @@ def main():
                     help="how each timed step is submitted (eager: one launch per kernel on one stream)")
     ap.add_argument("--two-stream", action="store_true",
                     help="shared expert's gate/up on the auxiliary stream")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the batch 8/64 and TP-rank-share measurements")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -230,10 +294,12 @@ def main():
         "kernel_us_eager": {k: round(v, 3) for k, v in kernels.items()},
         "roofline": roofline,
     }
+    layer.close()
+    if not args.no_sweep:
+        res["batch_sweep"] = sweep(cfg, w, args, s, flush)
     if not args.no_cpu:
         log("[bench] timing the oracle on the host cores")
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_reps)
-    layer.close()
     print(json.dumps(res), flush=True)
 
 
