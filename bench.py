@@ -29,6 +29,25 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 1 << 30
+COPY_BYTES = 256 << 20
+# rocprofv3 HBM byte counters per dominant kernel and workload: committed summaries, valid only
+# while the kernel's sources hash to what they were when the counters were taken
+TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/gateup_gemv_full_b1.json"}
+
+
+def measured_traffic(path_name: str, workload: str, B: int):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of the dominant kernel, or None when no
+    record exists or the kernel's sources changed since it was taken."""
+    import hashlib
+    rel = TRAFFIC_RECORDS.get((path_name, workload, B))
+    if rel is None or not os.path.exists(os.path.join(ROOT, rel)):
+        return None
+    rec = json.load(open(os.path.join(ROOT, rel)))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
 
 
 def log(*a):
@@ -158,6 +177,8 @@ def main():
                     help="shared expert's gate/up on the auxiliary stream")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the batch 8/64 and TP-rank-share measurements")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with two device copies of 256 MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -268,7 +289,9 @@ def main():
         ach = dom_bytes / (kernels[dom_name] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": None, "bytes_per_launch": dom_bytes,
+                    "traffic": measured_traffic(plan["path_name"], cfg.name, B),
+                    "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+                    "bytes_per_launch": dom_bytes,
                     "avg_launch_us": round(kernels[dom_name], 3)}
 
     gbs = by["total"] / (med * 1e-6) / 1e9
@@ -295,6 +318,13 @@ def main():
         "roofline": roofline,
     }
     layer.close()
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_sweep:
         res["batch_sweep"] = sweep(cfg, w, args, s, flush)
     if not args.no_cpu:
