@@ -141,7 +141,8 @@ kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t*
                         void* out, void* ws, kk_stream stream);
 
 /* The whole step: o-proj + residual, router logits, top-k || shared expert gate/up, routed
- * gate/up, down-projection, combine (six launches on `stream`).  topk_idx / topk_gate are optional
+ * gate/up, down-projection with the combine (batch 1-2: five launches on `stream`; the split-K
+ * MFMA path for larger batches: see kk_query_plan).  topk_idx / topk_gate are optional
  * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
  * first use for these (B, pointers, stream, flags) and replayed afterwards. */
 kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,

@@ -66,7 +66,7 @@ Layout make_layout(const kk_config& c, int Bm) {
   L.offsets = take((size_t)(c.n_experts + 1) * 4);
   L.perm = take(slots * 4);
   L.inv_perm = take(slots * 4);
-  L.act = take((size_t)c.n_experts * 4);
+  L.act = take((size_t)std::max(c.n_experts, 64) * 4);  // read 64 lanes at a time
   L.n_act = take(16);
   L.A = take(slots * c.inter * 4);
   L.As = take((size_t)Bm * c.shared_inter * 4);
@@ -120,7 +120,7 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
 }
 
 const char* kernel_names[] = {"oproj_gemv",  "router_logits", "gateup_gemv_shared",
-                              "gateup_gemv_routed", "down_gemv", "moe_prep", "topk_shared",
+                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep", "topk_shared",
                               "topk",        "combine",       "oproj_mfma", "oproj_reduce",
                               "router_mfma", "gateup_mfma",   "down_mfma",  "topk_rows",
                               "tables"};
@@ -182,14 +182,14 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   if (p->path == KK_PATH_GEMV) {
     if (!kk::gemv_supported(c->shape, B))
       return fail(KK_ERR_UNSUPPORTED, "GEMV path has no kernels for batch %d of this shape", B);
-    const size_t lds_down = (size_t)(B * c->shape.k + B) * c->shape.I * 4;
+    const size_t lds_down = kk::down_combine_gemv_lds(c->shape, c->dev, B);
     if ((long)lds_down > c->dev.max_lds)
       return fail(KK_ERR_UNSUPPORTED, "GEMV down-projection needs %zu B of LDS (device: %d)",
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
     p->router_splitk = kk::router_gemv_splits(c->shape);
-    // oproj, router logits, top-k || shared gate/up, routed gate/up, down, combine
-    p->kernels_per_step = 6;
+    // oproj, router logits, top-k || shared gate/up, routed gate/up, down + combine
+    p->kernels_per_step = 5;
     return KK_OK;
   }
   if (!kk::mfma_supported(c->shape, B))
@@ -376,13 +376,10 @@ kk_status enqueue_down_combine(kk_ctx* c, int B, const float* h32, const kk::Rou
                                const WsPtrs& p, void* out, hipStream_t s) {
   KK_HIP(timed(c, K_DOWN, s,
                [&] {
-                 return kk::launch_down_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
-                                             p.Y, p.ys, s);
+                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
+                                                     c->w.ws2, h32, rt, out, s);
                }),
-         "down launch");
-  KK_HIP(timed(c, K_COMBINE, s,
-               [&] { return kk::launch_combine(c->shape, B, h32, p.Y, p.ys, rt, out, s); }),
-         "combine launch");
+         "down + combine launch");
   return KK_OK;
 }
 

@@ -1,6 +1,8 @@
 // Device helpers shared by the kernels of the decode-layer step (gfx950, wave64).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -214,6 +216,26 @@ __device__ __forceinline__ double wave_sum_f64_dpp(double v) {
     v += __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
   }
   return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), 63));
+}
+
+// Sum of v over each segment of SEG lanes (16, 32 or 64) in a fixed combining order, valid in
+// the segment's last lane (lane % SEG == SEG - 1).  Four steps give every lane of a row of 16
+// its row total; rows 1 and 3 then add the total of the row before them, and row 3 the total
+// of rows 0-1.
+template <int SEG>
+__device__ __forceinline__ float seg_sum_dpp(float v) {
+  static_assert(SEG == 16 || SEG == 32 || SEG == 64, "segments of 16, 32 or 64 lanes");
+  auto mv = [](float x, auto ctrl_tag) {
+    constexpr int C = decltype(ctrl_tag)::value;
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), C, 0xF, 0xF, false));
+  };
+  v += mv(v, std::integral_constant<int, 0xB1>{});
+  v += mv(v, std::integral_constant<int, 0x4E>{});
+  v += mv(v, std::integral_constant<int, 0x141>{});
+  v += mv(v, std::integral_constant<int, 0x140>{});
+  if (SEG >= 32) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  if (SEG >= 64) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return v;
 }
 
 // Inclusive prefix sum of v over lanes 0..63 (Hillis-Steele within rows of 16, then the

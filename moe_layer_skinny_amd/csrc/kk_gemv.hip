@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kGemvThreads) void oproj_gemv_kernel(
   }
 }
 
-// ------------------------------------------------------------------------------ gate / up
+// ------------------------------------------------------------------------------ gate / up helpers
 // One gate/up row pair of one expert for the positions [p0, p1) of that expert:
 // A[p][i] = silu(W1[i] . u_t) * (W3[i] . u_t), u_t an fp32 row in LDS.
 template <typename T, int CPR, int NT>
@@ -112,9 +112,10 @@ __device__ __forceinline__ void gateup_unit(const u32x4 (&wg)[Geo<T, CPR>::CPL],
       const int t = identity_tokens ? p : rt.perm[p] / k;
       float z1, z3;
       dot2_lane<T, CPR>(wg, wu, lds_u + t * G::K, lane, z1, z3);
-      z1 = seg_sum<64>(z1);
-      z3 = seg_sum<64>(z3);
-      if (lane == 0) A[(size_t)p * I + i] = silu_f32(z1) * z3;
+      // same per-lane order and lane combining as the routed gate/up kernel
+      z1 = seg_sum_dpp<64>(z1);
+      z3 = seg_sum_dpp<64>(z3);
+      if (lane == 63) A[(size_t)p * I + i] = silu_f32(z1) * z3;
     }
   }
 }
@@ -129,10 +130,32 @@ __device__ __forceinline__ void load_pair(const T* __restrict__ w13, int e, int 
   load_row<T, CPR>(g_row + (size_t)I * G::K, lane, wu);
 }
 
-__device__ __forceinline__ void stage_rows_f32(float* dst, const float* __restrict__ src, int n) {
-  for (int i = threadIdx.x; i < n / 4; i += blockDim.x)
-    reinterpret_cast<float4*>(dst)[i] = reinterpret_cast<const float4*>(src)[i];
-}
+// Global -> LDS copy of n floats (n % 4 == 0, n > 0) in two halves: load() puts a thread's
+// first Q float4s in registers, all in flight together (indices clamped instead of branched
+// around), so it can be issued ahead of a weight stream; store() writes them to LDS after it,
+// waiting only on these loads, and copies anything past Q * blockDim.x float4s by a loop.
+template <int Q>
+struct Stage {
+  float4 v[Q];
+  const float4* src;
+  int n4;
+  __device__ __forceinline__ void load(const float* __restrict__ s, int n) {
+    src = reinterpret_cast<const float4*>(s);
+    n4 = n / 4;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) v[j] = src[min((int)(threadIdx.x + j * blockDim.x), n4 - 1)];
+  }
+  __device__ __forceinline__ void store(float* d) const {
+    float4* dst = reinterpret_cast<float4*>(d);
+    // past the end the last float4 is written again with its own value (no branch)
+#pragma unroll
+    for (int j = 0; j < Q; ++j) dst[min((int)(threadIdx.x + j * blockDim.x), n4 - 1)] = v[j];
+    for (int i = threadIdx.x + Q * blockDim.x; i < n4; i += blockDim.x) dst[i] = src[i];
+  }
+};
+
+// float4s per thread that cover `rows` fp32 rows of K elements with kGemvThreads threads.
+constexpr int stage_q(int rows, int K) { return (rows * K / 4 + kGemvThreads - 1) / kGemvThreads; }
 
 // ------------------------------------------------------------------------------ router
 // Shared expert gate/up rows [i0, i1) over all B tokens, spread over `nw` workers (waves),
@@ -171,6 +194,13 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   const bool shared = ws13 != nullptr;
   u32x4 wg[GH::CPL], wu[GH::CPL];
   if (shared && gw < i_split) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
+  if (shared) {
+    // the first logit load waits for the row pair anyway (loads complete in order), so the
+    // u rows are staged here, behind it, without holding registers through the logit loop
+    Stage<stage_q(NT, GH::K)> st;
+    st.load(h32, B * GH::K);
+    st.store(lds);
+  }
   const int units = E * splits;
   for (int unit = gw; unit < units; unit += nw) {
     const int e = unit / splits, s = unit - e * splits;
@@ -184,7 +214,6 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
     }
   }
   if (!shared) return;
-  stage_rows_f32(lds, h32, B * GH::K);
   __syncthreads();
   shared_rows<T, CPRH, NT>(ws13, Is, 0, i_split, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
@@ -208,8 +237,10 @@ __global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
   const int nw = (gridDim.x - 1) * wpb;
   const int gw = (blockIdx.x - 1) * wpb + wave;
   u32x4 wg[GH::CPL], wu[GH::CPL];
+  Stage<stage_q(NT, GH::K)> st;
+  st.load(h32, B * GH::K);
   if (i_split + gw < Is) load_pair<T, CPRH>(ws13, 0, i_split + gw, Is, wg, wu, lane);
-  stage_rows_f32(lds, h32, B * GH::K);
+  st.store(lds);
   __syncthreads();
   shared_rows<T, CPRH, NT>(ws13, Is, i_split, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
@@ -233,112 +264,139 @@ __global__ __launch_bounds__(256) void tables_kernel(int E, int k, int B, Routin
 
 // ------------------------------------------------------------------------------ gate / up
 // Routed experts (act / n_act / offsets / perm) or the shared expert (positions = tokens).
+// One wave per (expert, row i) unit: gate row i and up row i against the unit's tokens,
+// A[position][i] = silu(W1[i] . u_t) * (W3[i] . u_t).  A unit's two rows are fetched in two
+// K halves that alternate with their consumption, so a wave always has one half in flight
+// while it works on the other (a unit past the end fetches from the activation buffer, so
+// no load is branched around).  Tables come from the wave's own lanes: lane j holds act[j],
+// the first position of that expert and its position count, lane p the token of position p.
 template <typename T, int CPR, int NT>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     const float* __restrict__ u, const T* __restrict__ w13, int I, int k, int B, int shared,
     Routing rt, float* __restrict__ A) {
   using G = Geo<T, CPR>;
-  static_assert(G::SEG == 64, "gate/up rows must span the wave");
-  extern __shared__ float lds[];  // u [B][H]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
-  const int n = shared ? 1 : *rt.n_act;
+  static_assert(G::SEG == 64 && G::EXACT, "gate/up rows must span the wave exactly");
+  constexpr int HA = (G::CPL + 1) / 2, HB = G::CPL - HA;
+  extern __shared__ float lds[];  // u [B][K]
+  const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nslot = B * k;
+  // (act has at least 64 entries; entries past n_act are not expert ids)
+  const int t_a = rt.act[lane];
+  const int t_p = rt.perm[min(lane, nslot - 1)];
+  const int n = shared ? 1 : min(*rt.n_act, 64);
+  const int t_e = (!shared && lane < n) ? t_a : 0;
+  const int t_lo = shared ? 0 : rt.offsets[t_e];
+  const int t_cnt = shared ? B : rt.offsets[t_e + 1] - t_lo;
+  const int t_tok = min(max(t_p / k, 0), B - 1);
+  Stage<stage_q(NT, G::K)> st;
+  st.load(u, B * G::K);
+
   const int units = n * I;
   const int stride = gridDim.x * wpb;
-  int unit = blockIdx.x * wpb + wave;
-
-  u32x4 wg[G::CPL], wu[G::CPL];
-  auto expert_of = [&](int un) { return shared ? 0 : rt.act[un / I]; };
-  if (unit < units) load_pair<T, CPR>(w13, expert_of(unit), unit % I, I, wg, wu, lane);
-  stage_rows_f32(lds, u, B * G::K);
-  __syncthreads();
-  if (unit >= units) return;
-  while (true) {
-    const int i = unit % I;
-    int p0 = 0, p1 = B;
-    if (!shared) {
-      const int e = rt.act[unit / I];
-      p0 = rt.offsets[e];
-      p1 = rt.offsets[e + 1];
-    }
-    gateup_unit<T, CPR, NT>(wg, wu, lds, p0, p1, i, I, k, shared != 0, rt, A, lane);
-    unit += stride;
-    if (unit >= units) break;
-    __builtin_amdgcn_sched_barrier(0);
-    load_pair<T, CPR>(w13, expert_of(unit), unit % I, I, wg, wu, lane);
-  }
-}
-
-// ------------------------------------------------------------------------------ down (per expert)
-// Y[p][n] = W2_e[n] . A[p] for every position p of active expert e, and ys[t][n] = Ws2[n] .
-// As[t] for the shared expert (unit index n_act).  A unit is R consecutive row groups of
-// one expert, so each wave streams a contiguous run of that expert's W2 and consecutive
-// waves continue it; the weighted combine is a separate small launch.
-template <typename T, int CPR, int NT, int R>
-__global__ __launch_bounds__(kGemvThreads) void down_gemv_kernel(
-    const float* __restrict__ A, const float* __restrict__ As, const T* __restrict__ w2,
-    const T* __restrict__ ws2, int H, int k, int B, Routing rt, float* __restrict__ Y,
-    float* __restrict__ ys) {
-  using G = Geo<T, CPR>;
-  extern __shared__ float lds[];  // A [B*k][I], As [B][I]
-  float* sA = lds;
-  float* sAs = lds + (size_t)B * k * G::K;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
-  const int sub = lane % G::SEG, seg = lane / G::SEG;
-  const int n_act = *rt.n_act;
-  const int rows_per_unit = G::RPW * R;
-  const int rb_per_expert = (H + rows_per_unit - 1) / rows_per_unit;
-  const int units = (n_act + 1) * rb_per_expert;
-  const int stride = gridDim.x * wpb;
-  int unit = blockIdx.x * wpb + wave;
-
-  u32x4 w[R][G::CPL];
-  auto issue = [&](int u) {
-    const int a = u / rb_per_expert, rb = u - a * rb_per_expert;
-    const T* base = a < n_act ? w2 + (size_t)rt.act[a] * H * G::K : ws2;
+  const T* dummy = reinterpret_cast<const T*>(u);
+  u32x4 ga[HA], ua[HA], gb[HB > 0 ? HB : 1], ub[HB > 0 ? HB : 1];
+  auto rows = [&](int un, const T*& g, const T*& up) {
+    const int a = un / I, i = un - a * I;
+    const int e = __builtin_amdgcn_readlane(t_e, min(a, 63));
+    g = w13 + ((size_t)e * 2 * I + i) * G::K;
+    up = g + (size_t)I * G::K;
+    if (un >= units) g = up = dummy;
+  };
+  auto issue_a = [&](int un) {
+    const T *g, *up;
+    rows(un, g, up);
+    const u32x4* pg = reinterpret_cast<const u32x4*>(g);
+    const u32x4* pu = reinterpret_cast<const u32x4*>(up);
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const int n = rb * rows_per_unit + seg + G::RPW * q;
-      if (n < H)
-        load_row<T, CPR>(base + (size_t)n * G::K, sub, w[q]);
-      else
-#pragma unroll
-        for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < HA; ++i) {
+      ga[i] = __builtin_nontemporal_load(pg + lane + 64 * i);
+      ua[i] = __builtin_nontemporal_load(pu + lane + 64 * i);
     }
   };
-  if (unit < units) issue(unit);
-  stage_rows_f32(sA, A, B * k * G::K);
-  stage_rows_f32(sAs, As, B * G::K);
-  __syncthreads();
-  if (unit >= units) return;
-  while (true) {
-    const int a = unit / rb_per_expert, rb = unit - a * rb_per_expert;
-    int p0 = 0, p1 = B;
-    const bool routed = a < n_act;
-    if (routed) {
-      const int e = rt.act[a];
-      p0 = rt.offsets[e];
-      p1 = rt.offsets[e + 1];
+  auto issue_b = [&](int un) {
+    const T *g, *up;
+    rows(un, g, up);
+    const u32x4* pg = reinterpret_cast<const u32x4*>(g);
+    const u32x4* pu = reinterpret_cast<const u32x4*>(up);
+#pragma unroll
+    for (int i = 0; i < HB; ++i) {
+      gb[i] = __builtin_nontemporal_load(pg + lane + 64 * (HA + i));
+      ub[i] = __builtin_nontemporal_load(pu + lane + 64 * (HA + i));
     }
+  };
+  float z1[NT], z3[NT];
+  // chunk j of both rows against the activation rows of the unit's tokens
+  auto eat = [&](const u32x4& wg, const u32x4& wu, int j, const float* const (&xr)[NT]) {
+    float fg[G::EPC], fu[G::EPC];
+    Elem<T>::unpack(wg, fg);
+    Elem<T>::unpack(wu, fu);
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const int n = rb * rows_per_unit + seg + G::RPW * q;
+    for (int q = 0; q < NT; ++q) {
+      const float4* x = reinterpret_cast<const float4*>(xr[q] + 64 * j * G::EPC);
 #pragma unroll
-      for (int qq = 0; qq < NT; ++qq) {
-        const int p = p0 + qq;
-        if (p < p1) {
-          const float* act = routed ? sA + (size_t)p * G::K : sAs + (size_t)p * G::K;
-          const float v = seg_sum<G::SEG>(dot_lane<T, CPR>(w[q], act, sub));
-          if (sub == 0 && n < H) (routed ? Y : ys)[(size_t)p * H + n] = v;
-        }
+      for (int h = 0; h < G::EPC / 4; ++h) {
+        const float4 v = x[h];
+        z1[q] = fmaf(fg[4 * h + 0], v.x, z1[q]);
+        z3[q] = fmaf(fu[4 * h + 0], v.x, z3[q]);
+        z1[q] = fmaf(fg[4 * h + 1], v.y, z1[q]);
+        z3[q] = fmaf(fu[4 * h + 1], v.y, z3[q]);
+        z1[q] = fmaf(fg[4 * h + 2], v.z, z1[q]);
+        z3[q] = fmaf(fu[4 * h + 2], v.z, z3[q]);
+        z1[q] = fmaf(fg[4 * h + 3], v.w, z1[q]);
+        z3[q] = fmaf(fu[4 * h + 3], v.w, z3[q]);
       }
     }
-    unit += stride;
-    if (unit >= units) break;
+  };
+
+  int cur = blockIdx.x * wpb + wave;
+  issue_a(cur);
+  issue_b(cur);
+  st.store(lds);
+  __syncthreads();
+  for (; cur < units; cur += stride) {
+    const int a = cur / I, i = cur - a * I;
+    const int p0 = __builtin_amdgcn_readlane(t_lo, min(a, 63));
+    const int cnt = __builtin_amdgcn_readlane(t_cnt, min(a, 63));
+    const float* xr[NT];  // this lane's first activation value of each token's row
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const int tq = __builtin_amdgcn_readlane(t_tok, min(p0 + min(q, cnt - 1), 63));
+      xr[q] = lds + (shared ? min(q, B - 1) : tq) * G::K + lane * G::EPC;
+    }
+#pragma unroll
+    for (int q = 0; q < NT; ++q) z1[q] = z3[q] = 0.f;
+    // (one chunk at a time: unpacked weights of several chunks would not fit beside the
+    // buffers)
+#pragma unroll
+    for (int j = 0; j < HA; ++j) {
+      eat(ga[j], ua[j], j, xr);
+      if (NT > 1) __builtin_amdgcn_sched_barrier(0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    issue(unit);
+    issue_a(cur + stride);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < HB; ++j) {
+      eat(gb[j], ub[j], HA + j, xr);
+      if (NT > 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // the sums are needed here for every token slot, used or not: keeps the compiler from
+    // sinking a slot's whole dot product (and the weights it holds) into its store branch
+#pragma unroll
+    for (int q = 0; q < NT; ++q) asm volatile("" : "+v"(z1[q]), "+v"(z3[q]));
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(cur + stride);
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+      const float g = seg_sum_dpp<64>(z1[q]);
+      const float v = seg_sum_dpp<64>(z3[q]);
+      if (q < cnt && lane == 63) A[(size_t)(p0 + q) * I + i] = silu_f32(g) * v;
+    }
   }
 }
 
+// ------------------------------------------------------------------------------ combine (MFMA path)
 // out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] * Y[inv_perm[t*k+j]][n] + ys[t][n]), j in
 // ascending expert order.  KMAX >= k; every load is issued before the sum (clamped indices,
 // zero gates past k) so the launch costs one memory latency.
@@ -352,19 +410,178 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = i / H, n = i - t * H;
   float g[KMAX];
   int q[KMAX];
+  const bool routed = *rt.n_act > 0;  // 0: tables failed validation, routed terms left out
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int slot = t * k + min(j, k - 1);
-    g[j] = j < k ? rt.topk_gate[slot] : 0.f;
-    q[j] = rt.inv_perm[slot];
+    g[j] = (j < k && routed) ? rt.topk_gate[slot] : 0.f;
+    q[j] = min(max(rt.inv_perm[slot], 0), B * k - 1);
   }
   float y[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) y[j] = Y[(size_t)q[j] * H + n];
+  for (int j = 0; j < KMAX; ++j) {
+    y[j] = Y[(size_t)q[j] * H + n];
+    y[j] = routed ? y[j] : 0.f;  // unwritten rows of Y are never used
+  }
   float acc = h32[i];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) acc = fmaf(g[j], y[j], acc);
   Elem<T>::store(out, i, acc + ys[i]);
+}
+
+// ------------------------------------------------------------------------------ down + combine
+// Row ownership: block b owns RG row groups (RPW consecutive rows each) of the output, groups
+// b, b + nb, b + 2 nb, ... (interleaved, so the blocks that work in step read neighbouring
+// rows and every HBM channel stays busy).  Its work items are (a, row group) for every active
+// expert a and the shared expert (a = n_act); an item's dot products W2_a[n] . A[p] for each
+// position p of expert a land in LDS, and once all items are done the block writes
+// out[t][n] = RNE(h32[t][n] + sum_j g[t][j] * part[pos(t,j)][n] + part_shared[t][n]) (j in
+// ascending expert order, shared last), so the expert outputs never leave the chip.
+// Items are split into contiguous runs over the waves.  A wave alternates two register
+// buffers of U items (the loads of one in flight while the other is consumed), keeps the
+// activation values of the expert it is on in registers, and reads the active-expert tables
+// from its own lanes (lane i: expert act[i], its first position and its position count).
+template <typename T, int CPR, int NT, int U, int WPB, int MINB>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB * WPB / 4))) void down_combine_kernel(
+    const float* __restrict__ A, const float* __restrict__ As, const T* __restrict__ w2,
+    const T* __restrict__ ws2, const float* __restrict__ h32, int H, int k, int B, int RG,
+    Routing rt, T* __restrict__ out) {
+  using G = Geo<T, CPR>;
+  extern __shared__ float lds[];
+  const int nslot = B * k, nrow = nslot + B, RB = RG * G::RPW;
+  float* sA = lds;                               // [nslot + B][K]: A rows, then As rows
+  float* part = sA + (size_t)nrow * G::K;        // [nslot + B][RB]
+  float* sG = part + (size_t)nrow * RB;          // [nslot] gates
+  int* sQ = (int*)(sG + nslot);                  // [nslot] slot -> position
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane % G::SEG, seg = lane / G::SEG;
+  const int t_a = rt.act[lane];                  // act has E >= 64 entries (read before n_act)
+  const int n_act = min(*rt.n_act, 64);          // at most B * k <= 32 on this path
+  const int nb = gridDim.x;
+  auto row_of = [&](int rg, int sg) { return ((int)blockIdx.x + nb * rg) * G::RPW + sg; };
+  const int items = (n_act + 1) * RG;
+  const int i0 = wave * items / WPB, i1 = (wave + 1) * items / WPB;
+
+  // activation rows (up to 8 slots per token in registers; more are copied by a loop)
+  Stage<stage_q(8 * NT, G::K)> sta;
+  Stage<stage_q(NT, G::K)> sts;
+  sta.load(A, nslot * G::K);
+  sts.load(As, B * G::K);
+  const int t_e = lane < n_act ? t_a : 0;  // entries past n_act are not expert ids
+  const int t_lo = rt.offsets[t_e];
+  const int t_cnt = rt.offsets[t_e + 1] - t_lo;
+
+  // Two register buffers of U items.  Loads are never branched around: an item past the
+  // run's end reads the first row of A instead (L2-resident), so the waits stay exact.
+  u32x4 w0[U][G::CPL], w1[U][G::CPL];
+  const T* dummy = reinterpret_cast<const T*>(A);
+  struct Cursor { int it, a, rg; };
+  auto advance = [&](Cursor& c) {
+    ++c.it;
+    if (++c.rg == RG) { c.rg = 0; ++c.a; }
+  };
+  Cursor ci{i0, i0 / RG, i0 - (i0 / RG) * RG}, cc = ci;
+  auto issue = [&](u32x4 (&w)[U][G::CPL]) {
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int e = __builtin_amdgcn_readlane(t_e, min(ci.a, 63));
+      const T* src = ci.a < n_act ? w2 + (size_t)e * H * G::K : ws2;
+      const int n = min(row_of(ci.rg, seg), H - 1);
+      load_row<T, CPR>(ci.it < i1 ? src + (size_t)n * G::K : dummy, sub, w[q]);
+      advance(ci);
+    }
+  };
+  // The lane's activation values for the positions of the expert being consumed, held in
+  // registers while the run stays on that expert (reloaded from LDS when it moves on).
+  float xa[NT][G::CPL][G::EPC];
+  int a_cur = -1;
+  auto consume = [&](const u32x4 (&w)[U][G::CPL]) {
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      if (cc.it < i1) {
+        const int a = cc.a;
+        const bool routed = a < n_act;
+        const int r0 = routed ? __builtin_amdgcn_readlane(t_lo, min(a, 63)) : nslot;
+        const int cnt = routed ? __builtin_amdgcn_readlane(t_cnt, min(a, 63)) : B;
+        if (a != a_cur) {
+          a_cur = a;
+#pragma unroll
+          for (int qq = 0; qq < NT; ++qq) {
+            const float* row = sA + (size_t)(r0 + min(qq, cnt - 1)) * G::K;
+#pragma unroll
+            for (int i = 0; i < G::CPL; ++i) {
+              const int c = min(sub + G::SEG * i, CPR - 1);
+#pragma unroll
+              for (int h = 0; h < G::EPC / 4; ++h) {
+                const float4 v = reinterpret_cast<const float4*>(row + c * G::EPC)[h];
+                xa[qq][i][4 * h + 0] = v.x;
+                xa[qq][i][4 * h + 1] = v.y;
+                xa[qq][i][4 * h + 2] = v.z;
+                xa[qq][i][4 * h + 3] = v.w;
+              }
+            }
+          }
+        }
+        const int nl = cc.rg * G::RPW + seg;
+        const bool live = row_of(cc.rg, seg) < H;
+        float acc[NT];
+#pragma unroll
+        for (int qq = 0; qq < NT; ++qq) acc[qq] = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::CPL; ++i) {
+          if (G::EXACT || sub + G::SEG * i < CPR) {
+            float f[G::EPC];
+            Elem<T>::unpack(w[q][i], f);
+#pragma unroll
+            for (int qq = 0; qq < NT; ++qq)
+#pragma unroll
+              for (int x = 0; x < G::EPC; ++x) acc[qq] = fmaf(f[x], xa[qq][i][x], acc[qq]);
+          }
+        }
+        // (needed for every slot, used or not: keeps a slot's dot product out of its branch)
+#pragma unroll
+        for (int qq = 0; qq < NT; ++qq) asm volatile("" : "+v"(acc[qq]));
+#pragma unroll
+        for (int qq = 0; qq < NT; ++qq) {
+          const float v = seg_sum_dpp<G::SEG>(acc[qq]);
+          if (qq < cnt && sub == G::SEG - 1 && live) part[(r0 + qq) * RB + nl] = v;
+        }
+      }
+      advance(cc);
+    }
+  };
+  issue(w0);
+  issue(w1);
+  sta.store(sA);
+  sts.store(sA + (size_t)nslot * G::K);
+  // (n_act == 0 marks tables that failed validation: the routed terms are then left out, and
+  // positions are clamped so that no index leaves the block's arrays)
+  for (int i = threadIdx.x; i < nslot; i += blockDim.x) {
+    sG[i] = n_act > 0 ? rt.topk_gate[i] : 0.f;
+    sQ[i] = min(max(rt.inv_perm[i], 0), nslot - 1);
+  }
+  __syncthreads();
+  for (int base = i0; base < i1; base += 2 * U) {
+    consume(w0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(w0);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(w1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(w1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * RB; i += blockDim.x) {
+    const int t = i / RB, nl = i - t * RB;
+    const int n = row_of(nl / G::RPW, nl % G::RPW);
+    if (n < H) {
+      float acc = h32[(size_t)t * H + n];
+      if (n_act > 0)
+        for (int j = 0; j < k; ++j) acc = fmaf(sG[t * k + j], part[sQ[t * k + j] * RB + nl], acc);
+      Elem<T>::store(out, (size_t)t * H + n, acc + part[(nslot + t) * RB + nl]);
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------ prep
@@ -477,7 +694,7 @@ hipError_t topk_shared_t(const Shape& s, const Device& d, int B, const float* pa
   const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
   auto kern = B == 1 ? topk_shared_kernel<T, CPRH, 1> : topk_shared_kernel<T, CPRH, 2>;
   allow_lds(kern, lds);
-  const int blocks = ws13 ? 1 + d.num_cu : 1;
+  const int blocks = ws13 ? d.num_cu : 1;  // block 0 top-k, the rest shared rows: one wave of blocks
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, part, splits, bias, s.E, s.k,
                      B, s.routed_scale, rt, (const T*)ws13, s.Is, ws13 ? shared_split(s) : s.Is,
                      h32, As);
@@ -497,18 +714,41 @@ hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, cons
 }
 
 template <typename T, int CPR>
-hipError_t down_t(const Shape& s, const Device& d, int B, const float* A, const float* As,
-                  const void* w2, const void* ws2, const Routing& rt, float* Y, float* ys,
-                  hipStream_t st) {
+size_t down_combine_lds(const Shape& s, int B, int RG) {
   using G = Geo<T, CPR>;
-  constexpr int R = G::CPL >= 4 ? 2 : 4;  // rows per unit: 8 KB runs at I = 2048
-  const size_t lds = (size_t)(B * s.k + B) * G::K * sizeof(float);
-  auto kern = B == 1 ? down_gemv_kernel<T, CPR, 1, R> : down_gemv_kernel<T, CPR, 2, R>;
+  const int nslot = B * s.k, nrow = nslot + B;
+  return ((size_t)nrow * G::K + (size_t)nrow * RG * G::RPW + 2 * (size_t)nslot) * 4;
+}
+
+// Row groups per block: two blocks of 8 waves per CU when their LDS fits and the kernel
+// fits in 128 VGPRs (not so for two tokens' activations over 4 KB rows), else one.
+template <typename T, int CPR>
+int down_groups_per_block(const Shape& s, const Device& d, int B, int* per_cu) {
+  const int groups = (s.H + Geo<T, CPR>::RPW - 1) / Geo<T, CPR>::RPW;
+  const int rg2 = (groups + 2 * d.num_cu - 1) / (2 * d.num_cu);
+  const bool two = 2 * down_combine_lds<T, CPR>(s, B, rg2) <= (size_t)d.max_lds &&
+                   !(B == 2 && Geo<T, CPR>::CPL >= 4);
+  if (per_cu) *per_cu = two ? 2 : 1;
+  return two ? rg2 : (groups + d.num_cu - 1) / d.num_cu;
+}
+
+template <typename T, int CPR, int U>
+hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A, const float* As,
+                          const void* w2, const void* ws2, const float* h32, const Routing& rt,
+                          void* out, hipStream_t st) {
+  using G = Geo<T, CPR>;
+  int per_cu = 1;
+  const int RG = down_groups_per_block<T, CPR>(s, d, B, &per_cu);
+  const int groups = (s.H + G::RPW - 1) / G::RPW;
+  const size_t lds = down_combine_lds<T, CPR>(s, B, RG);
+  constexpr int NT2_PER_CU = Geo<T, CPR>::CPL >= 4 ? 1 : 2;
+  auto kern = per_cu == 2 ? (B == 1 ? down_combine_kernel<T, CPR, 1, U, 8, 2>
+                                    : down_combine_kernel<T, CPR, 2, U, 8, NT2_PER_CU>)
+                          : (B == 1 ? down_combine_kernel<T, CPR, 1, U, 8, 1>
+                                    : down_combine_kernel<T, CPR, 2, U, 8, 1>);
   allow_lds(kern, lds);
-  int bpc = (int)((size_t)d.max_lds / (lds ? lds : 1));
-  bpc = bpc < 1 ? 1 : (bpc > 2 ? 2 : bpc);
-  hipLaunchKernelGGL(kern, dim3(d.num_cu * bpc), dim3(kGemvThreads), lds, st, A, As, (const T*)w2,
-                     (const T*)ws2, s.H, s.k, B, rt, Y, ys);
+  hipLaunchKernelGGL(kern, dim3((groups + RG - 1) / RG), dim3(kGemvThreads), lds, st, A, As,
+                     (const T*)w2, (const T*)ws2, h32, s.H, s.k, B, RG, rt, (T*)out);
   return hipGetLastError();
 }
 
@@ -578,15 +818,25 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down_gemv(const Shape& s, const Device& d, int B, const float* A,
-                            const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, hipStream_t st) {
+size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B) {
+  const int c = cpr_of(s.I, s.dtype);
+  if (s.dtype == 1 && c == 256)
+    return down_combine_lds<uint16_t, 256>(s, B, down_groups_per_block<uint16_t, 256>(s, d, B, nullptr));
+  if (s.dtype == 1 && c == 16)
+    return down_combine_lds<uint16_t, 16>(s, B, down_groups_per_block<uint16_t, 16>(s, d, B, nullptr));
+  return down_combine_lds<float, 32>(s, B, down_groups_per_block<float, 32>(s, d, B, nullptr));
+}
+
+hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
+                                    const float* As, const void* w2, const void* ws2,
+                                    const float* h32, const Routing& rt, void* out,
+                                    hipStream_t st) {
   const int c = cpr_of(s.I, s.dtype);
   if (s.dtype == 1) {
-    if (c == 256) return down_t<uint16_t, 256>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
-    if (c == 16) return down_t<uint16_t, 16>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
+    if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
+    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
   } else if (c == 32) {
-    return down_t<float, 32>(s, d, B, A, As, w2, ws2, rt, Y, ys, st);
+    return down_combine_t<float, 32, 2>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
   }
   return hipErrorInvalidValue;
 }

@@ -67,13 +67,15 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
                               const void* w13, bool shared, const Routing& rt, float* A,
                               hipStream_t st);
 
-// Y[p][n] = W2_e[n] . A[p] for every position p of each active expert, ys[t][n] =
-// Ws2[n] . As[t] for the shared expert.
-hipError_t launch_down_gemv(const Shape& s, const Device& d, int B, const float* A,
-                            const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, hipStream_t st);
-
-// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] + ys[t][n]).
+// Down projection of the active experts and the shared expert fused with the weighted
+// combine (GEMV path): out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] +
+// ys[t][n]) with Y[p][n] = W2_e[n] . A[p] and ys[t][n] = Ws2[n] . As[t] kept on chip.
+size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B);
+hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
+                                    const float* As, const void* w2, const void* ws2,
+                                    const float* h32, const Routing& rt, void* out,
+                                    hipStream_t st);
+// Weighted combine of Y / ys written by the grouped MFMA down-projection.
 hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
                           const Routing& rt, void* out, hipStream_t st);
 

@@ -64,7 +64,7 @@ def test_plan_is_gemv_and_visible(name, B):
     _, _, L = gpu_layer(name)
     p = L.query_plan(B)
     assert p["path_name"] == "gemv" and p["forced"] == 0
-    assert p["kernels_per_step"] == 6 and p["streams"] == 1
+    assert p["kernels_per_step"] == 5 and p["streams"] == 1
 
 
 @pytest.mark.parametrize("name,B", GEMV_CASES)
@@ -195,3 +195,32 @@ def test_device_side_argument_errors():
     with pytest.raises(kk.KKError) as e:
         L.layer_decode(1, x, r, b["out"], ws, stream=0, graph=True)
     assert e.value.status == kk.KK_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("B", [2, 8])
+def test_invalid_tables_leave_routed_part_out(B):
+    """kk_moe_decode validates caller-supplied tables on the device: offsets that do not end at
+    B*k mark the routing invalid, no routed expert is read, and out = h + shared expert(h)."""
+    log(f"[invalid-tables] tp_rank B={B}")
+    torch = _torch()
+    import synth.device as sd
+    import oracle as O
+    from tests.gpu_common import host_layer_weights
+    cfg, _, L = gpu_layer("tp_rank")
+    ref = oracle_step("tp_rank", B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    L.oproj_residual(B, x, r, b["h32"], ws)
+    b["offsets"].zero_()
+    b["offsets"][-1] = B * cfg.top_k + 5
+    b["perm"].fill_(-7)
+    b["idx"].zero_()
+    b["gate"].fill_(0.5)
+    L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws)
+    torch.cuda.synchronize()
+    w = host_layer_weights("tp_rank")
+    ws13, ws2 = w.shared()
+    expect = ref["h"] + O.swiglu_expert(ref["h"], ws13, ws2)
+    rep = assert_close(as_f64_out(b["out"]), expect, "out without routed experts")
+    log(f"[invalid-tables] B={B}: {rep}")
