@@ -32,7 +32,7 @@ FLUSH_BYTES = 1 << 30
 COPY_BYTES = 256 << 20
 # rocprofv3 HBM byte counters per dominant kernel and workload: committed summaries, valid only
 # while the kernel's sources hash to what they were when the counters were taken
-TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/gateup_gemv_full_b1.json"}
+TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/topk_gateup_gemv_full_b1.json"}
 
 
 def measured_traffic(path_name: str, workload: str, B: int):
@@ -62,7 +62,8 @@ def unique_bytes(cfg, n_act: int) -> dict:
         "router": wb * E * H + 4 * E,
         "shared_gateup": wb * 2 * Is * H,
         "routed_gateup": wb * n_act * 2 * I * H,
-        "down": wb * (n_act * H * I + H * Is),
+        "shared_down": wb * H * Is,
+        "routed_down": wb * n_act * H * I,
     }
     parts["total"] = sum(parts.values())
     return parts
@@ -282,10 +283,14 @@ def main():
             kernels.setdefault(name, []).append(ms * 1e3)
         kernels = {k: statistics.mean(v) for k, v in kernels.items()}
 
-    dom_name = "gateup_gemv_routed" if plan["path_name"] == "gemv" else "gateup_mfma_routed"
+    # dominant kernel and the weight bytes one launch of it must read: on the GEMV path the
+    # routed gate/up launch also runs the top-k and streams the shared expert's down rows
+    if plan["path_name"] == "gemv":
+        dom_name, dom_bytes = "topk_gateup_gemv_routed", by["routed_gateup"] + by["shared_down"]
+    else:
+        dom_name, dom_bytes = "gateup_mfma_routed", by["routed_gateup"]
     roofline = None
     if dom_name in kernels:
-        dom_bytes = by["routed_gateup"]
         ach = dom_bytes / (kernels[dom_name] * 1e-6) / 1e9
         roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),

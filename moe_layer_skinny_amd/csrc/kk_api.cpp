@@ -119,14 +119,15 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
   return KK_OK;
 }
 
-const char* kernel_names[] = {"oproj_gemv",  "router_logits", "gateup_gemv_shared",
-                              "gateup_gemv_routed", "down_combine_gemv", "moe_prep", "topk_shared",
-                              "topk",        "combine",       "oproj_mfma", "oproj_reduce",
-                              "router_mfma", "gateup_mfma",   "down_mfma",  "topk_rows",
-                              "tables"};
+const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_logits",
+                              "gateup_gemv_shared", "gateup_gemv_routed", "topk_gateup_gemv_routed",
+                              "down_combine_gemv", "moe_prep",    "combine",    "oproj_mfma",
+                              "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
+                              "topk_rows",   "tables"};
 enum KName {
-  K_OPROJ, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_DOWN, K_PREP, K_TOPK_SHARED, K_TOPK, K_COMBINE,
-  K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS, K_TABLES
+  K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
+  K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
+  K_TABLES
 };
 
 struct TimingRec {
@@ -188,8 +189,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
     p->router_splitk = kk::router_gemv_splits(c->shape);
-    // oproj, router logits, top-k || shared gate/up, routed gate/up, down + combine
-    p->kernels_per_step = 5;
+    // oproj, router logits + shared gate/up, top-k + shared down + routed gate/up,
+    // routed down + combine
+    p->kernels_per_step = 4;
     return KK_OK;
   }
   if (!kk::mfma_supported(c->shape, B))
@@ -343,22 +345,15 @@ kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* h32, const kk::Rou
   return KK_OK;
 }
 
-// Router logits, then top-k / tables; with ws13 the shared expert's gate/up is split over
-// both launches.
-kk_status enqueue_router(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+// GEMV path: router logit partials (with ws13: and the shared expert's gate/up).
+kk_status enqueue_logits(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                          float* logit_part, const void* ws13, float* As, hipStream_t s) {
-  KK_HIP(timed(c, K_LOGITS, s,
+  KK_HIP(timed(c, ws13 ? K_LOGITS_SHARED : K_LOGITS, s,
                [&] {
                  return kk::launch_router_logits(c->shape, c->dev, B, h32, c->w.w_r, logit_part,
                                                  ws13, rt, As, s);
                }),
          "router logits launch");
-  KK_HIP(timed(c, ws13 ? K_TOPK_SHARED : K_TOPK, s,
-               [&] {
-                 return kk::launch_topk_shared(c->shape, c->dev, B, logit_part, c->w.bias, rt, ws13,
-                                               h32, As, s);
-               }),
-         "top-k launch");
   return KK_OK;
 }
 
@@ -366,32 +361,41 @@ kk_status enqueue_shared_gateup(kk_ctx* c, int B, const float* h32, const kk::Ro
                                 float* As, hipStream_t s) {
   KK_HIP(timed(c, K_GU_SHARED, s,
                [&] {
-                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt, As, s);
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt, As,
+                                               kk::GateupExtras{}, s);
                }),
          "shared gate/up launch");
   return KK_OK;
 }
 
-kk_status enqueue_down_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
-                               const WsPtrs& p, void* out, hipStream_t s) {
+// Routed gate/up (with the shared expert's down-projection in its first moments; with
+// logit_part: after running the top-k itself), then the routed down-projection and the
+// combine, on s.
+kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+                                     const WsPtrs& p, const float* logit_part, void* out,
+                                     hipStream_t s) {
+  kk::GateupExtras x;
+  if (logit_part) {
+    x.part = logit_part;
+    x.splits = kk::router_gemv_splits(c->shape);
+    x.bias = c->w.bias;
+  }
+  x.ws2 = c->w.ws2;
+  x.As = p.As;
+  x.ys = p.ys;
+  KK_HIP(timed(c, logit_part ? K_TOPK_GU : K_GU_ROUTED, s,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A,
+                                               x, s);
+               }),
+         "routed gate/up launch");
   KK_HIP(timed(c, K_DOWN, s,
                [&] {
-                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.As, c->w.w2,
-                                                     c->w.ws2, h32, rt, out, s);
+                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.ys, c->w.w2, h32,
+                                                     rt, out, s);
                }),
          "down + combine launch");
   return KK_OK;
-}
-
-// Routed gate/up, then the routed + shared down-projection and the combine, on s.
-kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
-                                     const WsPtrs& p, void* out, hipStream_t s) {
-  KK_HIP(timed(c, K_GU_ROUTED, s,
-               [&] {
-                 return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A, s);
-               }),
-         "routed gate/up launch");
-  return enqueue_down_combine(c, B, h32, rt, p, out, s);
 }
 
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
@@ -407,26 +411,22 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
     return enqueue_experts_mfma(c, B, p.h32, rt, p, out, s);
   }
   if (!two_stream) {
-    // the shared expert's gate/up streams inside the top-k launch
-    st = enqueue_router(c, B, p.h32, rt, p.logit_part, c->w.ws13, p.As, s);
+    // the shared expert's gate/up streams with the router logits, its down-projection
+    // with the top-k at the start of the routed gate/up launch
+    st = enqueue_logits(c, B, p.h32, rt, p.logit_part, c->w.ws13, p.As, s);
     if (st != KK_OK) return st;
-    return enqueue_routed_and_combine(c, B, p.h32, rt, p, out, s);
+    return enqueue_routed_and_combine(c, B, p.h32, rt, p, p.logit_part, out, s);
   }
-  // shared expert's gate/up on the auxiliary stream, joined before the down-projection
+  // shared expert's gate/up on the auxiliary stream, joined before the routed gate/up
   KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
   KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
   st = enqueue_shared_gateup(c, B, p.h32, rt, p.As, c->aux);
   if (st != KK_OK) return st;
   KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
-  st = enqueue_router(c, B, p.h32, rt, p.logit_part, nullptr, nullptr, s);
+  st = enqueue_logits(c, B, p.h32, rt, p.logit_part, nullptr, nullptr, s);
   if (st != KK_OK) return st;
-  KK_HIP(timed(c, K_GU_ROUTED, s,
-               [&] {
-                 return kk::launch_gateup_gemv(c->shape, c->dev, B, p.h32, c->w.w13, false, rt, p.A, s);
-               }),
-         "routed gate/up launch");
   KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
-  return enqueue_down_combine(c, B, p.h32, rt, p, out, s);
+  return enqueue_routed_and_combine(c, B, p.h32, rt, p, p.logit_part, out, s);
 }
 
 void destroy_graphs(kk_ctx* c) {
@@ -568,7 +568,19 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
     if (plan.path == KK_PATH_SPLITK_MFMA)
       return enqueue_router_mfma(c, B, h32, rt, p.logit_part, (hipStream_t)stream);
-    return enqueue_router(c, B, h32, rt, p.logit_part, nullptr, nullptr, (hipStream_t)stream);
+    // GEMV path on its own: logits, then the top-k rows and the tables
+    hipStream_t s = (hipStream_t)stream;
+    st = enqueue_logits(c, B, h32, rt, p.logit_part, nullptr, nullptr, s);
+    if (st != KK_OK) return st;
+    KK_HIP(timed(c, K_TOPK_ROWS, s,
+                 [&] {
+                   return kk::launch_topk_rows(c->shape, B, p.logit_part,
+                                               kk::router_gemv_splits(c->shape), c->w.bias, rt, s);
+                 }),
+           "top-k launch");
+    KK_HIP(timed(c, K_TABLES, s, [&] { return kk::launch_tables(c->shape, B, rt, s); }),
+           "routing tables launch");
+    return KK_OK;
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_router_topk");
   }
@@ -597,7 +609,7 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
     if (plan.path == KK_PATH_SPLITK_MFMA) return enqueue_experts_mfma(c, B, h32, rt, p, out, s);
     st = enqueue_shared_gateup(c, B, h32, rt, p.As, s);
     if (st != KK_OK) return st;
-    return enqueue_routed_and_combine(c, B, h32, rt, p, out, s);
+    return enqueue_routed_and_combine(c, B, h32, rt, p, nullptr, out, s);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_moe_decode");
   }

@@ -177,72 +177,52 @@ __device__ __forceinline__ void shared_rows(const T* __restrict__ ws13, int Is, 
   }
 }
 
-// Logit partials part[s][t][e] over `splits` K-slices (one (expert, slice) unit per wave,
-// h32 read from L2); with ws13 != nullptr the launch also streams the shared expert's
-// gate/up rows [0, i_split), each wave's first row pair requested before the logit work so
-// HBM stays busy through this latency-bound phase.
+// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s] (at most two
+// (expert, slice) units per wave) and, with ws13 != nullptr, the shared expert's gate/up
+// rows, As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  Every wave requests its router
+// slices and its first shared row pair at the start, so the launch streams both weight sets
+// at full bandwidth; the top-k runs at the start of the routed gate/up launch.
 template <typename T, int CPS, int CPRH, int NT>
 __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
     const float* __restrict__ h32, const T* __restrict__ w_r, int H, int E, int B, int splits,
-    float* __restrict__ part, const T* __restrict__ ws13, int Is, int i_split, int k, Routing rt,
+    float* __restrict__ part, const T* __restrict__ ws13, int Is, int k, Routing rt,
     float* __restrict__ As) {
   using G = Geo<T, CPS>;
   using GH = Geo<T, CPRH>;
-  extern __shared__ float lds[];  // u [B][H] when the shared rows are streamed here
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
+  constexpr int MAXU = 2;  // (expert, slice) units per wave; the host checks E * splits
+  extern __shared__ float lds[];  // u [B][H]
+  const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
   const bool shared = ws13 != nullptr;
-  u32x4 wg[GH::CPL], wu[GH::CPL];
-  if (shared && gw < i_split) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
-  if (shared) {
-    // the first logit load waits for the row pair anyway (loads complete in order), so the
-    // u rows are staged here, behind it, without holding registers through the logit loop
-    Stage<stage_q(NT, GH::K)> st;
-    st.load(h32, B * GH::K);
-    st.store(lds);
-  }
   const int units = E * splits;
-  for (int unit = gw; unit < units; unit += nw) {
-    const int e = unit / splits, s = unit - e * splits;
-    u32x4 w[G::CPL];
-    load_row<T, CPS>(w_r + (size_t)e * H + (size_t)s * G::K, lane, w);
+  // router slices of this wave's units (a missing second unit re-reads the last one)
+  u32x4 wr[MAXU][G::CPL];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float acc =
-          seg_sum<64>(dot_lane<T, CPS>(w, h32 + (size_t)t * H + (size_t)s * G::K, lane));
-      if (lane == 0) part[((size_t)s * B + t) * E + e] = acc;
-    }
+  for (int j = 0; j < MAXU; ++j) {
+    const int un = min(gw + j * nw, units - 1);
+    const int e = un / splits, sl = un - e * splits;
+    load_row<T, CPS>(w_r + (size_t)e * H + (size_t)sl * G::K, lane, wr[j]);
   }
-  if (!shared) return;
-  __syncthreads();
-  shared_rows<T, CPRH, NT>(ws13, Is, 0, i_split, gw, nw, wg, wu, lds, k, B, rt, As, lane);
-}
-
-// Block 0: top-k, gates and routing tables from the logit partials.  Blocks 1..: the shared
-// expert's gate/up rows [i_split, Is) over all B tokens (ws13 != nullptr), so its weight
-// stream overlaps the serial top-k without any cross-block communication.
-template <typename T, int CPRH, int NT>
-__global__ __launch_bounds__(kGemvThreads) void topk_shared_kernel(
-    const float* __restrict__ part, int splits, const float* __restrict__ bias, int E, int k,
-    int B, float routed_scale, Routing rt, const T* __restrict__ ws13, int Is, int i_split,
-    const float* __restrict__ h32, float* __restrict__ As) {
-  using GH = Geo<T, CPRH>;
-  extern __shared__ float lds[];  // blocks >= 1: u [B][H]
-  if (blockIdx.x == 0) {
-    __shared__ TopkScratch sm;
-    topk_tables(part, splits, bias, B, E, k, routed_scale, rt, sm);
-    return;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wpb = blockDim.x >> 6;
-  const int nw = (gridDim.x - 1) * wpb;
-  const int gw = (blockIdx.x - 1) * wpb + wave;
   u32x4 wg[GH::CPL], wu[GH::CPL];
+  if (shared && gw < Is) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
   Stage<stage_q(NT, GH::K)> st;
-  st.load(h32, B * GH::K);
-  if (i_split + gw < Is) load_pair<T, CPRH>(ws13, 0, i_split + gw, Is, wg, wu, lane);
+  st.load(h32, B * H);
   st.store(lds);
   __syncthreads();
-  shared_rows<T, CPRH, NT>(ws13, Is, i_split, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
+#pragma unroll
+  for (int j = 0; j < MAXU; ++j) {
+    const int un = gw + j * nw;
+    if (un < units) {
+      const int e = un / splits, sl = un - e * splits;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float v = seg_sum_dpp<64>(dot_lane<T, CPS>(wr[j], lds + t * H + sl * G::K, lane));
+        if (t < B && lane == 63) part[((size_t)sl * B + t) * E + e] = v;
+      }
+    }
+  }
+  if (shared) shared_rows<T, CPRH, NT>(ws13, Is, 0, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
 
 // ------------------------------------------------------------------------------ top-k, large batch
@@ -263,6 +243,81 @@ __global__ __launch_bounds__(256) void tables_kernel(int E, int k, int B, Routin
 }
 
 // ------------------------------------------------------------------------------ gate / up
+// Shared expert's down-projection rows for this launch's workers (waves 1.. of every block):
+// ys[t][n] = Ws2[n] . As[t] over row groups g = worker, worker + nworkers, ...; each worker
+// requests up to R row groups at once.
+template <typename T, int CPRS, int NT, int R>
+__device__ __forceinline__ void shared_down_rows(const T* __restrict__ ws2,
+                                                 const float* __restrict__ As,
+                                                 float* __restrict__ ys, int H, int B,
+                                                 int worker, int nworkers, int lane) {
+  using G = Geo<T, CPRS>;
+  const int sub = lane % G::SEG, seg = lane / G::SEG;
+  const int groups = (H + G::RPW - 1) / G::RPW;
+  // the lane's activation values (As is fp32 [B][Is])
+  float xa[NT][G::CPL][G::EPC];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < G::CPL; ++i) {
+      const int c = min(sub + G::SEG * i, CPRS - 1);
+      const float4* p = reinterpret_cast<const float4*>(As + (size_t)min(t, B - 1) * G::K + c * G::EPC);
+#pragma unroll
+      for (int h = 0; h < G::EPC / 4; ++h) {
+        const float4 v = p[h];
+        xa[t][i][4 * h + 0] = v.x;
+        xa[t][i][4 * h + 1] = v.y;
+        xa[t][i][4 * h + 2] = v.z;
+        xa[t][i][4 * h + 3] = v.w;
+      }
+    }
+  for (int g0 = worker; g0 < groups; g0 += R * nworkers) {
+    u32x4 w[R][G::CPL];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int n = min((g0 + q * nworkers) * G::RPW + seg, H - 1);
+      load_row<T, CPRS>(ws2 + (size_t)n * G::K, sub, w[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int g = g0 + q * nworkers;
+      const int n = g * G::RPW + seg;
+      float acc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = 0.f;
+#pragma unroll
+      for (int i = 0; i < G::CPL; ++i) {
+        if (G::EXACT || sub + G::SEG * i < CPRS) {
+          float f[G::EPC];
+          Elem<T>::unpack(w[q][i], f);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int x = 0; x < G::EPC; ++x) acc[t] = fmaf(f[x], xa[t][i][x], acc[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(acc[t]));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float v = seg_sum_dpp<G::SEG>(acc[t]);
+        if (t < B && g < groups && n < H && sub == G::SEG - 1) ys[(size_t)t * H + n] = v;
+      }
+    }
+  }
+}
+
+// Routing tables held in LDS by the routed gate/up launch when it runs the top-k itself.
+struct LdsTables {
+  int idx[kMaxSlots];
+  float gate[kMaxSlots];
+  int perm[kMaxSlots];
+  int inv[kMaxSlots];
+  int offsets[kMaxExperts + 1];
+  int act[kMaxExperts];
+  int n_act;
+};
+
 // Routed experts (act / n_act / offsets / perm) or the shared expert (positions = tokens).
 // One wave per (expert, row i) unit: gate row i and up row i against the unit's tokens,
 // A[position][i] = silu(W1[i] . u_t) * (W3[i] . u_t).  A unit's two rows are fetched in two
@@ -270,27 +325,66 @@ __global__ __launch_bounds__(256) void tables_kernel(int E, int k, int B, Routin
 // while it works on the other (a unit past the end fetches from the activation buffer, so
 // no load is branched around).  Tables come from the wave's own lanes: lane j holds act[j],
 // the first position of that expert and its position count, lane p the token of position p.
-template <typename T, int CPR, int NT>
+//
+// Before the routed rows, the launch can do two things that only need the previous launch:
+//  * TOPK: every block runs the top-k from the logit partials (wave 0) and builds the
+//    routing tables in its own LDS -- the same bits in every block; block 0 also writes
+//    them out (topk_idx / topk_gate / offsets / perm / inv_perm / act / n_act);
+//  * ws2 != nullptr: waves 1.. compute the shared expert's down-projection into ys, so its
+//    weight stream covers the top-k's latency.
+template <typename T, int CPR, int CPRS, int NT, bool TOPK>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     const float* __restrict__ u, const T* __restrict__ w13, int I, int k, int B, int shared,
-    Routing rt, float* __restrict__ A) {
+    Routing rt, float* __restrict__ A, const float* __restrict__ part, int splits,
+    const float* __restrict__ bias, int E, float routed_scale, const T* __restrict__ ws2,
+    const float* __restrict__ As, float* __restrict__ ys, int H) {
   using G = Geo<T, CPR>;
   static_assert(G::SEG == 64 && G::EXACT, "gate/up rows must span the wave exactly");
   constexpr int HA = (G::CPL + 1) / 2, HB = G::CPL - HA;
   extern __shared__ float lds[];  // u [B][K]
+  __shared__ TopkScratch sm;
+  __shared__ LdsTables tb;
   const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nslot = B * k;
-  // (act has at least 64 entries; entries past n_act are not expert ids)
-  const int t_a = rt.act[lane];
-  const int t_p = rt.perm[min(lane, nslot - 1)];
-  const int n = shared ? 1 : min(*rt.n_act, 64);
-  const int t_e = (!shared && lane < n) ? t_a : 0;
-  const int t_lo = shared ? 0 : rt.offsets[t_e];
-  const int t_cnt = shared ? B : rt.offsets[t_e + 1] - t_lo;
-  const int t_tok = min(max(t_p / k, 0), B - 1);
   Stage<stage_q(NT, G::K)> st;
   st.load(u, B * G::K);
+  if (TOPK && wave == 0) {
+    Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
+    for (int t = 0; t < B; ++t) topk_row(part, splits, bias, B, E, k, routed_scale, t, rl, sm.sel);
+  }
+  if (ws2 && wave > 0)
+    shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, blockIdx.x * (wpb - 1) + wave - 1,
+                                     gridDim.x * (wpb - 1), lane);
+  st.store(lds);
+  __syncthreads();
+  if (TOPK) {
+    Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
+    build_tables(B, E, k, rl, sm);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      for (int i = threadIdx.x; i < nslot; i += blockDim.x) {
+        rt.topk_idx[i] = tb.idx[i];
+        rt.topk_gate[i] = tb.gate[i];
+        rt.perm[i] = tb.perm[i];
+        rt.inv_perm[i] = tb.inv[i];
+      }
+      for (int i = threadIdx.x; i <= E; i += blockDim.x) rt.offsets[i] = tb.offsets[i];
+      for (int i = threadIdx.x; i < tb.n_act; i += blockDim.x) rt.act[i] = tb.act[i];
+      if (threadIdx.x == 0) *rt.n_act = tb.n_act;
+    }
+  }
+  // (act has at least 64 entries; entries past n_act are not expert ids)
+  const int* act = TOPK ? tb.act : rt.act;
+  const int* offsets = TOPK ? tb.offsets : rt.offsets;
+  const int* perm = TOPK ? tb.perm : rt.perm;
+  const int t_a = act[lane];
+  const int t_p = perm[min(lane, nslot - 1)];
+  const int n = shared ? 1 : min(TOPK ? tb.n_act : *rt.n_act, 64);
+  const int t_e = (!shared && lane < n) ? t_a : 0;
+  const int t_lo = shared ? 0 : offsets[t_e];
+  const int t_cnt = shared ? B : offsets[t_e + 1] - t_lo;
+  const int t_tok = min(max(t_p / k, 0), B - 1);
 
   const int units = n * I;
   const int stride = gridDim.x * wpb;
@@ -352,8 +446,6 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   int cur = blockIdx.x * wpb + wave;
   issue_a(cur);
   issue_b(cur);
-  st.store(lds);
-  __syncthreads();
   for (; cur < units; cur += stride) {
     const int a = cur / I, i = cur - a * I;
     const int p0 = __builtin_amdgcn_readlane(t_lo, min(a, 63));
@@ -433,25 +525,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Row ownership: block b owns RG row groups (RPW consecutive rows each) of the output, groups
 // b, b + nb, b + 2 nb, ... (interleaved, so the blocks that work in step read neighbouring
 // rows and every HBM channel stays busy).  Its work items are (a, row group) for every active
-// expert a and the shared expert (a = n_act); an item's dot products W2_a[n] . A[p] for each
-// position p of expert a land in LDS, and once all items are done the block writes
-// out[t][n] = RNE(h32[t][n] + sum_j g[t][j] * part[pos(t,j)][n] + part_shared[t][n]) (j in
-// ascending expert order, shared last), so the expert outputs never leave the chip.
+// expert a; an item's dot products W2_a[n] . A[p] for each position p of expert a land in
+// LDS, and once all items are done the block writes out[t][n] = RNE(h32[t][n] + sum_j
+// g[t][j] * part[pos(t,j)][n] + ys[t][n]) (j in ascending expert order, then the shared
+// expert's output ys), so the routed expert outputs never leave the chip.
 // Items are split into contiguous runs over the waves.  A wave alternates two register
 // buffers of U items (the loads of one in flight while the other is consumed), keeps the
 // activation values of the expert it is on in registers, and reads the active-expert tables
 // from its own lanes (lane i: expert act[i], its first position and its position count).
 template <typename T, int CPR, int NT, int U, int WPB, int MINB>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB * WPB / 4))) void down_combine_kernel(
-    const float* __restrict__ A, const float* __restrict__ As, const T* __restrict__ w2,
-    const T* __restrict__ ws2, const float* __restrict__ h32, int H, int k, int B, int RG,
-    Routing rt, T* __restrict__ out) {
+    const float* __restrict__ A, const float* __restrict__ ys, const T* __restrict__ w2,
+    const float* __restrict__ h32, int H, int k, int B, int RG, Routing rt,
+    T* __restrict__ out) {
   using G = Geo<T, CPR>;
   extern __shared__ float lds[];
-  const int nslot = B * k, nrow = nslot + B, RB = RG * G::RPW;
-  float* sA = lds;                               // [nslot + B][K]: A rows, then As rows
-  float* part = sA + (size_t)nrow * G::K;        // [nslot + B][RB]
-  float* sG = part + (size_t)nrow * RB;          // [nslot] gates
+  const int nslot = B * k, RB = RG * G::RPW;
+  float* sA = lds;                               // [nslot][K]: A rows
+  float* part = sA + (size_t)nslot * G::K;       // [nslot][RB]
+  float* sG = part + (size_t)nslot * RB;         // [nslot] gates
   int* sQ = (int*)(sG + nslot);                  // [nslot] slot -> position
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -460,14 +552,12 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
   const int n_act = min(*rt.n_act, 64);          // at most B * k <= 32 on this path
   const int nb = gridDim.x;
   auto row_of = [&](int rg, int sg) { return ((int)blockIdx.x + nb * rg) * G::RPW + sg; };
-  const int items = (n_act + 1) * RG;
+  const int items = n_act * RG;
   const int i0 = wave * items / WPB, i1 = (wave + 1) * items / WPB;
 
   // activation rows (up to 8 slots per token in registers; more are copied by a loop)
   Stage<stage_q(8 * NT, G::K)> sta;
-  Stage<stage_q(NT, G::K)> sts;
   sta.load(A, nslot * G::K);
-  sts.load(As, B * G::K);
   const int t_e = lane < n_act ? t_a : 0;  // entries past n_act are not expert ids
   const int t_lo = rt.offsets[t_e];
   const int t_cnt = rt.offsets[t_e + 1] - t_lo;
@@ -486,9 +576,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
 #pragma unroll
     for (int q = 0; q < U; ++q) {
       const int e = __builtin_amdgcn_readlane(t_e, min(ci.a, 63));
-      const T* src = ci.a < n_act ? w2 + (size_t)e * H * G::K : ws2;
       const int n = min(row_of(ci.rg, seg), H - 1);
-      load_row<T, CPR>(ci.it < i1 ? src + (size_t)n * G::K : dummy, sub, w[q]);
+      load_row<T, CPR>(ci.it < i1 ? w2 + ((size_t)e * H + n) * G::K : dummy, sub, w[q]);
       advance(ci);
     }
   };
@@ -501,9 +590,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
     for (int q = 0; q < U; ++q) {
       if (cc.it < i1) {
         const int a = cc.a;
-        const bool routed = a < n_act;
-        const int r0 = routed ? __builtin_amdgcn_readlane(t_lo, min(a, 63)) : nslot;
-        const int cnt = routed ? __builtin_amdgcn_readlane(t_cnt, min(a, 63)) : B;
+        const int r0 = __builtin_amdgcn_readlane(t_lo, min(a, 63));
+        const int cnt = __builtin_amdgcn_readlane(t_cnt, min(a, 63));
         if (a != a_cur) {
           a_cur = a;
 #pragma unroll
@@ -554,7 +642,6 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
   issue(w0);
   issue(w1);
   sta.store(sA);
-  sts.store(sA + (size_t)nslot * G::K);
   // (n_act == 0 marks tables that failed validation: the routed terms are then left out, and
   // positions are clamped so that no index leaves the block's arrays)
   for (int i = threadIdx.x; i < nslot; i += blockDim.x) {
@@ -579,7 +666,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
       float acc = h32[(size_t)t * H + n];
       if (n_act > 0)
         for (int j = 0; j < k; ++j) acc = fmaf(sG[t * k + j], part[sQ[t * k + j] * RB + nl], acc);
-      Elem<T>::store(out, (size_t)t * H + n, acc + part[(nslot + t) * RB + nl]);
+      Elem<T>::store(out, (size_t)t * H + n, acc + ys[(size_t)t * H + n]);
     }
   }
 }
@@ -667,57 +754,45 @@ hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const 
   return hipGetLastError();
 }
 
-// Shared expert rows streamed by the logits launch (the rest go with the top-k launch).
-inline int shared_split(const Shape& s) { return s.Is / 2; }
-
 template <typename T, int CPS, int CPRH>
 hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* h32,
                            const void* w_r, float* part, const void* ws13, const Routing& rt,
                            float* As, hipStream_t st) {
   const int splits = s.H / Geo<T, CPS>::K;
-  const int units = s.E * splits;
-  const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
+  const int nw = d.num_cu * (kGemvThreads / 64);
+  if (s.E * splits > 2 * nw) return hipErrorInvalidValue;
+  const size_t lds = (size_t)B * s.H * sizeof(float);
   auto kern = B == 1 ? router_logits_kernel<T, CPS, CPRH, 1> : router_logits_kernel<T, CPS, CPRH, 2>;
   allow_lds(kern, lds);
-  int blocks = (units + 7) / 8;
-  if (ws13 && blocks < d.num_cu) blocks = d.num_cu;
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, s.H, s.E,
-                     B, splits, part, (const T*)ws13, s.Is, ws13 ? shared_split(s) : 0, s.k, rt, As);
+  hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, s.H,
+                     s.E, B, splits, part, (const T*)ws13, s.Is, s.k, rt, As);
   return hipGetLastError();
 }
 
-template <typename T, int CPS, int CPRH>
-hipError_t topk_shared_t(const Shape& s, const Device& d, int B, const float* part,
-                         const float* bias, const Routing& rt, const void* ws13,
-                         const float* h32, float* As, hipStream_t st) {
-  const int splits = s.H / Geo<T, CPS>::K;
-  const size_t lds = ws13 ? (size_t)B * Geo<T, CPRH>::K * sizeof(float) : 0;
-  auto kern = B == 1 ? topk_shared_kernel<T, CPRH, 1> : topk_shared_kernel<T, CPRH, 2>;
-  allow_lds(kern, lds);
-  const int blocks = ws13 ? d.num_cu : 1;  // block 0 top-k, the rest shared rows: one wave of blocks
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(kGemvThreads), lds, st, part, splits, bias, s.E, s.k,
-                     B, s.routed_scale, rt, (const T*)ws13, s.Is, ws13 ? shared_split(s) : s.Is,
-                     h32, As);
-  return hipGetLastError();
-}
-
-template <typename T, int CPR>
+template <typename T, int CPR, int CPRS>
 hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, const void* w13,
-                    bool shared, const Routing& rt, float* A, hipStream_t st) {
+                    bool shared, const Routing& rt, float* A, const GateupExtras& x,
+                    hipStream_t st) {
+  if (x.part && (x.splits > kMaxTopkSplits || shared)) return hipErrorInvalidValue;
   const size_t lds = (size_t)B * Geo<T, CPR>::K * sizeof(float);
-  auto kern = B == 1 ? gateup_gemv_kernel<T, CPR, 1> : gateup_gemv_kernel<T, CPR, 2>;
+  auto pick = [&](auto k1, auto k2) { return B == 1 ? k1 : k2; };
+  auto kern = x.part ? pick(gateup_gemv_kernel<T, CPR, CPRS, 1, true>,
+                            gateup_gemv_kernel<T, CPR, CPRS, 2, true>)
+                     : pick(gateup_gemv_kernel<T, CPR, CPRS, 1, false>,
+                            gateup_gemv_kernel<T, CPR, CPRS, 2, false>);
   allow_lds(kern, lds);
   const int inter = shared ? s.Is : s.I;
   hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, u, (const T*)w13, inter,
-                     s.k, B, shared ? 1 : 0, rt, A);
+                     s.k, B, shared ? 1 : 0, rt, A, x.part, x.splits, x.bias, s.E, s.routed_scale,
+                     (const T*)x.ws2, x.As, x.ys, s.H);
   return hipGetLastError();
 }
 
 template <typename T, int CPR>
 size_t down_combine_lds(const Shape& s, int B, int RG) {
   using G = Geo<T, CPR>;
-  const int nslot = B * s.k, nrow = nslot + B;
-  return ((size_t)nrow * G::K + (size_t)nrow * RG * G::RPW + 2 * (size_t)nslot) * 4;
+  const int nslot = B * s.k;
+  return ((size_t)nslot * G::K + (size_t)nslot * RG * G::RPW + 2 * (size_t)nslot) * 4;
 }
 
 // Row groups per block: two blocks of 8 waves per CU when their LDS fits and the kernel
@@ -733,9 +808,9 @@ int down_groups_per_block(const Shape& s, const Device& d, int B, int* per_cu) {
 }
 
 template <typename T, int CPR, int U>
-hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A, const float* As,
-                          const void* w2, const void* ws2, const float* h32, const Routing& rt,
-                          void* out, hipStream_t st) {
+hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A, const float* ys,
+                          const void* w2, const float* h32, const Routing& rt, void* out,
+                          hipStream_t st) {
   using G = Geo<T, CPR>;
   int per_cu = 1;
   const int RG = down_groups_per_block<T, CPR>(s, d, B, &per_cu);
@@ -747,8 +822,8 @@ hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A
                           : (B == 1 ? down_combine_kernel<T, CPR, 1, U, 8, 1>
                                     : down_combine_kernel<T, CPR, 2, U, 8, 1>);
   allow_lds(kern, lds);
-  hipLaunchKernelGGL(kern, dim3((groups + RG - 1) / RG), dim3(kGemvThreads), lds, st, A, As,
-                     (const T*)w2, (const T*)ws2, h32, s.H, s.k, B, RG, rt, (T*)out);
+  hipLaunchKernelGGL(kern, dim3((groups + RG - 1) / RG), dim3(kGemvThreads), lds, st, A, ys,
+                     (const T*)w2, h32, s.H, s.k, B, RG, rt, (T*)out);
   return hipGetLastError();
 }
 
@@ -799,22 +874,16 @@ hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const fl
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk_shared(const Shape& s, const Device& d, int B, const float* part,
-                              const float* bias, const Routing& rt, const void* ws13,
-                              const float* h32, float* As, hipStream_t st) {
-  if (s.dtype == 1 && s.H == 7168)
-    return topk_shared_t<uint16_t, 128, 896>(s, d, B, part, bias, rt, ws13, h32, As, st);
-  if (s.dtype == 0 && s.H == 256)
-    return topk_shared_t<float, 64, 64>(s, d, B, part, bias, rt, ws13, h32, As, st);
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const float* u,
                               const void* w13, bool shared, const Routing& rt, float* A,
-                              hipStream_t st) {
-  const int c = cpr_of(s.H, s.dtype);
-  if (s.dtype == 1 && c == 896) return gateup_t<uint16_t, 896>(s, d, B, u, w13, shared, rt, A, st);
-  if (s.dtype == 0 && c == 64) return gateup_t<float, 64>(s, d, B, u, w13, shared, rt, A, st);
+                              const GateupExtras& x, hipStream_t st) {
+  const int c = cpr_of(s.H, s.dtype), cs = cpr_of(s.Is, s.dtype);
+  if (s.dtype == 1 && c == 896 && cs == 256)
+    return gateup_t<uint16_t, 896, 256>(s, d, B, u, w13, shared, rt, A, x, st);
+  if (s.dtype == 1 && c == 896 && cs == 16)
+    return gateup_t<uint16_t, 896, 16>(s, d, B, u, w13, shared, rt, A, x, st);
+  if (s.dtype == 0 && c == 64 && cs == 32)
+    return gateup_t<float, 64, 32>(s, d, B, u, w13, shared, rt, A, x, st);
   return hipErrorInvalidValue;
 }
 
@@ -828,15 +897,14 @@ size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B) {
 }
 
 hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
-                                    const float* As, const void* w2, const void* ws2,
-                                    const float* h32, const Routing& rt, void* out,
-                                    hipStream_t st) {
+                                    const float* ys, const void* w2, const float* h32,
+                                    const Routing& rt, void* out, hipStream_t st) {
   const int c = cpr_of(s.I, s.dtype);
   if (s.dtype == 1) {
-    if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
-    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
+    if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, ys, w2, h32, rt, out, st);
+    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, ys, w2, h32, rt, out, st);
   } else if (c == 32) {
-    return down_combine_t<float, 32, 2>(s, d, B, A, As, w2, ws2, h32, rt, out, st);
+    return down_combine_t<float, 32, 2>(s, d, B, A, ys, w2, h32, rt, out, st);
   }
   return hipErrorInvalidValue;
 }

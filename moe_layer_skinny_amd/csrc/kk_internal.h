@@ -48,33 +48,38 @@ bool gemv_supported(const Shape& s, int B);
 hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void* x, const void* r,
                              const void* w_o, float* h32, void* h_out, hipStream_t st);
 
-// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s].  With ws13 !=
-// nullptr the same launch computes the first half of the shared expert's gate/up rows,
-// As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t); launch_topk_shared does the rest.
+// Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s]; with ws13 !=
+// nullptr the same launch computes the shared expert's gate/up,
+// As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  The top-k runs in the routed gate/up
+// launch (GateupExtras::part) or, on its own, in launch_topk_rows + launch_tables.
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
                                 const void* w_r, float* partials, const void* ws13,
                                 const Routing& rt, float* As, hipStream_t st);
-// Top-k, gates and routing tables from the partials (one block); with ws13 != nullptr the
-// same launch computes the second half of the shared expert's gate/up in its other blocks.
-hipError_t launch_topk_shared(const Shape& s, const Device& d, int B, const float* partials,
-                              const float* bias, const Routing& rt, const void* ws13,
-                              const float* h32, float* As, hipStream_t st);
 int router_gemv_splits(const Shape& s);
+
+// Optional work of the routed gate/up launch.
+struct GateupExtras {
+  const float* part = nullptr;  // logit partials [splits][B][E]: run the top-k in the launch
+  int splits = 0;               // and write the routing tables (rt) from its block 0
+  const float* bias = nullptr;
+  const void* ws2 = nullptr;    // shared expert's down-projection ys = Ws2 . As in the launch
+  const float* As = nullptr;
+  float* ys = nullptr;
+};
 
 // Routed gate/up over the active experts (act/n_act) or the shared expert (shared=true):
 // A[position][i] = silu(W1[i] . u_t) * (W3[i] . u_t), t = token of the position.
 hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const float* u,
                               const void* w13, bool shared, const Routing& rt, float* A,
-                              hipStream_t st);
+                              const GateupExtras& extras, hipStream_t st);
 
-// Down projection of the active experts and the shared expert fused with the weighted
-// combine (GEMV path): out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] +
-// ys[t][n]) with Y[p][n] = W2_e[n] . A[p] and ys[t][n] = Ws2[n] . As[t] kept on chip.
+// Down projection of the active experts fused with the weighted combine (GEMV path):
+// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] + ys[t][n]) with
+// Y[p][n] = W2_e[n] . A[p] kept on chip and ys the shared expert's output.
 size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B);
 hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
-                                    const float* As, const void* w2, const void* ws2,
-                                    const float* h32, const Routing& rt, void* out,
-                                    hipStream_t st);
+                                    const float* ys, const void* w2, const float* h32,
+                                    const Routing& rt, void* out, hipStream_t st);
 // Weighted combine of Y / ys written by the grouped MFMA down-projection.
 hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
                           const Routing& rt, void* out, hipStream_t st);

@@ -1,6 +1,6 @@
 // Router tail shared by both paths: logits (sum of K-slice partials) -> sigmoid scores ->
 // fp64 selection keys -> top-k by wavefront arg-max rounds (DPP) -> renormalised gates ->
-// token->expert permutation and expert offsets by prefix sum.  Runs in one block.
+// token->expert permutation and expert offsets by prefix sum.
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering time
 // between operators" (router scores in MoE preparation).  Reading of the unstated math:
@@ -33,35 +33,23 @@ __device__ __forceinline__ uint64_t rank_key(double key, int e) {
   return (u & ~0x1FFull) | (uint64_t)(511 - e);
 }
 
-// One token's top-k on one wave: logits (partials summed in slice order), sigmoid scores,
-// fp64 keys, k rounds of wave arg-max, renormalised gates; topk_idx / topk_gate rows written
-// in ascending expert order, and the selected experts returned through sel (nullable).
-// part: [splits][B][E] (splits <= kMaxTopkSplits).  All global loads are issued before any
-// is used (addresses clamped instead of branched around, so nothing waits on a join).
-constexpr int kMaxTopkSplits = 8;
-__device__ inline void topk_row(const float* part, int splits, const float* __restrict__ bias,
-                                int B, int E, int k, float routed_scale, int t, const Routing& rt,
-                                int* sel) {
-  constexpr int MAXM = kMaxExperts / 64;
-  constexpr int MAXS = kMaxTopkSplits;
+// One token's selection on one wave from its logits (lane l holds experts l + 64 m in
+// l_[m]): sigmoid scores, fp64 keys, k rounds of wave arg-max, renormalised gates;
+// topk_idx / topk_gate rows written in ascending expert order, and the selected experts
+// returned through sel (nullable).
+constexpr int kMaxM = kMaxExperts / 64;
+__device__ inline void topk_select(const float (&l_)[kMaxM], const float* __restrict__ bias, int E,
+                                   int k, float routed_scale, int t, const Routing& rt, int* sel) {
   const int lane = threadIdx.x & 63;
-  float pv[MAXM][MAXS], bv[MAXM];
+  float bv[kMaxM];
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
-    const int ec = min(lane + 64 * m, E - 1);
-    bv[m] = bias[ec];
+  for (int m = 0; m < kMaxM; ++m) bv[m] = bias[min(lane + 64 * m, E - 1)];
+  double sc[kMaxM];
+  uint64_t rk[kMaxM];
 #pragma unroll
-    for (int s = 0; s < MAXS; ++s) pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
-  }
-  double sc[MAXM];
-  uint64_t rk[MAXM];
-#pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
+  for (int m = 0; m < kMaxM; ++m) {
     const int e = lane + 64 * m;
-    float l = 0.f;
-#pragma unroll
-    for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
-    const double sv = 1.0 / (1.0 + exp(-(double)l));
+    const double sv = 1.0 / (1.0 + exp(-(double)l_[m]));
     sc[m] = sv;
     rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
   }
@@ -70,7 +58,7 @@ __device__ inline void topk_row(const float* part, int splits, const float* __re
   for (int r = 0; r < k; ++r) {
     uint64_t best = 0;
 #pragma unroll
-    for (int m = 0; m < MAXM; ++m)
+    for (int m = 0; m < kMaxM; ++m)
       if (!((selmask >> m) & 1u)) best = max_u64(best, rk[m]);
     best = wave_max_u64(best);
     const int win = 511 - (int)(best & 0x1FFull);
@@ -78,12 +66,12 @@ __device__ inline void topk_row(const float* part, int splits, const float* __re
   }
   double ssum = 0.0;
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m)
+  for (int m = 0; m < kMaxM; ++m)
     if ((selmask >> m) & 1u) ssum += sc[m];
   ssum = wave_sum_f64_dpp(ssum);
   int base = 0;
 #pragma unroll
-  for (int m = 0; m < MAXM; ++m) {
+  for (int m = 0; m < kMaxM; ++m) {
     const bool on = (selmask >> m) & 1u;
     const unsigned long long bal = __ballot(on);
     if (on) {
@@ -95,6 +83,70 @@ __device__ inline void topk_row(const float* part, int splits, const float* __re
     }
     base += __popcll(bal);
   }
+}
+
+// One token's top-k on one wave from logit partials part[splits][B][E] (splits <=
+// kMaxTopkSplits), summed in slice order.  All global loads are issued before any is used
+// (addresses clamped instead of branched around, so nothing waits on a join).
+constexpr int kMaxTopkSplits = 8;
+__device__ inline void topk_row(const float* part, int splits, const float* __restrict__ bias,
+                                int B, int E, int k, float routed_scale, int t, const Routing& rt,
+                                int* sel) {
+  constexpr int MAXS = kMaxTopkSplits;
+  const int lane = threadIdx.x & 63;
+  float pv[kMaxM][MAXS];
+#pragma unroll
+  for (int m = 0; m < kMaxM; ++m) {
+    const int ec = min(lane + 64 * m, E - 1);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
+  }
+  float l_[kMaxM];
+#pragma unroll
+  for (int m = 0; m < kMaxM; ++m) {
+    float l = 0.f;
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
+    l_[m] = l;
+  }
+  topk_select(l_, bias, E, k, routed_scale, t, rt, sel);
+}
+
+// Block-wide: logits lg[t * E + e] of all B tokens summed from part[splits][B][E] in slice
+// order (B * E <= 2 * blockDim.x), each thread's loads all in flight together; DEVICE: read
+// at device scope (partials written by other blocks in the same launch).
+template <bool DEVICE>
+__device__ inline void logits_to_lds(const float* part, int splits, int B, int E, float* lg) {
+  constexpr int MAXS = kMaxTopkSplits;
+  const int n = B * E;
+  float pv[2][MAXS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = min((int)(threadIdx.x + j * blockDim.x), n - 1);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      const float* src = part + (size_t)min(s, splits - 1) * n + i;
+      pv[j][s] = DEVICE ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    float l = 0.f;
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[j][s] : 0.f;
+    if (i < n) lg[i] = l;
+  }
+}
+
+// One token's top-k on one wave from its logits in LDS.
+__device__ inline void topk_row_lds(const float* lg, const float* __restrict__ bias, int E, int k,
+                                    float routed_scale, int t, const Routing& rt, int* sel) {
+  const int lane = threadIdx.x & 63;
+  float l_[kMaxM];
+#pragma unroll
+  for (int m = 0; m < kMaxM; ++m) l_[m] = lg[t * E + min(lane + 64 * m, E - 1)];
+  topk_select(l_, bias, E, k, routed_scale, t, rt, sel);
 }
 
 // Routing tables from the selected experts of all B tokens (sm.sel filled, block-wide):
@@ -143,16 +195,6 @@ __device__ inline void build_tables(int B, int E, int k, const Routing& rt, Topk
     rt.perm[p] = i;
     rt.inv_perm[i] = p;
   }
-}
-
-// Both steps in one block (blockDim.x >= 64): each wave takes tokens wave, wave + nw, ...
-__device__ inline void topk_tables(const float* part, int splits, const float* __restrict__ bias,
-                                   int B, int E, int k, float routed_scale, const Routing& rt,
-                                   TopkScratch& sm) {
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int t = wave; t < B; t += nw) topk_row(part, splits, bias, B, E, k, routed_scale, t, rt, sm.sel);
-  __syncthreads();
-  build_tables(B, E, k, rt, sm);
 }
 
 }  // namespace kk

@@ -64,7 +64,7 @@ def test_plan_is_gemv_and_visible(name, B):
     _, _, L = gpu_layer(name)
     p = L.query_plan(B)
     assert p["path_name"] == "gemv" and p["forced"] == 0
-    assert p["kernels_per_step"] == 5 and p["streams"] == 1
+    assert p["kernels_per_step"] == 4 and p["streams"] == 1
 
 
 @pytest.mark.parametrize("name,B", GEMV_CASES)
