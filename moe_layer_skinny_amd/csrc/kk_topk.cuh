@@ -154,6 +154,22 @@ __device__ inline void topk_row_lds(const float* lg, const float* __restrict__ b
 // (slots by (expert, token)) and its inverse.
 __device__ inline void build_tables(int B, int E, int k, const Routing& rt, TopkScratch& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (B == 1) {
+    // one token: its k experts (ascending, one slot each) are the active list in order, and
+    // positions are slots
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) {
+      int c = 0;
+      for (int j = 0; j < k; ++j) c += sm.sel[j] < e ? 1 : 0;
+      rt.offsets[e] = c;
+    }
+    for (int j = threadIdx.x; j < k; j += blockDim.x) {
+      rt.act[j] = sm.sel[j];
+      rt.perm[j] = j;
+      rt.inv_perm[j] = j;
+    }
+    if (threadIdx.x == 0) *rt.n_act = k;
+    return;
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) sm.mask[e] = 0ull;
   __syncthreads();
   for (int i = threadIdx.x; i < B * k; i += blockDim.x)
