@@ -109,7 +109,9 @@ struct UnitArgs {
 //   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
 //   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
 // GSEL picks the groups a launch covers: 0 all, 1 those with <= 16 tokens, 2 the others.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL>
+// DEPTH stages of loads are kept in flight (registers); a stage past the end reads the
+// activation buffer instead (small and cache-resident), so no load is branched around.
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   constexpr int K8 = KS / 8;
   constexpr int WP = K8 + 1;
@@ -178,17 +180,23 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
       const size_t off = (size_t)src * K + kbase + ch * 8;
       asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
     }
-    u32x4 wreg[WLD], areg[ALD][AW];
-    auto load_stage = [&](int st) {
+    u32x4 wreg[DEPTH][WLD], areg[DEPTH][ALD][AW];
+    const void* dummy = x.act_routed;
+    auto load_stage = [&](int st, int slot) {
+      const bool live = st < nst;
 #pragma unroll
-      for (int i = 0; i < WLD; ++i)
-        wreg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wsrc[i] + st * KS));
+      for (int i = 0; i < WLD; ++i) {
+        const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
+                              : reinterpret_cast<const u32x4*>(dummy);
+        wreg[slot][i] = __builtin_nontemporal_load(p);
+      }
 #pragma unroll
       for (int i = 0; i < ALD; ++i) {
         const u32x4* p = BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
                                  : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
+        if (!live) p = reinterpret_cast<const u32x4*>(dummy);
 #pragma unroll
-        for (int w = 0; w < AW; ++w) areg[i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
+        for (int w = 0; w < AW; ++w) areg[slot][i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
       }
     };
     f32x4 acc[2][TT];
@@ -197,25 +205,25 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_stage(0);
-    for (int st = 0; st < nst; ++st) {
+    auto store_stage = [&](int slot) {
 #pragma unroll
       for (int i = 0; i < WLD; ++i) {
         const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
-        if (q < 32 * K8) lw[rr * WP + ch] = wreg[i];
+        if (q < 32 * K8) lw[rr * WP + ch] = wreg[slot][i];
       }
+      // only the group's own token slots: the others were zeroed at the start of the unit
 #pragma unroll
       for (int i = 0; i < ALD; ++i) {
         const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
-        if (q < NTOK * K8) {
+        if (q < NTOK * K8 && aok[i]) {
           if constexpr (BF16SRC) {
-            la[ch * NTOK + j] = aok[i] ? areg[i][0] : u32x4{0u, 0u, 0u, 0u};
+            la[ch * NTOK + j] = areg[slot][i][0];
           } else {
             float v[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              v[e] = aok[i] ? __uint_as_float(areg[i][0][e]) : 0.f;
-              v[4 + e] = aok[i] ? __uint_as_float(areg[i][1][e]) : 0.f;
+              v[e] = __uint_as_float(areg[slot][i][0][e]);
+              v[4 + e] = __uint_as_float(areg[slot][i][1][e]);
             }
             u32x4 terms[NTERM];
             split_terms<NTERM>(v, terms);
@@ -224,8 +232,11 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
           }
         }
       }
-      __syncthreads();
-      if (st + 1 < nst) load_stage(st + 1);
+    };
+    if (cnt < NTOK)
+      for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
+        if (q % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
+    auto compute_stage = [&]() {
       for (int pr = wave; pr < KSTEPS * ntt; pr += 4) {
         const int ks = pr % KSTEPS, tt = pr / KSTEPS;
         const u32x4 a0 = lw[c * WP + ks * 4 + g];
@@ -244,7 +255,34 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
           }
         }
       }
-      __syncthreads();
+    };
+
+    if constexpr (DEPTH == 1) {
+      load_stage(0, 0);
+      for (int st = 0; st < nst; ++st) {
+        store_stage(0);
+        __syncthreads();
+        if (st + 1 < nst) load_stage(st + 1, 0);
+        compute_stage();
+        __syncthreads();
+      }
+    } else {
+      load_stage(0, 0);
+      load_stage(1, 1);
+      for (int st = 0; st < nst; st += 2) {
+        store_stage(0);
+        __syncthreads();
+        load_stage(st + 2, 0);
+        compute_stage();
+        __syncthreads();
+        if (st + 1 < nst) {
+          store_stage(1);
+          __syncthreads();
+          load_stage(st + 3, 1);
+          compute_stage();
+          __syncthreads();
+        }
+      }
     }
     // sum the four waves' partial tiles in wave order, then the epilogue
     f32x4* red = reinterpret_cast<f32x4*>(lds);
@@ -298,9 +336,9 @@ void allow_lds_mfma(Kern kernel) {
 
 inline int token_tiles(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0, int DEPTH = 1>
 hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
-  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL>;
+  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL, DEPTH>;
   constexpr size_t lds_main = (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
   constexpr size_t lds_red = (size_t)4 * 2 * TT * 64 * 16;
   constexpr size_t lds = lds_main > lds_red ? lds_main : lds_red;
