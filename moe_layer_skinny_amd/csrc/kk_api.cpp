@@ -199,9 +199,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                 B);
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
-  // oproj, reduce, router logits, top-k rows, tables, gate/up, down, combine; B > 16 adds
-  // a second gate/up and down launch for groups of more than 16 tokens
-  p->kernels_per_step = B > 16 ? 10 : 8;
+  // oproj, reduce, router logits, top-k rows, tables, gate/up, down, combine; B > 32 adds
+  // a second gate/up launch for groups of more than 16 tokens
+  p->kernels_per_step = B > 32 ? 9 : 8;
   return KK_OK;
 }
 

@@ -109,10 +109,14 @@ struct UnitArgs {
 //   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
 //   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
 // GSEL picks the groups a launch covers: 0 all, 1 those with <= 16 tokens, 2 the others.
-// DEPTH stages of loads are kept in flight (registers); a stage past the end reads the
-// activation buffer instead (small and cache-resident), so no load is branched around.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
-__global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
+// One unit of the LDS-staged product: the tile pair `tile` of group (wbase, positions p0 ..
+// p0 + cnt - 1, `shared`) over K chunk `chunk`.  DEPTH stages of loads are kept in flight
+// (registers); a stage past the end reads the activation buffer instead (small and cache-
+// resident), so no load is branched around.
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int DEPTH>
+__device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
+                                            int p0, int cnt, const uint16_t* wbase,
+                                            bool shared) {
   constexpr int K8 = KS / 8;
   constexpr int WP = K8 + 1;
   constexpr int NTOK = 16 * TT;
@@ -121,204 +125,256 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   constexpr int ALD = (NTOK * K8 + 255) / 256;  // activation chunks (8 values) per thread
   constexpr int KSTEPS = KS / 32;
   constexpr int AW = BF16SRC ? 1 : 2;           // 16-byte words per activation chunk
-  extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
   u32x4* lw = lds;
   u32x4* la = lds + W_CH;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
   const int K = MODE == 0 ? x.H : (MODE == 1 ? x.I : x.K);
+  const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
+  const int chunks = MODE == 2 ? x.chunks : 1;
+  const int kchunk = K / chunks;
+  const int nst = kchunk / KS;
+  const int ntt = (cnt + 15) / 16;
+  const int row0 = MODE == 0 ? tile * 16 : tile * 32;
+  const int kbase = chunk * kchunk;
+  // this thread's weight chunks: q = tid + 256 i -> (row q / K8, chunk q % K8)
+  const uint16_t* wsrc[WLD];
+#pragma unroll
+  for (int i = 0; i < WLD; ++i) {
+    const int q = min(tid + 256 * i, 32 * K8 - 1), rr = q / K8, ch = q - rr * K8;
+    const int wr = MODE == 0 ? (rr < 16 ? row0 + rr : x.I + row0 + rr - 16) : row0 + rr;
+    wsrc[i] = wbase + (size_t)wr * K + kbase + ch * 8;
+  }
+  // this thread's activation chunks: q = tid + 256 i -> (token slot q / K8, chunk q % K8)
+  const void* asrc[ALD];
+  bool aok[ALD];
+#pragma unroll
+  for (int i = 0; i < ALD; ++i) {
+    const int q = min(tid + 256 * i, NTOK * K8 - 1), j = q / K8, ch = q - j * K8;
+    aok[i] = j < cnt;
+    const int jj = aok[i] ? j : 0;
+    int src;
+    if (MODE == 0)
+      src = shared ? jj : x.rt.perm[p0 + jj] / x.k;
+    else if (MODE == 1)
+      src = shared ? jj : p0 + jj;
+    else
+      src = jj;
+    const void* base = (MODE == 1 && shared) ? (const void*)x.act_shared : x.act_routed;
+    const size_t off = (size_t)src * K + kbase + ch * 8;
+    asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
+  }
+  u32x4 wreg[DEPTH][WLD], areg[DEPTH][ALD][AW];
+  const void* dummy = x.act_routed;
+  auto load_stage = [&](int st, int slot) {
+    const bool live = st < nst;
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
+                            : reinterpret_cast<const u32x4*>(dummy);
+      wreg[slot][i] = __builtin_nontemporal_load(p);
+    }
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      const u32x4* p = BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
+                               : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
+      if (!live) p = reinterpret_cast<const u32x4*>(dummy);
+#pragma unroll
+      for (int w = 0; w < AW; ++w) areg[slot][i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  f32x4 acc[2][TT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto store_stage = [&](int slot) {
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+      if (q < 32 * K8) lw[rr * WP + ch] = wreg[slot][i];
+    }
+    // only the group's own token slots: the others were zeroed at the start of the unit
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
+      if (q < NTOK * K8 && aok[i]) {
+        if constexpr (BF16SRC) {
+          la[ch * NTOK + j] = areg[slot][i][0];
+        } else {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = __uint_as_float(areg[slot][i][0][e]);
+            v[4 + e] = __uint_as_float(areg[slot][i][1][e]);
+          }
+          u32x4 terms[NTERM];
+          split_terms<NTERM>(v, terms);
+#pragma unroll
+          for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
+        }
+      }
+    }
+  };
+  if (cnt < NTOK)
+    for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
+      if (q % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
+  auto compute_stage = [&]() {
+    for (int pr = wave; pr < KSTEPS * ntt; pr += 4) {
+      const int ks = pr % KSTEPS, tt = pr / KSTEPS;
+      const u32x4 a0 = lw[c * WP + ks * 4 + g];
+      const u32x4 a1 = lw[(16 + c) * WP + ks * 4 + g];
+      u32x4 bq[NTERM];
+#pragma unroll
+      for (int q2 = 0; q2 < NTERM; ++q2) bq[q2] = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
+#pragma unroll
+      for (int t2 = 0; t2 < TT; ++t2) {
+        if (t2 == tt) {
+#pragma unroll
+          for (int q2 = 0; q2 < NTERM; ++q2) {
+            acc[0][t2] = mfma(a0, bq[q2], acc[0][t2]);
+            acc[1][t2] = mfma(a1, bq[q2], acc[1][t2]);
+          }
+        }
+      }
+    }
+  };
+
+  if constexpr (DEPTH == 1) {
+    load_stage(0, 0);
+    for (int st = 0; st < nst; ++st) {
+      store_stage(0);
+      __syncthreads();
+      if (st + 1 < nst) load_stage(st + 1, 0);
+      compute_stage();
+      __syncthreads();
+    }
+  } else {
+    load_stage(0, 0);
+    load_stage(1, 1);
+    for (int st = 0; st < nst; st += 2) {
+      store_stage(0);
+      __syncthreads();
+      load_stage(st + 2, 0);
+      compute_stage();
+      __syncthreads();
+      if (st + 1 < nst) {
+        store_stage(1);
+        __syncthreads();
+        load_stage(st + 3, 1);
+        compute_stage();
+        __syncthreads();
+      }
+    }
+  }
+  // sum the four waves' partial tiles in wave order, then the epilogue
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) red[((wave * 2 + r) * TT + tt) * 64 + lane] = acc[r][tt];
+  __syncthreads();
+  float* outp = shared ? x.out_shared : x.out_routed;
+  for (int idx = tid; idx < TT * 64; idx += 256) {
+    const int tt = idx >> 6, ln = idx & 63;
+    const int j = tt * 16 + (ln & 15), gg = ln >> 4;
+    if (tt < ntt && j < cnt) {
+      f32x4 s0 = red[((0 * 2 + 0) * TT + tt) * 64 + ln];
+      f32x4 s1 = red[((0 * 2 + 1) * TT + tt) * 64 + ln];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        s0 += red[((w * 2 + 0) * TT + tt) * 64 + ln];
+        s1 += red[((w * 2 + 1) * TT + tt) * 64 + ln];
+      }
+      float* o;
+      if (MODE == 2)
+        o = outp + ((size_t)chunk * x.B + j) * out_rows + row0 + 4 * gg;
+      else
+        o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
+      if (MODE == 0) {
+        *reinterpret_cast<float4*>(o) =
+            float4{silu_f32(s0[0]) * s1[0], silu_f32(s0[1]) * s1[1], silu_f32(s0[2]) * s1[2],
+                   silu_f32(s0[3]) * s1[3]};
+      } else {
+        *reinterpret_cast<float4*>(o) = float4{s0[0], s0[1], s0[2], s0[3]};
+        *reinterpret_cast<float4*>(o + 16) = float4{s1[0], s1[1], s1[2], s1[3]};
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// LDS bytes of one block of staged_unit<.., TT, KS, NTERM, ..>.
+constexpr size_t staged_lds(int TT, int KS, int NTERM) {
+  return (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16 > (size_t)4 * 2 * TT * 64 * 16
+             ? (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16
+             : (size_t)4 * 2 * TT * 64 * 16;
+}
+
+// Group a of a launch: its weights, positions and token count.
+struct Group {
+  const uint16_t* wbase;
+  int p0, cnt;
+  bool shared;
+};
+template <int MODE>
+__device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups) {
+  Group gr{x.w_routed, 0, x.B, false};
+  if (MODE == 2) return gr;
+  const size_t wstride = MODE == 0 ? (size_t)2 * x.I * x.H : (size_t)x.H * x.I;
+  gr.shared = a == n_groups - 1;
+  if (gr.shared) {
+    gr.wbase = x.w_shared;
+  } else {
+    const int e = x.rt.act[a];
+    gr.p0 = x.rt.offsets[e];
+    gr.cnt = x.rt.offsets[e + 1] - gr.p0;
+    gr.wbase = x.w_routed + (size_t)e * wstride;
+  }
+  return gr;
+}
+
+// All MFMA launches of one token-tile width: units (group, tile pair, K chunk) over a
+// persistent grid.  GSEL picks the groups a launch covers: 0 all, 1 those with <= 16
+// tokens, 2 the others.
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
+__global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
+  extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
+  const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
   const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
   const int tiles = MODE == 0 ? x.I / 16 : out_rows / 32;
   const int chunks = MODE == 2 ? x.chunks : 1;
-  const size_t wstride = MODE == 0 ? (size_t)2 * x.I * x.H : (size_t)x.H * x.I;
   const int units = n_groups * tiles * chunks;
-  const int kchunk = K / chunks;
-  const int nst = kchunk / KS;
-
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int a = unit / (tiles * chunks);
     const int rem = unit - a * tiles * chunks;
     const int tile = rem / chunks, chunk = rem - tile * chunks;
-    const bool shared = MODE != 2 && a == n_groups - 1;
-    int p0 = 0, cnt = x.B;
-    const uint16_t* wbase = shared ? x.w_shared : x.w_routed;
-    if (MODE != 2 && !shared) {
-      const int e = x.rt.act[a];
-      p0 = x.rt.offsets[e];
-      cnt = x.rt.offsets[e + 1] - p0;
-      wbase = x.w_routed + (size_t)e * wstride;
-    }
-    if ((GSEL == 1 && cnt > 16) || (GSEL == 2 && cnt <= 16)) continue;  // block-uniform
-    const int ntt = (cnt + 15) / 16;
-    const int row0 = MODE == 0 ? tile * 16 : tile * 32;
-    const int kbase = chunk * kchunk;
-    // this thread's weight chunks: q = tid + 256 i -> (row q / K8, chunk q % K8)
-    const uint16_t* wsrc[WLD];
-#pragma unroll
-    for (int i = 0; i < WLD; ++i) {
-      const int q = min(tid + 256 * i, 32 * K8 - 1), rr = q / K8, ch = q - rr * K8;
-      const int wr = MODE == 0 ? (rr < 16 ? row0 + rr : x.I + row0 + rr - 16) : row0 + rr;
-      wsrc[i] = wbase + (size_t)wr * K + kbase + ch * 8;
-    }
-    // this thread's activation chunks: q = tid + 256 i -> (token slot q / K8, chunk q % K8)
-    const void* asrc[ALD];
-    bool aok[ALD];
-#pragma unroll
-    for (int i = 0; i < ALD; ++i) {
-      const int q = min(tid + 256 * i, NTOK * K8 - 1), j = q / K8, ch = q - j * K8;
-      aok[i] = j < cnt;
-      const int jj = aok[i] ? j : 0;
-      int src;
-      if (MODE == 0)
-        src = shared ? jj : x.rt.perm[p0 + jj] / x.k;
-      else if (MODE == 1)
-        src = shared ? jj : p0 + jj;
-      else
-        src = jj;
-      const void* base = (MODE == 1 && shared) ? (const void*)x.act_shared : x.act_routed;
-      const size_t off = (size_t)src * K + kbase + ch * 8;
-      asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
-    }
-    u32x4 wreg[DEPTH][WLD], areg[DEPTH][ALD][AW];
-    const void* dummy = x.act_routed;
-    auto load_stage = [&](int st, int slot) {
-      const bool live = st < nst;
-#pragma unroll
-      for (int i = 0; i < WLD; ++i) {
-        const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
-                              : reinterpret_cast<const u32x4*>(dummy);
-        wreg[slot][i] = __builtin_nontemporal_load(p);
-      }
-#pragma unroll
-      for (int i = 0; i < ALD; ++i) {
-        const u32x4* p = BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
-                                 : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
-        if (!live) p = reinterpret_cast<const u32x4*>(dummy);
-#pragma unroll
-        for (int w = 0; w < AW; ++w) areg[slot][i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    f32x4 acc[2][TT];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const Group gr = group_of<MODE>(x, a, n_groups);
+    if ((GSEL == 1 && gr.cnt > 16) || (GSEL == 2 && gr.cnt <= 16)) continue;  // block-uniform
+    staged_unit<MODE, TT, KS, NTERM, BF16SRC, DEPTH>(x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
+                                                    gr.shared);
+  }
+}
 
-    auto store_stage = [&](int slot) {
-#pragma unroll
-      for (int i = 0; i < WLD; ++i) {
-        const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
-        if (q < 32 * K8) lw[rr * WP + ch] = wreg[slot][i];
-      }
-      // only the group's own token slots: the others were zeroed at the start of the unit
-#pragma unroll
-      for (int i = 0; i < ALD; ++i) {
-        const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
-        if (q < NTOK * K8 && aok[i]) {
-          if constexpr (BF16SRC) {
-            la[ch * NTOK + j] = areg[slot][i][0];
-          } else {
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] = __uint_as_float(areg[slot][i][0][e]);
-              v[4 + e] = __uint_as_float(areg[slot][i][1][e]);
-            }
-            u32x4 terms[NTERM];
-            split_terms<NTERM>(v, terms);
-#pragma unroll
-            for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
-          }
-        }
-      }
-    };
-    if (cnt < NTOK)
-      for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
-        if (q % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
-    auto compute_stage = [&]() {
-      for (int pr = wave; pr < KSTEPS * ntt; pr += 4) {
-        const int ks = pr % KSTEPS, tt = pr / KSTEPS;
-        const u32x4 a0 = lw[c * WP + ks * 4 + g];
-        const u32x4 a1 = lw[(16 + c) * WP + ks * 4 + g];
-        u32x4 bq[NTERM];
-#pragma unroll
-        for (int q2 = 0; q2 < NTERM; ++q2) bq[q2] = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
-#pragma unroll
-        for (int t2 = 0; t2 < TT; ++t2) {
-          if (t2 == tt) {
-#pragma unroll
-            for (int q2 = 0; q2 < NTERM; ++q2) {
-              acc[0][t2] = mfma(a0, bq[q2], acc[0][t2]);
-              acc[1][t2] = mfma(a1, bq[q2], acc[1][t2]);
-            }
-          }
-        }
-      }
-    };
-
-    if constexpr (DEPTH == 1) {
-      load_stage(0, 0);
-      for (int st = 0; st < nst; ++st) {
-        store_stage(0);
-        __syncthreads();
-        if (st + 1 < nst) load_stage(st + 1, 0);
-        compute_stage();
-        __syncthreads();
-      }
-    } else {
-      load_stage(0, 0);
-      load_stage(1, 1);
-      for (int st = 0; st < nst; st += 2) {
-        store_stage(0);
-        __syncthreads();
-        load_stage(st + 2, 0);
-        compute_stage();
-        __syncthreads();
-        if (st + 1 < nst) {
-          store_stage(1);
-          __syncthreads();
-          load_stage(st + 3, 1);
-          compute_stage();
-          __syncthreads();
-        }
-      }
-    }
-    // sum the four waves' partial tiles in wave order, then the epilogue
-    f32x4* red = reinterpret_cast<f32x4*>(lds);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) red[((wave * 2 + r) * TT + tt) * 64 + lane] = acc[r][tt];
-    __syncthreads();
-    float* outp = shared ? x.out_shared : x.out_routed;
-    for (int idx = tid; idx < TT * 64; idx += 256) {
-      const int tt = idx >> 6, ln = idx & 63;
-      const int j = tt * 16 + (ln & 15), gg = ln >> 4;
-      if (tt < ntt && j < cnt) {
-        f32x4 s0 = red[((0 * 2 + 0) * TT + tt) * 64 + ln];
-        f32x4 s1 = red[((0 * 2 + 1) * TT + tt) * 64 + ln];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          s0 += red[((w * 2 + 0) * TT + tt) * 64 + ln];
-          s1 += red[((w * 2 + 1) * TT + tt) * 64 + ln];
-        }
-        float* o;
-        if (MODE == 2)
-          o = outp + ((size_t)chunk * x.B + j) * out_rows + row0 + 4 * gg;
-        else
-          o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
-        if (MODE == 0) {
-          *reinterpret_cast<float4*>(o) =
-              float4{silu_f32(s0[0]) * s1[0], silu_f32(s0[1]) * s1[1], silu_f32(s0[2]) * s1[2],
-                     silu_f32(s0[3]) * s1[3]};
-        } else {
-          *reinterpret_cast<float4*>(o) = float4{s0[0], s0[1], s0[2], s0[3]};
-          *reinterpret_cast<float4*>(o + 16) = float4{s1[0], s1[1], s1[2], s1[3]};
-        }
-      }
-    }
-    __syncthreads();
+// Grouped launch (gate/up or down) for batches over 16 tokens: groups of more than 16 tokens
+// (the shared expert, and any routed expert that hot) use TTB-wide token tiles, the rest one
+// tile, in the same launch; the groups are walked from the last (the shared expert) down, so
+// its long units start first and overlap the routed ones.
+template <int MODE, int TTB, int KSB, int KS1>
+__global__ __launch_bounds__(256) void mfma_grouped_kernel(UnitArgs x) {
+  extern __shared__ u32x4 lds[];
+  const int n_groups = *x.rt.n_act + 1;
+  const int tiles = MODE == 0 ? x.I / 16 : x.H / 32;
+  const int units = n_groups * tiles;
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int a = n_groups - 1 - unit / tiles;
+    const int tile = unit - (n_groups - 1 - a) * tiles;
+    const Group gr = group_of<MODE>(x, a, n_groups);
+    if (gr.cnt > 16)
+      staged_unit<MODE, TTB, KSB, 2, false, 1>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
+    else
+      staged_unit<MODE, 1, KS1, 2, false, 1>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
   }
 }
 
@@ -336,23 +392,36 @@ void allow_lds_mfma(Kern kernel) {
 
 inline int token_tiles(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
 
+// Persistent grid: as many blocks as are resident at once (registers and LDS permitting).
+template <typename Kern>
+int resident_grid(const Device& d, Kern kern, size_t lds, int max_units, int* cache) {
+  if (*cache == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, lds) != hipSuccess || n < 1) n = 1;
+    *cache = n;
+  }
+  const int grid = d.num_cu * *cache;
+  return grid > max_units ? max_units : grid;
+}
+
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0, int DEPTH = 1>
 hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
   auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL, DEPTH>;
-  constexpr size_t lds_main = (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
-  constexpr size_t lds_red = (size_t)4 * 2 * TT * 64 * 16;
-  constexpr size_t lds = lds_main > lds_red ? lds_main : lds_red;
+  constexpr size_t lds = staged_lds(TT, KS, NTERM);
   if (lds > 64 * 1024) allow_lds_mfma(kern);
-  // persistent grid: as many blocks as are resident at once (registers and LDS permitting)
   static thread_local int bpc = 0;
-  if (bpc == 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 256, lds) != hipSuccess || n < 1) n = 1;
-    bpc = n;
-  }
-  int grid = d.num_cu * bpc;
-  if (grid > max_units) grid = max_units;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, x);
+  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, max_units, &bpc)), dim3(256), lds, st, x);
+  return hipGetLastError();
+}
+
+template <int MODE, int TTB, int KSB, int KS1>
+hipError_t grouped_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
+  auto kern = mfma_grouped_kernel<MODE, TTB, KSB, KS1>;
+  constexpr size_t lds = staged_lds(TTB, KSB, 2) > staged_lds(1, KS1, 2) ? staged_lds(TTB, KSB, 2)
+                                                                          : staged_lds(1, KS1, 2);
+  if (lds > 64 * 1024) allow_lds_mfma(kern);
+  static thread_local int bpc = 0;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, max_units, &bpc)), dim3(256), lds, st, x);
   return hipGetLastError();
 }
 
@@ -368,16 +437,19 @@ hipError_t staged_dispatch(const Device& d, const UnitArgs& x, int max_units, hi
   }
 }
 
-// Grouped launches: groups of up to 16 tokens (nearly all routed experts) go through the
-// one-tile kernel with 256-k stages; when B > 16 a second launch covers the shared expert
-// and any routed expert with more than 16 tokens.
+// Grouped launches: up to 16 tokens, every group goes through the one-tile kernel with
+// 256-k stages.  Beyond, one launch mixes one-tile units with wider ones for the groups of
+// more than 16 tokens (the shared expert and any routed expert that hot) -- except the
+// gate/up over more than 32 tokens, where the four-tile path would lower the occupancy of
+// the whole launch: there the wide groups get a launch of their own.
 template <int MODE, int KMAX = 256>
 hipError_t grouped_dispatch(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
   constexpr int K1 = KMAX < 256 ? KMAX : 256, K4 = KMAX < 128 ? KMAX : 128;
   if (x.B <= 16) return staged_t<MODE, 1, K1, 2, false, 0>(d, x, max_units, st);
+  if (x.B <= 32) return grouped_t<MODE, 2, K1, K1>(d, x, max_units, st);
+  if (MODE == 1) return grouped_t<MODE, 4, K4, K1>(d, x, max_units, st);
   hipError_t e = staged_t<MODE, 1, K1, 2, false, 1>(d, x, max_units, st);
   if (e != hipSuccess) return e;
-  if (x.B <= 32) return staged_t<MODE, 2, K1, 2, false, 2>(d, x, max_units, st);
   return staged_t<MODE, 4, K4, 2, false, 2>(d, x, max_units, st);
 }
 
