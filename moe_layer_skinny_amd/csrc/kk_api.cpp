@@ -50,6 +50,11 @@ struct Layout {
       oproj_part, total;
 };
 
+kk::Shape to_shape(const kk_config& c) {
+  return kk::Shape{c.hidden, c.oproj_in, c.n_experts, c.top_k, c.inter, c.shared_inter, c.dtype,
+                   c.routed_scale};
+}
+
 Layout make_layout(const kk_config& c, int Bm) {
   Layout L{};
   size_t o = 0;
@@ -72,15 +77,14 @@ Layout make_layout(const kk_config& c, int Bm) {
   L.As = take((size_t)Bm * c.shared_inter * 4);
   L.Y = take(slots * c.hidden * 4);
   L.ys = take((size_t)Bm * c.hidden * 4);
-  L.oproj_part = take((size_t)kMaxOprojSplits * Bm * c.hidden * 4);
+  // o-proj partials of the split-K path; reused afterwards by the shared expert's split-K
+  // gate/up partials
+  L.oproj_part = take(std::max((size_t)kMaxOprojSplits * Bm * c.hidden,
+                               kk::mfma_scratch_floats(to_shape(c), Bm)) * 4);
   L.total = o;
   return L;
 }
 
-kk::Shape to_shape(const kk_config& c) {
-  return kk::Shape{c.hidden, c.oproj_in, c.n_experts, c.top_k, c.inter, c.shared_inter, c.dtype,
-                   c.routed_scale};
-}
 
 bool misaligned(const void* p, size_t a = 16) { return ((uintptr_t)p) % a != 0; }
 
@@ -200,8 +204,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
   // oproj, reduce, router logits, top-k rows, tables, gate/up, down, combine; B > 32 adds
-  // a second gate/up launch for groups of more than 16 tokens
-  p->kernels_per_step = B > 32 ? 9 : 8;
+  // the shared expert's split-K gate/up and its SwiGLU, and a launch for routed groups of
+  // more than 16 tokens
+  p->kernels_per_step = B > 32 ? 11 : 8;
   return KK_OK;
 }
 
@@ -329,8 +334,9 @@ kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* h32, const kk::Rou
                                const WsPtrs& p, void* out, hipStream_t s) {
   KK_HIP(timed(c, K_GU_MFMA, s,
                [&] {
+                 // (the o-proj partials are consumed by now: their region is scratch)
                  return kk::launch_gateup_mfma(c->shape, c->dev, B, h32, c->w.w13, c->w.ws13, rt,
-                                               p.A, p.As, s);
+                                               p.A, p.As, p.oproj_part, s);
                }),
          "gate/up launch");
   KK_HIP(timed(c, K_DOWN_MFMA, s,

@@ -105,10 +105,13 @@ hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const v
 // Router logit partials from h32 (three bf16 terms per fp32 value).
 hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w_r, float* part, hipStream_t st);
-// Grouped gate/up (routed experts and the shared expert) -> A, As.
+// Grouped gate/up (routed experts and the shared expert) -> A, As.  Over 32 tokens the
+// shared expert's gate/up is split over K; its partials use `scratch`
+// (mfma_scratch_floats floats).
+size_t mfma_scratch_floats(const Shape& s, int B);
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
-                              float* As, hipStream_t st);
+                              float* As, float* scratch, hipStream_t st);
 // Grouped down-projection -> Y (per position), ys (shared).
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,

@@ -29,6 +29,9 @@
 namespace kk {
 namespace {
 
+// K chunks of the shared expert's split-K gate/up over more than 32 tokens.
+constexpr int kSharedSplits = 7;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -76,6 +79,32 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restri
   const float hv = Elem<T>::load(r, i) + acc;
   h32[i] = hv;
   if (h_out) Elem<T>::store(h_out, i, hv);
+}
+
+// As[t][i] = silu(sum_c P[c][t][i]) * sum_c P[c][t][Is + i] over `chunks` K-chunk partials of
+// the shared expert's gate/up rows (fixed chunk order).
+template <int MAXC>
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part,
+                                                            int chunks, int B, int Is,
+                                                            float* __restrict__ As) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= B * Is) return;
+  const int t = i / Is, n = i - t * Is;
+  const size_t cs = (size_t)B * 2 * Is;
+  float g[MAXC], u[MAXC];
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    const size_t o = (size_t)min(c, chunks - 1) * cs + (size_t)t * 2 * Is + n;
+    g[c] = part[o];
+    u[c] = part[o + Is];
+  }
+  float zg = 0.f, zu = 0.f;
+#pragma unroll
+  for (int c = 0; c < MAXC; ++c) {
+    zg += c < chunks ? g[c] : 0.f;
+    zu += c < chunks ? u[c] : 0.f;
+  }
+  As[i] = silu_f32(zg) * zu;
 }
 
 // Arguments of the grouped / split-K launches.
@@ -337,7 +366,7 @@ __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups
 
 // All MFMA launches of one token-tile width: units (group, tile pair, K chunk) over a
 // persistent grid.  GSEL picks the groups a launch covers: 0 all, 1 those with <= 16
-// tokens, 2 the others.
+// tokens, 2 the others, 3 the routed ones with more than 16 tokens.
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
@@ -351,7 +380,9 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
     const int rem = unit - a * tiles * chunks;
     const int tile = rem / chunks, chunk = rem - tile * chunks;
     const Group gr = group_of<MODE>(x, a, n_groups);
-    if ((GSEL == 1 && gr.cnt > 16) || (GSEL == 2 && gr.cnt <= 16)) continue;  // block-uniform
+    if ((GSEL == 1 && gr.cnt > 16) || (GSEL == 2 && gr.cnt <= 16) ||
+        (GSEL == 3 && (gr.cnt <= 16 || gr.shared)))
+      continue;  // block-uniform
     staged_unit<MODE, TT, KS, NTERM, BF16SRC, DEPTH>(x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
                                                     gr.shared);
   }
@@ -439,18 +470,13 @@ hipError_t staged_dispatch(const Device& d, const UnitArgs& x, int max_units, hi
 
 // Grouped launches: up to 16 tokens, every group goes through the one-tile kernel with
 // 256-k stages.  Beyond, one launch mixes one-tile units with wider ones for the groups of
-// more than 16 tokens (the shared expert and any routed expert that hot) -- except the
-// gate/up over more than 32 tokens, where the four-tile path would lower the occupancy of
-// the whole launch: there the wide groups get a launch of their own.
+// more than 16 tokens (the shared expert and any routed expert that hot).
 template <int MODE, int KMAX = 256>
 hipError_t grouped_dispatch(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
   constexpr int K1 = KMAX < 256 ? KMAX : 256, K4 = KMAX < 128 ? KMAX : 128;
   if (x.B <= 16) return staged_t<MODE, 1, K1, 2, false, 0>(d, x, max_units, st);
   if (x.B <= 32) return grouped_t<MODE, 2, K1, K1>(d, x, max_units, st);
-  if (MODE == 1) return grouped_t<MODE, 4, K4, K1>(d, x, max_units, st);
-  hipError_t e = staged_t<MODE, 1, K1, 2, false, 1>(d, x, max_units, st);
-  if (e != hipSuccess) return e;
-  return staged_t<MODE, 4, K4, 2, false, 2>(d, x, max_units, st);
+  return grouped_t<MODE, 4, K4, K1>(d, x, max_units, st);
 }
 
 }  // namespace
@@ -464,6 +490,7 @@ bool mfma_supported(const Shape& s, int B) {
 
 // K chunks of the split-K launches (the partials the reduce / top-k launches sum).
 int mfma_oproj_splits(const Shape& s) { return s.Ko == 7168 ? 7 : 1; }
+size_t mfma_scratch_floats(const Shape& s, int B) { return (size_t)kSharedSplits * B * 2 * s.Is; }
 int mfma_router_splits(const Shape& s) { return 7; }
 
 hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x,
@@ -505,7 +532,7 @@ hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const floa
 
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
-                              float* As, hipStream_t st) {
+                              float* As, float* scratch, hipStream_t st) {
   UnitArgs a{};
   a.w_routed = (const uint16_t*)w13;
   a.w_shared = (const uint16_t*)ws13;
@@ -519,7 +546,25 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   a.B = B;
   a.rt = rt;
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.I / 16);
-  return grouped_dispatch<0>(d, a, max_units, st);
+  if (B <= 32) return grouped_dispatch<0>(d, a, max_units, st);
+  // over 32 tokens the shared expert's gate/up is a split-K product of its own (its group
+  // alone has too few row tiles to fill the chip), summed by the SwiGLU launch
+  UnitArgs sh{};
+  sh.w_routed = (const uint16_t*)ws13;
+  sh.act_routed = h32;
+  sh.out_routed = scratch;
+  sh.B = B;
+  sh.N = 2 * s.Is;
+  sh.K = s.H;
+  sh.chunks = kSharedSplits;
+  hipError_t e = staged_dispatch<2, 2, false>(d, sh, (sh.N / 32) * sh.chunks, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((swiglu_reduce_kernel<kSharedSplits>), dim3((B * s.Is + 255) / 256), dim3(256),
+                     0, st, scratch, kSharedSplits, B, s.Is, As);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = staged_t<0, 1, 256, 2, false, 1>(d, a, max_units, st);
+  if (e != hipSuccess) return e;
+  return staged_t<0, 4, 128, 2, false, 3>(d, a, max_units, st);
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
