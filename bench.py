@@ -121,8 +121,9 @@ def time_steps(layer, B, x, r, out, idx, gate, ws, s, flush, steps, warmup):
 
 
 def sweep(main_cfg, main_w, args, s, flush) -> dict:
-    """The other workloads: batch 8 / 64 of the full-size layer on the same resident weights
-    (only the router bias differs), and one TP rank's share at batch 1, 2, 8, 64."""
+    """The other workloads: batch 8 / 64 of the full-size layer and an 8-token speculative-
+    verify batch (correlated tokens of one sequence) on the same resident weights (only the
+    router bias differs), and one TP rank's share at batch 1, 2, 8, 64."""
     import torch
 
     import synth
@@ -130,7 +131,7 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
     from moe_layer_skinny_amd import kk
 
     out = {}
-    plan = [("full_b8", 8), ("full_b64", 64)] + [("tp_rank", b) for b in (1, 2, 8, 64)]
+    plan = [("full_b8", 8), ("full_b64", 64), ("verify_b8", 8)] + [("tp_rank", b) for b in (1, 2, 8, 64)]
     weights = {}
     for name, B in plan:
         cfg = synth.CONFIGS[name]

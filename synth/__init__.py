@@ -40,6 +40,11 @@ T_WO, T_WR, T_BIAS, T_W13, T_W2, T_WS13, T_WS2, T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 # Token streams: key0 = token seed, key1 = TOKEN_BASE + 16 * attempt + kind.
 TOKEN_BASE = 0x100
 KIND_X, KIND_R = 0, 1
+# Speculative-verify tokens (one sequence): a component shared by all tokens, stream
+# (VERIFY_SEED, TOKEN_BASE + kind), mixed with each token's own stream as
+# sqrt(VERIFY_RHO) * shared + sqrt(1 - VERIFY_RHO) * own.
+VERIFY_SEED = 0x5EED
+VERIFY_RHO = 0.9
 
 WEIGHT_SIGMA = 0.02
 ACT_SIGMA = 1.0
@@ -69,6 +74,7 @@ class LayerConfig:
     gap_space: str  # "key" | "logit"
     layer_seed: int = 0
     description: str = ""
+    tokens: str = "independent"  # "independent" | "verify" (correlated tokens of one sequence)
 
     @property
     def wbytes(self) -> int:
@@ -92,6 +98,10 @@ CONFIGS = {
                     description="full-size layer, batch 64, uniform router bias"),
         LayerConfig("tp_rank", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8, 64), "zipf", "key",
                     description="one TP16 rank's share, Zipf(1.2) router bias, batch sweep"),
+        LayerConfig("verify_b8", 7168, 7168, 384, 8, 2048, 2048, "bf16", (8,), "normal", "key",
+                    description="full-size layer, speculative-verify batch: 8 correlated tokens "
+                                "of one sequence (shared component, rho 0.9)",
+                    tokens="verify"),
     ]
 }
 
@@ -225,11 +235,36 @@ def token_key(attempt: int, kind: int) -> int:
     return TOKEN_BASE + 16 * int(attempt) + kind
 
 
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return np.where(nan, ((u >> 16) | 0x40).astype(np.uint16), r)
+
+
 def host_token(cfg: LayerConfig, t: int, attempt: int):
-    """(x_t [Ko], r_t [H]) for token seed t, resample attempt `attempt`."""
-    x = host_stream(cfg.oproj_in, t, token_key(attempt, KIND_X), ACT_SIGMA, cfg.dtype)
-    r = host_stream(cfg.hidden, t, token_key(attempt, KIND_R), ACT_SIGMA, cfg.dtype)
-    return x, r
+    """(x_t [Ko], r_t [H]) for token seed t, resample attempt `attempt`.
+
+    Independent tokens draw each vector from the token's own stream.  Verify tokens mix a
+    component shared by the whole batch with the token's own stream (fp32 draws, mixed in
+    fp64, rounded to fp32 and then to the config dtype); a resample redraws only the token's
+    own part.
+    """
+    if cfg.tokens == "independent":
+        x = host_stream(cfg.oproj_in, t, token_key(attempt, KIND_X), ACT_SIGMA, cfg.dtype)
+        r = host_stream(cfg.hidden, t, token_key(attempt, KIND_R), ACT_SIGMA, cfg.dtype)
+        return x, r
+    if cfg.tokens != "verify":
+        raise ValueError(cfg.tokens)
+    out = []
+    for n, kind in ((cfg.oproj_in, KIND_X), (cfg.hidden, KIND_R)):
+        shared = host_stream(n, VERIFY_SEED, token_key(0, kind), ACT_SIGMA, "f32")
+        own = host_stream(n, t, token_key(attempt, kind), ACT_SIGMA, "f32")
+        v = (np.sqrt(VERIFY_RHO) * shared.astype(np.float64) +
+             np.sqrt(1.0 - VERIFY_RHO) * own.astype(np.float64)).astype(np.float32)
+        out.append(f32_to_bf16_bits(v) if cfg.dtype == "bf16" else v)
+    return out[0], out[1]
 
 
 def load_attempts(path: str = ATTEMPTS_JSON) -> dict:

@@ -16,7 +16,7 @@ from tests.gpu_common import (as_f64_out, assert_close, assert_routing_equal, gp
 
 pytestmark = pytest.mark.gpu
 
-MFMA_CASES = [("tp_rank", 8), ("tp_rank", 64), ("full_b8", 8), ("full_b64", 64)]
+MFMA_CASES = [("tp_rank", 8), ("tp_rank", 64), ("full_b8", 8), ("verify_b8", 8), ("full_b64", 64)]
 SAMPLE = {("full_b64", 64): (0, 21, 42, 63)}
 
 

@@ -105,3 +105,30 @@ def test_attempt_table_tiny_recomputed():
         h = O.oproj_residual(x[None], r[None], synth.host_weight(cfg, "w_o"))
         key = O.selection_keys(O.sigmoid(O.router_logits(h, synth.host_weight(cfg, "w_r"))), synth.host_bias(cfg))
         assert O.topk_gap(key, cfg.top_k)[0] < 1e-3
+
+
+def test_verify_tokens_share_a_component():
+    """Speculative-verify tokens: sqrt(rho) * shared + sqrt(1 - rho) * own, so two tokens of
+    the batch correlate by rho, each has unit variance, and a resample redraws only the own
+    part (the shared part is the same stream for every token and attempt)."""
+    cfg = synth.CONFIGS["verify_b8"]
+    f = synth.bf16_bits_to_f32
+    x0, r0 = synth.host_token(cfg, 0, 0)
+    x1, r1 = synth.host_token(cfg, 1, 0)
+    rho = synth.VERIFY_RHO
+    assert abs(np.corrcoef(f(x0), f(x1))[0, 1] - rho) < 0.02
+    assert abs(np.corrcoef(f(r0), f(r1))[0, 1] - rho) < 0.02
+    assert abs(np.std(f(r0)) - 1.0) < 0.02
+    # x_t(attempt 1) - x_t(attempt 0) = sqrt(1 - rho) * (own_1 - own_0), up to rounding
+    x0b, _ = synth.host_token(cfg, 0, 1)
+    d = f(x0b).astype(np.float64) - f(x0)
+    own0 = synth.host_stream(cfg.oproj_in, 0, synth.token_key(0, synth.KIND_X), 1.0, "f32")
+    own1 = synth.host_stream(cfg.oproj_in, 0, synth.token_key(1, synth.KIND_X), 1.0, "f32")
+    want = np.sqrt(1 - rho) * (own1.astype(np.float64) - own0)
+    assert np.max(np.abs(d - want)) < 0.05  # two bf16 roundings of values of size ~3
+
+
+def test_bf16_rounding_helper_matches_generator():
+    a = synth.host_stream(4096, 11, 7, 1.0, "f32")
+    b = synth.host_stream(4096, 11, 7, 1.0, "bf16")
+    assert np.array_equal(synth.f32_to_bf16_bits(a), b)
