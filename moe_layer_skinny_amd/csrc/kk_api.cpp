@@ -127,11 +127,11 @@ const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_log
                               "gateup_gemv_shared", "gateup_gemv_routed", "topk_gateup_gemv_routed",
                               "down_combine_gemv", "moe_prep",    "combine",    "oproj_mfma",
                               "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
-                              "topk_rows",   "tables"};
+                              "topk_rows",   "tables", "topk_tables"};
 enum KName {
   K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
   K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
-  K_TABLES
+  K_TABLES, K_TOPK_TABLES
 };
 
 struct TimingRec {
@@ -203,10 +203,10 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
                 B);
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
-  // oproj, reduce, router logits, top-k rows, tables, gate/up, down, combine; B > 32 adds
-  // the shared expert's split-K gate/up and its SwiGLU, and a launch for routed groups of
-  // more than 16 tokens
-  p->kernels_per_step = B > 32 ? 11 : 8;
+  // oproj, reduce, router logits, top-k rows + tables (one launch up to 16 tokens), gate/up,
+  // down, combine; B > 32 adds the shared expert's split-K gate/up and its SwiGLU, and a
+  // launch for routed groups of more than 16 tokens
+  p->kernels_per_step = B > 32 ? 11 : (B > 16 ? 8 : 7);
   return KK_OK;
 }
 
@@ -312,21 +312,33 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
   return KK_OK;
 }
 
+// Top-k rows and routing tables from logit partials: one launch up to 16 tokens, else one
+// wave-per-token launch and a tables launch.
+kk_status enqueue_topk(kk_ctx* c, int B, const float* logit_part, int splits,
+                       const kk::Routing& rt, hipStream_t s) {
+  if (B <= 16) {
+    KK_HIP(timed(c, K_TOPK_TABLES, s,
+                 [&] {
+                   return kk::launch_topk_tables(c->shape, B, logit_part, splits, c->w.bias, rt, s);
+                 }),
+           "top-k launch");
+    return KK_OK;
+  }
+  KK_HIP(timed(c, K_TOPK_ROWS, s,
+               [&] { return kk::launch_topk_rows(c->shape, B, logit_part, splits, c->w.bias, rt, s); }),
+         "top-k launch");
+  KK_HIP(timed(c, K_TABLES, s, [&] { return kk::launch_tables(c->shape, B, rt, s); }),
+         "routing tables launch");
+  return KK_OK;
+}
+
 // MFMA path: router logits, top-k rows (one wave per token), routing tables (one block).
 kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
                               float* logit_part, hipStream_t s) {
   KK_HIP(timed(c, K_ROUTER_MFMA, s,
                [&] { return kk::launch_router_mfma(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s); }),
          "router logits launch");
-  KK_HIP(timed(c, K_TOPK_ROWS, s,
-               [&] {
-                 return kk::launch_topk_rows(c->shape, B, logit_part,
-                                             kk::mfma_router_splits(c->shape), c->w.bias, rt, s);
-               }),
-         "top-k launch");
-  KK_HIP(timed(c, K_TABLES, s, [&] { return kk::launch_tables(c->shape, B, rt, s); }),
-         "routing tables launch");
-  return KK_OK;
+  return enqueue_topk(c, B, logit_part, kk::mfma_router_splits(c->shape), rt, s);
 }
 
 // MFMA path: grouped gate/up and down over the active experts plus the shared one, combine.
@@ -578,15 +590,7 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     hipStream_t s = (hipStream_t)stream;
     st = enqueue_logits(c, B, h32, rt, p.logit_part, nullptr, nullptr, s);
     if (st != KK_OK) return st;
-    KK_HIP(timed(c, K_TOPK_ROWS, s,
-                 [&] {
-                   return kk::launch_topk_rows(c->shape, B, p.logit_part,
-                                               kk::router_gemv_splits(c->shape), c->w.bias, rt, s);
-                 }),
-           "top-k launch");
-    KK_HIP(timed(c, K_TABLES, s, [&] { return kk::launch_tables(c->shape, B, rt, s); }),
-           "routing tables launch");
-    return KK_OK;
+    return enqueue_topk(c, B, p.logit_part, kk::router_gemv_splits(c->shape), rt, s);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_router_topk");
   }

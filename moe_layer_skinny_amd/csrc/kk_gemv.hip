@@ -360,6 +360,20 @@ __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__
   topk_row(part, splits, bias, B, E, k, routed_scale, blockIdx.x, rt, nullptr);
 }
 
+// Up to 16 tokens in one block: wave t writes token t's top-k row, then the block builds the
+// routing tables (one launch instead of two).
+__global__ __launch_bounds__(1024) void topk_tables_kernel(const float* __restrict__ part,
+                                                          int splits,
+                                                          const float* __restrict__ bias, int E,
+                                                          int k, int B, float routed_scale,
+                                                          Routing rt) {
+  __shared__ TopkScratch sm;
+  const int wave = threadIdx.x >> 6;
+  if (wave < B) topk_row(part, splits, bias, B, E, k, routed_scale, wave, rt, sm.sel);
+  __syncthreads();
+  build_tables(B, E, k, rt, sm);
+}
+
 // One block: routing tables from the topk_idx rows of all B tokens.
 __global__ __launch_bounds__(256) void tables_kernel(int E, int k, int B, Routing rt) {
   __shared__ TopkScratch sm;
@@ -1051,6 +1065,14 @@ hipError_t launch_topk_rows(const Shape& s, int B, const float* part, int splits
                             const float* bias, const Routing& rt, hipStream_t st) {
   hipLaunchKernelGGL(topk_rows_kernel, dim3(B), dim3(64), 0, st, part, splits, bias, s.E, s.k, B,
                      s.routed_scale, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_tables(const Shape& s, int B, const float* part, int splits,
+                              const float* bias, const Routing& rt, hipStream_t st) {
+  if (B > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_tables_kernel, dim3(1), dim3(64 * B), 0, st, part, splits, bias, s.E,
+                     s.k, B, s.routed_scale, rt);
   return hipGetLastError();
 }
 

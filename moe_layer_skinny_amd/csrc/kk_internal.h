@@ -89,6 +89,9 @@ hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* 
 hipError_t launch_topk_rows(const Shape& s, int B, const float* part, int splits,
                             const float* bias, const Routing& rt, hipStream_t st);
 hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t st);
+// Both in one launch, for up to 16 tokens.
+hipError_t launch_topk_tables(const Shape& s, int B, const float* part, int splits,
+                              const float* bias, const Routing& rt, hipStream_t st);
 
 // act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
