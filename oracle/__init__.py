@@ -13,6 +13,7 @@ from .layer import (  # noqa: F401
     gates_for,
     layer_step,
     oproj_residual,
+    rms_norm,
     router_logits,
     routing_tables,
     selection_keys,

@@ -19,7 +19,9 @@ in each docstring as READING:
     the bias steers selection only;
   * expert FFN: gated SwiGLU, W2 (silu(W1 u) * (W3 u)); in the stacked W13 the gate rows
     W1 come first, then the up rows W3;
-  * no normalisation between the residual add and the experts: u = h;
+  * no normalisation between the residual add and the experts (u = h), unless the layer
+    carries an RMSNorm weight: then u = RMSNorm(h) feeds the router and every expert while
+    the residual stream h goes on to the combine unnormalised (eps 1e-6);
   * the shared expert is added unweighted;
   * output order of the selected experts: ascending expert index.
 
@@ -47,6 +49,19 @@ def oproj_residual(x, r, w_o) -> np.ndarray:
     all-reduce is the identity.  x [B][Ko], r [B][H], W_o [H][Ko] (row n = output n).
     """
     return as_f64(r) + as_f64(x) @ as_f64(w_o).T
+
+
+def rms_norm(h, weight, eps: float) -> np.ndarray:
+    """u = weight * h / sqrt(mean(h^2) + eps), row by row (RMS normalisation, per-channel weight).
+
+    READING of the "residual processing" that [P3 "Recovering time between operators"]
+    fuses with the attention output projection: the residual add, then the normalisation
+    whose output is the MoE block's input.  The pages give neither the norm nor eps; RMSNorm
+    with eps = 1e-6 is the plain reading for this layer family.  h [B][H], weight [H].
+    """
+    h = np.asarray(h, dtype=np.float64)
+    ms = np.mean(h * h, axis=1, keepdims=True)
+    return as_f64(weight)[None, :] * h / np.sqrt(ms + eps)
 
 
 def router_logits(h, w_r) -> np.ndarray:
@@ -152,14 +167,15 @@ class LayerWeights:
     """Accessor for one layer's weights: dense tensors as attributes, experts on demand.
 
     w_o [H][Ko], w_r [E][H], bias [E]; expert(e) -> (w13_e [2I][H], w2_e [H][I]);
-    shared() -> (ws13 [2Is][H], ws2 [H][Is]).  ``expert_fn`` lets callers regenerate one
-    expert at a time instead of holding all of them.
+    shared() -> (ws13 [2Is][H], ws2 [H][Is]); norm_weight [H] or None (no normalisation).
+    ``expert_fn`` lets callers regenerate one expert at a time instead of holding all of them.
     """
 
-    def __init__(self, w_o, w_r, bias, expert_fn, ws13, ws2):
+    def __init__(self, w_o, w_r, bias, expert_fn, ws13, ws2, norm_weight=None):
         self.w_o, self.w_r, self.bias = w_o, w_r, bias
         self._expert_fn = expert_fn
         self._ws13, self._ws2 = ws13, ws2
+        self.norm_weight = norm_weight
 
     def expert(self, e: int):
         return self._expert_fn(int(e))
@@ -169,13 +185,13 @@ class LayerWeights:
 
 
 def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
-               out_tokens=None) -> dict:
+               out_tokens=None, norm_eps: float = 1e-6) -> dict:
     """One decode-layer step for B tokens.
 
       h   = r + x W_o^T                                     (o-proj + residual)
-      l   = h W_r^T ; s = sigmoid(l) ; key = s + b           (router scores, READING)
+      u   = h, or RMSNorm(h) with w.norm_weight             (READING)
+      l   = u W_r^T ; s = sigmoid(l) ; key = s + b           (router scores, READING)
       S_t = top-k of key_t ; g_t = s_t[S_t] / sum s_t[S_t]   (READING: gates from unbiased s)
-      u   = h                                               (READING: no norm)
       out_t = h_t + sum_{e in S_t} g_{t,e} swiglu_e(u_t) + swiglu_shared(u_t)
 
     [P2 "What's Optimized"], [P3 "Recovering time between operators"]: the shared expert
@@ -186,7 +202,8 @@ def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
     """
     h = oproj_residual(x, r, w.w_o)
     B, H = h.shape
-    logits = router_logits(h, w.w_r)
+    u = h if w.norm_weight is None else rms_norm(h, w.norm_weight, norm_eps)
+    logits = router_logits(u, w.w_r)
     s = sigmoid(logits)
     key = selection_keys(s, w.bias)
     idx = topk_sets(key, top_k)
@@ -196,7 +213,6 @@ def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
     tokens = np.arange(B) if out_tokens is None else np.asarray(sorted(set(out_tokens)))
     want = np.zeros(B, dtype=bool)
     want[tokens] = True
-    u = h
     routed = np.zeros((B, H), dtype=np.float64)
     for e in tables["act"]:
         rows = [(t, j) for t in range(B) for j in range(top_k) if idx[t, j] == e and want[t]]
@@ -212,5 +228,5 @@ def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
     ys[tokens] = swiglu_expert(u[tokens], ws13, ws2)
     out = np.full((B, H), np.nan)
     out[tokens] = h[tokens] + routed[tokens] + ys[tokens]
-    return {"h": h, "logits": logits, "scores": s, "key": key, "topk_idx": idx,
+    return {"h": h, "u": u, "logits": logits, "scores": s, "key": key, "topk_idx": idx,
             "topk_gate": gates, **tables, "out": out, "tokens": tokens}

@@ -36,7 +36,7 @@ DEV_LIB = os.path.join(_HERE, "libsynth_dev.so")
 ATTEMPTS_JSON = os.path.join(_ROOT, "tests", "golden", "attempts.json")
 
 # Tensor stream ids (key1) for weights; key0 is the layer seed.
-T_WO, T_WR, T_BIAS, T_W13, T_W2, T_WS13, T_WS2, T_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+T_WO, T_WR, T_BIAS, T_W13, T_W2, T_WS13, T_WS2, T_PERM, T_NORM = 1, 2, 3, 4, 5, 6, 7, 8, 9
 # Token streams: key0 = token seed, key1 = TOKEN_BASE + 16 * attempt + kind.
 TOKEN_BASE = 0x100
 KIND_X, KIND_R = 0, 1
@@ -49,6 +49,9 @@ VERIFY_RHO = 0.9
 WEIGHT_SIGMA = 0.02
 ACT_SIGMA = 1.0
 BIAS_SIGMA = 0.1
+# RMSNorm weight: 1 + a draw of this standard deviation per channel
+NORM_SIGMA = 0.1
+NORM_EPS = 1e-6
 ZIPF_S = 1.2
 
 # std of the sum of four independent uniform 32-bit words
@@ -75,6 +78,7 @@ class LayerConfig:
     layer_seed: int = 0
     description: str = ""
     tokens: str = "independent"  # "independent" | "verify" (correlated tokens of one sequence)
+    norm: bool = False  # RMSNorm (weight [H], eps NORM_EPS) between the residual add and experts
 
     @property
     def wbytes(self) -> int:
@@ -102,6 +106,15 @@ CONFIGS = {
                     description="full-size layer, speculative-verify batch: 8 correlated tokens "
                                 "of one sequence (shared component, rho 0.9)",
                     tokens="verify"),
+        LayerConfig("tiny_norm", 256, 256, 16, 2, 128, 128, "f32", (1, 2), "normal", "key",
+                    description="tiny fp32 layer with RMSNorm before router and experts",
+                    norm=True),
+        LayerConfig("full_norm", 7168, 7168, 384, 8, 2048, 2048, "bf16", (1, 8), "normal", "key",
+                    description="full-size layer with RMSNorm before router and experts",
+                    norm=True),
+        LayerConfig("tp_norm", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8, 64), "zipf", "key",
+                    description="one TP16 rank's share with RMSNorm before router and experts",
+                    norm=True),
     ]
 }
 
@@ -207,6 +220,15 @@ def host_expert(cfg: LayerConfig, e: int):
     w13 = host_stream(n13, cfg.layer_seed, T_W13, WEIGHT_SIGMA, cfg.dtype, first=e * n13)
     w2 = host_stream(n2, cfg.layer_seed, T_W2, WEIGHT_SIGMA, cfg.dtype, first=e * n2)
     return w13.reshape(2 * I, H), w2.reshape(H, I)
+
+
+def host_norm_weight(cfg: LayerConfig):
+    """RMSNorm weight [H] in the config dtype: 1 + NORM_SIGMA-scaled draw, fp64 -> fp32 -> dtype."""
+    if not cfg.norm:
+        return None
+    d = host_stream(cfg.hidden, cfg.layer_seed, T_NORM, NORM_SIGMA, "f32").astype(np.float64)
+    v = (1.0 + d).astype(np.float32)
+    return f32_to_bf16_bits(v) if cfg.dtype == "bf16" else v
 
 
 def host_bias(cfg: LayerConfig):

@@ -9,13 +9,13 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (LayerConfig, device_stream, host_bias, host_tokens, weight_spec)
+from . import (LayerConfig, device_stream, host_bias, host_norm_weight, host_tokens, weight_spec)
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
 def device_weights(cfg: LayerConfig, device="cuda", share_from: dict | None = None) -> dict:
-    """w_o, w_r, router_bias, w13, w2, ws13, ws2 as device tensors (out-major layouts).
+    """w_o, w_r, router_bias, w13, w2, ws13, ws2 (and norm_w with a norm) as device tensors.
 
     ``share_from``: reuse the weight tensors of another config with the same shapes and layer
     seed (only the router bias differs between such workloads).
@@ -31,6 +31,8 @@ def device_weights(cfg: LayerConfig, device="cuda", share_from: dict | None = No
         device_stream(t.data_ptr(), t.numel(), cfg.layer_seed, tid, sigma, cfg.dtype, stream=stream)
         out[name] = t
     out["router_bias"] = torch.from_numpy(host_bias(cfg)).to(device)
+    if cfg.norm:
+        out["norm_w"] = host_to_device(host_norm_weight(cfg), cfg.dtype, device)
     torch.cuda.synchronize(device)
     return out
 

@@ -3,7 +3,7 @@
 For every workload and token seed t = 0..B_max-1, attempt j = 0, 1, ... draws (x_t, r_t)
 from the seeded generator (synth) and the fp64 oracle computes the router's ranking values;
 the first attempt whose gap between the k-th and (k+1)-th largest value is >= 1e-3 is kept.
-Gap space (a reading of "seeded so the top-k boundary gap is >= 1e-3"): the selection key
+Layers with an RMSNorm rank on the router logits of the normalised h.  Gap space (a reading of "seeded so the top-k boundary gap is >= 1e-3"): the selection key
 sigmoid(l) + b, except for the layer with a uniform (all-zero) bias, where the sigmoid is
 saturated and the key order is the logit order, so the gap is taken on the logits l.
 
@@ -28,7 +28,8 @@ MAX_ATTEMPTS = 64
 
 def ranking_values(cfg, x, r, w_o, w_r, b):
     h = O.oproj_residual(x[None], r[None], w_o)
-    l = O.router_logits(h, w_r)
+    g = synth.host_norm_weight(cfg)
+    l = O.router_logits(h if g is None else O.rms_norm(h, g, synth.NORM_EPS), w_r)
     if cfg.gap_space == "logit":
         return l
     return O.selection_keys(O.sigmoid(l), b)

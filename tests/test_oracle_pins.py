@@ -338,3 +338,84 @@ def test_out_tokens_subset_matches_full():
     np.testing.assert_allclose(sub["out"][[1, 4]], full["out"][[1, 4]], rtol=1e-13, atol=1e-13)
     assert np.isnan(sub["out"][0]).all()
     assert np.array_equal(sub["perm"], full["perm"])
+
+
+# ----------------------------------------------------------------------------- RMSNorm (optional step)
+def _with_norm(w: O.LayerWeights, gamma) -> O.LayerWeights:
+    return O.LayerWeights(w.w_o, w.w_r, w.bias, w.expert, *w.shared(), norm_weight=gamma)
+
+
+def test_rms_norm_unit_mean_square_and_row_scale():
+    """weight 1, eps 0: every row has mean square 1 exactly (to rounding) and is a positive
+    multiple of its input row."""
+    rng = np.random.default_rng(40)
+    h = rng.normal(0, 3.0, (5, 37))
+    u = O.rms_norm(h, np.ones(37), 0.0)
+    np.testing.assert_allclose(np.mean(u * u, axis=1), 1.0, rtol=0, atol=1e-13)
+    ratio = u / h
+    assert (ratio > 0).all()
+    np.testing.assert_allclose(ratio, ratio[:, :1] * np.ones((1, 37)), rtol=1e-13, atol=0)
+
+
+def test_rms_norm_constant_and_one_hot_rows_closed_form():
+    """h = c (every entry): u = w c / sqrt(c^2 + eps).  h = a e_i: u_i = w_i a /
+    sqrt(a^2 / H + eps), the other entries 0."""
+    rng = np.random.default_rng(41)
+    H = 24
+    w = rng.normal(1.0, 0.3, H)
+    c, eps = -3.0, 0.5
+    u = O.rms_norm(np.full((1, H), c), w, eps)
+    np.testing.assert_allclose(u[0], w * c / np.sqrt(9.0 + 0.5), rtol=1e-15, atol=0)
+    a, i = 2.5, 7
+    h = np.zeros((1, H))
+    h[0, i] = a
+    u = O.rms_norm(h, w, eps)
+    want = np.zeros(H)
+    want[i] = w[i] * a / np.sqrt(a * a / H + eps)
+    np.testing.assert_allclose(u[0], want, rtol=1e-15, atol=0)
+
+
+def test_rms_norm_scale_invariance_and_eps():
+    """eps 0: u(c h) = u(h) for c > 0 and -u(h) for c < 0; eps > 0 shrinks every |u|."""
+    rng = np.random.default_rng(42)
+    h = rng.normal(size=(3, 16))
+    w = rng.normal(1.0, 0.2, 16)
+    np.testing.assert_allclose(O.rms_norm(7.0 * h, w, 0.0), O.rms_norm(h, w, 0.0), rtol=1e-13)
+    np.testing.assert_allclose(O.rms_norm(-0.5 * h, w, 0.0), -O.rms_norm(h, w, 0.0), rtol=1e-13)
+    assert (np.abs(O.rms_norm(h, w, 1e-2)) < np.abs(O.rms_norm(h, w, 0.0))).all()
+
+
+def test_norm_layer_residual_keeps_h_experts_read_u():
+    """W_o = 0 and a constant residual row c: h = c, u = w c / sqrt(c^2 + eps) in closed form.
+    The normalised layer then routes like the plain layer fed u, and out - h equals that
+    layer's out - u: router and experts read u, the combine adds h."""
+    rng = np.random.default_rng(43)
+    H, E, k, I = 16, 8, 2, 6
+    w, _, _ = _rand_weights(H, H, E, I, I, rng)
+    gamma = rng.normal(1.0, 0.3, H)
+    B, c, eps = 3, np.array([2.0, -1.5, 0.25]), 1e-6
+    wz = O.LayerWeights(np.zeros((H, H)), w.w_r, w.bias, w.expert, *w.shared())
+    r = c[:, None] * np.ones((B, H))
+    x = rng.normal(size=(B, H))
+    got = O.layer_step(x, r, _with_norm(wz, gamma), k, norm_eps=eps)
+    u = gamma[None, :] * c[:, None] / np.sqrt(c[:, None] ** 2 + eps)
+    plain = O.layer_step(x, u, wz, k)
+    np.testing.assert_array_equal(got["topk_idx"], plain["topk_idx"])
+    np.testing.assert_allclose(got["topk_gate"], plain["topk_gate"], rtol=1e-13)
+    np.testing.assert_allclose(got["out"] - r, plain["out"] - u, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(got["u"], u, rtol=1e-14)
+
+
+def test_norm_layer_scale_invariance():
+    """eps 0: scaling x and r by c > 0 scales h by c and leaves u, the routing and the expert
+    part out - h unchanged."""
+    rng = np.random.default_rng(44)
+    H, Ko, E, k, I = 16, 12, 8, 3, 6
+    w, _, _ = _rand_weights(H, Ko, E, I, I, rng)
+    wn = _with_norm(w, rng.normal(1.0, 0.3, H))
+    x, r = rng.normal(size=(2, Ko)), rng.normal(size=(2, H))
+    a = O.layer_step(x, r, wn, k, norm_eps=0.0)
+    b = O.layer_step(4.0 * x, 4.0 * r, wn, k, norm_eps=0.0)
+    np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
+    np.testing.assert_allclose(b["h"], 4.0 * a["h"], rtol=1e-14)
+    np.testing.assert_allclose(b["out"] - b["h"], a["out"] - a["h"], rtol=1e-11, atol=1e-12)

@@ -132,3 +132,15 @@ def test_bf16_rounding_helper_matches_generator():
     a = synth.host_stream(4096, 11, 7, 1.0, "f32")
     b = synth.host_stream(4096, 11, 7, 1.0, "bf16")
     assert np.array_equal(synth.f32_to_bf16_bits(a), b)
+
+
+def test_norm_weight_recipe():
+    """RMSNorm weight: 1 + N(0, 0.1)-like per channel, in the config dtype; none without a norm."""
+    assert synth.host_norm_weight(synth.CONFIGS["full_b1"]) is None
+    g = synth.host_norm_weight(synth.CONFIGS["full_norm"])
+    assert g.dtype == np.uint16 and g.shape == (7168,)
+    v = synth.bf16_bits_to_f32(g).astype(np.float64)
+    assert abs(v.mean() - 1.0) < 0.01 and abs(v.std() - synth.NORM_SIGMA) < 0.01
+    t = synth.host_norm_weight(synth.CONFIGS["tiny_norm"])
+    assert t.dtype == np.float32 and t.shape == (256,)
+    np.testing.assert_array_equal(synth.host_norm_weight(synth.CONFIGS["full_norm"]), g)
