@@ -65,6 +65,8 @@ def unique_bytes(cfg, n_act: int) -> dict:
         "shared_down": wb * H * Is,
         "routed_down": wb * n_act * H * I,
     }
+    if cfg.norm:
+        parts["norm"] = wb * H
     parts["total"] = sum(parts.values())
     return parts
 
@@ -80,17 +82,19 @@ def cpu_baseline(cfg, B: int, reps: int) -> dict:
     dense = {n: synth.host_weight(cfg, n) for n in ("w_o", "w_r", "ws13", "ws2")}
     bias = synth.host_bias(cfg)
     # routing first (untimed) to pre-generate exactly the experts the step touches
+    gamma = synth.host_norm_weight(cfg)
     probe = O.layer_step(x, r, O.LayerWeights(dense["w_o"], dense["w_r"], bias,
                                               lambda e: (np.zeros((2 * cfg.inter, cfg.hidden)),
                                                          np.zeros((cfg.hidden, cfg.inter))),
-                                              dense["ws13"], dense["ws2"]), cfg.top_k)
+                                              dense["ws13"], dense["ws2"], norm_weight=gamma),
+                         cfg.top_k, norm_eps=synth.NORM_EPS)
     experts = {int(e): synth.host_expert(cfg, int(e)) for e in probe["act"]}
     W = O.LayerWeights(dense["w_o"], dense["w_r"], bias, lambda e: experts[int(e)], dense["ws13"],
-                       dense["ws2"])
+                       dense["ws2"], norm_weight=gamma)
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        O.layer_step(x, r, W, cfg.top_k)
+        O.layer_step(x, r, W, cfg.top_k, norm_eps=synth.NORM_EPS)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     cores = len(os.sched_getaffinity(0))
@@ -121,9 +125,10 @@ def time_steps(layer, B, x, r, out, idx, gate, ws, s, flush, steps, warmup):
 
 
 def sweep(main_cfg, main_w, args, s, flush) -> dict:
-    """The other workloads: batch 8 / 64 of the full-size layer and an 8-token speculative-
-    verify batch (correlated tokens of one sequence) on the same resident weights (only the
-    router bias differs), and one TP rank's share at batch 1, 2, 8, 64."""
+    """The other workloads: batch 8 / 64 of the full-size layer, an 8-token speculative-verify
+    batch (correlated tokens of one sequence) and the layer with an RMSNorm before the router
+    and experts at batch 1 / 8, on the same resident weights (only the router bias and the
+    norm weight differ), and one TP rank's share at batch 1, 2, 8, 64."""
     import torch
 
     import synth
@@ -131,7 +136,8 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
     from moe_layer_skinny_amd import kk
 
     out = {}
-    plan = [("full_b8", 8), ("full_b64", 64), ("verify_b8", 8)] + [("tp_rank", b) for b in (1, 2, 8, 64)]
+    plan = ([("full_b8", 8), ("full_b64", 64), ("verify_b8", 8), ("full_norm", 1), ("full_norm", 8)]
+            + [("tp_rank", b) for b in (1, 2, 8, 64)])
     weights = {}
     for name, B in plan:
         cfg = synth.CONFIGS[name]
@@ -144,7 +150,8 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
             weights[name] = sd.device_weights(cfg, share_from=share)
         w = weights[name]
         layer = kk.Layer(kk.make_config(cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.top_k,
-                                        cfg.inter, cfg.shared_inter, cfg.dtype), w, B)
+                                        cfg.inter, cfg.shared_inter, cfg.dtype,
+                                        norm_eps=synth.NORM_EPS), w, B)
         x, r, _, _ = sd.device_tokens(cfg, B)
         o = torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda")
         idx = torch.empty(B, cfg.top_k, dtype=torch.int32, device="cuda")
@@ -201,7 +208,7 @@ def main():
     log(f"[bench] {cfg.name} B={B}: filling weights on device")
     w = sd.device_weights(cfg, device=dev)
     layer = kk.Layer(kk.make_config(cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.top_k, cfg.inter,
-                                    cfg.shared_inter, cfg.dtype), w, B)
+                                    cfg.shared_inter, cfg.dtype, norm_eps=synth.NORM_EPS), w, B)
     plan = layer.query_plan(B)
     x, r, _, _ = sd.device_tokens(cfg, B, device=dev)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32

@@ -4,10 +4,11 @@
  * One small-batch (1..64 token) decode step of the weight-bandwidth-bound part of a
  * Kimi-K3-style layer:
  *   h   = r + x W_o^T                       attention output projection + residual
- *   l   = h W_r^T, s = sigmoid(l)            router scores
+ *   u   = h, or with a norm weight w:        u = w * h / sqrt(mean(h^2) + norm_eps)
+ *   l   = u W_r^T, s = sigmoid(l)            router scores
  *   S_t = top-k of (s + b)                   selection (bias steers selection only)
  *   g   = s[S_t] / sum s[S_t] * routed_scale renormalised gates
- *   out = h + sum_j g_j SwiGLU_{S_t,j}(h) + SwiGLU_shared(h)
+ *   out = h + sum_j g_j SwiGLU_{S_t,j}(u) + SwiGLU_shared(u)
  * Sources: "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section
  * "Recovering time between operators" (o-proj fused with residual processing; router
  * scores; selected experts; the shared expert on another stream; small-matrix kernels at
@@ -15,12 +16,14 @@
  * Blazing-FAST Inference", section "What's Optimized" (per-batch kernel choice, shared
  * expert in parallel on a separate stream).  The pages print no formula; the math above
  * is the plain reading of the operations they name (sigmoid + bias router, renormalised
- * gates, gated SwiGLU with gate rows before up rows, no norm before the experts).
+ * gates, gated SwiGLU with gate rows before up rows).  The "residual processing" fused with
+ * the o-proj is read as the residual add, optionally followed by an RMSNorm whose output
+ * feeds the router and the experts while h stays the residual stream.
  *
  * Layouts (all row-major, "out-major": each output row contiguous along its reduction dim)
  *   w_o  [H][Ko]     w_r [E][H]     router_bias [E] (fp32)
  *   w13  [E][2I][H]  rows 0..I-1 gate (W1), rows I..2I-1 up (W3)
- *   w2   [E][H][I]   ws13 [2Is][H]  ws2 [H][Is]
+ *   w2   [E][H][I]   ws13 [2Is][H]  ws2 [H][Is]  norm_weight [H] (optional)
  *   x [B][Ko], resid [B][H], out [B][H]  in the config dtype; h32 [B][H] fp32.
  *   topk_idx [B][k] int32, ascending expert index within each token; topk_gate [B][k] fp32
  *   in the same order.  Slot of (token t, position j) = t*k + j.
@@ -80,6 +83,7 @@ typedef struct {
   int32_t shared_inter; /* Is (shared SwiGLU intermediate) */
   int32_t dtype;        /* kk_dtype of weights, x, resid and out */
   float routed_scale;   /* multiplies the renormalised gates; 1.0 */
+  float norm_eps;       /* RMSNorm epsilon (>= 0; used only with kk_weights.norm_weight) */
 } kk_config;
 
 typedef struct {
@@ -90,6 +94,7 @@ typedef struct {
   const void* w2;
   const void* ws13;
   const void* ws2;
+  const void* norm_weight; /* [H] in the config dtype, or NULL: no norm (u = h) */
 } kk_weights;
 
 typedef struct {
@@ -124,7 +129,7 @@ kk_status kk_query_plan(const kk_ctx* ctx, int32_t B, kk_plan* out);
 kk_status kk_oproj_residual(kk_ctx* ctx, int32_t B, const void* x, const void* resid, float* h32,
                             void* h_out, void* ws, kk_stream stream);
 
-/* Router: logits from fp32 h32, sigmoid scores, selection keys (s + b, fp64), top-k,
+/* Router: logits from fp32 h32 (normalised first when the context has a norm weight), sigmoid scores, selection keys (s + b, fp64), top-k,
  * renormalised gates, and the token->expert permutation with expert offsets (prefix sum).
  * "Recovering time between operators": router scores in MoE preparation. */
 kk_status kk_router_topk(kk_ctx* ctx, int32_t B, const float* h32, int32_t* topk_idx,
@@ -132,7 +137,8 @@ kk_status kk_router_topk(kk_ctx* ctx, int32_t B, const float* h32, int32_t* topk
                          kk_stream stream);
 
 /* Routed experts (each selected expert's weights read once), the shared expert, and the
- * combine out = h32 + sum g y + y_shared (RNE to the config dtype), all on `stream`.
+ * combine out = h32 + sum g y + y_shared (RNE to the config dtype), all on `stream`; the
+ * experts read u = h32, or h32 normalised when the context has a norm weight.
  * Routing tables as written by kk_router_topk for the same B; tables that are not a valid
  * routing leave the routed part out (no out-of-bounds access) -- undefined output.
  * "Recovering time between operators": selected experts; shared expert on another stream. */
@@ -140,9 +146,10 @@ kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t*
                         const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
                         void* out, void* ws, kk_stream stream);
 
-/* The whole step: o-proj + residual, router logits, top-k || shared expert gate/up, routed
- * gate/up, down-projection with the combine (batch 1-2: five launches on `stream`; the split-K
- * MFMA path for larger batches: see kk_query_plan).  topk_idx / topk_gate are optional
+/* The whole step: o-proj + residual (+ norm), router logits, top-k || shared expert gate/up,
+ * routed gate/up, down-projection with the combine (batch 1-2: four launches on `stream`, the
+ * norm recomputed inside the launches that read u; the split-K MFMA path for larger batches,
+ * the norm fused into the o-proj's reduce: see kk_query_plan).  topk_idx / topk_gate are optional
  * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
  * first use for these (B, pointers, stream, flags) and replayed afterwards. */
 kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,

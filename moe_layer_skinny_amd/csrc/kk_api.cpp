@@ -46,8 +46,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace carve-up (offsets in bytes from ws, each 256-byte aligned).
 struct Layout {
-  size_t h32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, A, As, Y, ys,
-      oproj_part, total;
+  size_t h32, u32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, A, As, Y,
+      ys, oproj_part, total;
 };
 
 kk::Shape to_shape(const kk_config& c) {
@@ -65,6 +65,7 @@ Layout make_layout(const kk_config& c, int Bm) {
   };
   const size_t slots = (size_t)Bm * c.top_k;
   L.h32 = take((size_t)Bm * c.hidden * 4);
+  L.u32 = take((size_t)Bm * c.hidden * 4);  // normalised h (split-K path with a norm)
   L.logit_part = take((size_t)kMaxRouterSplits * Bm * c.n_experts * 4);
   L.topk_idx = take(slots * 4);
   L.topk_gate = take(slots * 4);
@@ -101,6 +102,8 @@ kk_status validate_cfg(const kk_config* c, int32_t max_batch) {
     return fail(KK_ERR_INVALID_ARG, "top_k %d > n_experts %d", c->top_k, c->n_experts);
   if (!(c->routed_scale > 0.f) || c->routed_scale != c->routed_scale)
     return fail(KK_ERR_INVALID_ARG, "routed_scale must be a positive number");
+  if (!(c->norm_eps >= 0.f && c->norm_eps <= 3.4e38f))
+    return fail(KK_ERR_INVALID_ARG, "norm_eps must be a finite number >= 0");
   if (c->top_k > kMaxTopK)
     return fail(KK_ERR_UNSUPPORTED, "top_k %d > %d", c->top_k, kMaxTopK);
   if (c->n_experts > kMaxExperts)
@@ -127,11 +130,12 @@ const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_log
                               "gateup_gemv_shared", "gateup_gemv_routed", "topk_gateup_gemv_routed",
                               "down_combine_gemv", "moe_prep",    "combine",    "oproj_mfma",
                               "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
-                              "topk_rows",   "tables", "topk_tables"};
+                              "topk_rows",   "tables", "topk_tables", "oproj_reduce_norm",
+                              "norm_rows"};
 enum KName {
   K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
   K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
-  K_TABLES, K_TOPK_TABLES
+  K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS
 };
 
 struct TimingRec {
@@ -154,6 +158,7 @@ struct kk_ctx {
   kk_config cfg;
   kk::Shape shape;
   kk::Weights w;
+  kk::Norm norm;  // gamma == nullptr: no norm
   int max_batch;
   int device;
   kk::Device dev;
@@ -241,6 +246,7 @@ hipError_t timed(kk_ctx* c, int name, hipStream_t s, F&& launch) {
 
 struct WsPtrs {
   float* h32;
+  float* u32;
   float* logit_part;
   int32_t* topk_idx;
   float* topk_gate;
@@ -259,7 +265,7 @@ struct WsPtrs {
 WsPtrs carve(const kk_ctx* c, void* ws) {
   char* b = (char*)ws;
   const Layout& L = c->L;
-  return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
+  return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.u32),        (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
                 (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
                 (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
                 (float*)(b + L.A),         (float*)(b + L.As),         (float*)(b + L.Y),
@@ -293,8 +299,10 @@ kk_status check_common(const kk_ctx* c, int B, void* ws) {
   } while (0)
 
 // ---- step pieces ------------------------------------------------------------------------
+// With u32 (and a norm): the split-K path's reduce also writes u32 = norm(h32); the GEMV path
+// leaves the norm to the launches that read u.
 kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h32, void* h_out,
-                        float* part, int path, hipStream_t s) {
+                        float* part, float* u32, int path, hipStream_t s) {
   if (path == KK_PATH_GEMV) {
     KK_HIP(timed(c, K_OPROJ, s,
                  [&] {
@@ -306,10 +314,30 @@ kk_status enqueue_oproj(kk_ctx* c, int B, const void* x, const void* r, float* h
   KK_HIP(timed(c, K_OPROJ_MFMA, s,
                [&] { return kk::launch_oproj_mfma(c->shape, c->dev, B, x, part, c->w.w_o, s); }),
          "oproj launch");
+  if (u32 && c->norm.gamma) {
+    KK_HIP(timed(c, K_OPROJ_REDUCE_NORM, s,
+                 [&] { return kk::launch_norm_rows(c->shape, B, part, r, h32, h_out, c->norm, u32, s); }),
+           "oproj reduce + norm launch");
+    return KK_OK;
+  }
   KK_HIP(timed(c, K_OPROJ_REDUCE, s,
                [&] { return kk::launch_oproj_reduce(c->shape, B, part, r, h32, h_out, s); }),
          "oproj reduce launch");
   return KK_OK;
+}
+
+// Split-K path on its own (router / experts from a caller's h32): u32 = norm(h32) when the
+// context has a norm; returns the rows the path should read (u32 or h32).
+const float* enqueue_norm_from_h32(kk_ctx* c, int B, const float* h32, float* u32, hipStream_t s,
+                                   kk_status* st) {
+  *st = KK_OK;
+  if (!c->norm.gamma) return h32;
+  hipError_t e = timed(c, K_NORM_ROWS, s, [&] {
+    return kk::launch_norm_rows(c->shape, B, nullptr, nullptr, const_cast<float*>(h32), nullptr,
+                                c->norm, u32, s);
+  });
+  if (e != hipSuccess) *st = hip_fail(e, "norm launch");
+  return u32;
 }
 
 // Top-k rows and routing tables from logit partials: one launch up to 16 tokens, else one
@@ -332,22 +360,23 @@ kk_status enqueue_topk(kk_ctx* c, int B, const float* logit_part, int splits,
   return KK_OK;
 }
 
-// MFMA path: router logits, top-k rows (one wave per token), routing tables (one block).
-kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
+// MFMA path: router logits from u (h32 or its normalised rows), then the top-k and tables.
+kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* u, const kk::Routing& rt,
                               float* logit_part, hipStream_t s) {
   KK_HIP(timed(c, K_ROUTER_MFMA, s,
-               [&] { return kk::launch_router_mfma(c->shape, c->dev, B, h32, c->w.w_r, logit_part, s); }),
+               [&] { return kk::launch_router_mfma(c->shape, c->dev, B, u, c->w.w_r, logit_part, s); }),
          "router logits launch");
   return enqueue_topk(c, B, logit_part, kk::mfma_router_splits(c->shape), rt, s);
 }
 
-// MFMA path: grouped gate/up and down over the active experts plus the shared one, combine.
-kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* h32, const kk::Routing& rt,
-                               const WsPtrs& p, void* out, hipStream_t s) {
+// MFMA path: grouped gate/up (from u) and down over the active experts plus the shared one,
+// combine (onto h32).
+kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* u, const float* h32,
+                               const kk::Routing& rt, const WsPtrs& p, void* out, hipStream_t s) {
   KK_HIP(timed(c, K_GU_MFMA, s,
                [&] {
                  // (the o-proj partials are consumed by now: their region is scratch)
-                 return kk::launch_gateup_mfma(c->shape, c->dev, B, h32, c->w.w13, c->w.ws13, rt,
+                 return kk::launch_gateup_mfma(c->shape, c->dev, B, u, c->w.w13, c->w.ws13, rt,
                                                p.A, p.As, p.oproj_part, s);
                }),
          "gate/up launch");
@@ -369,7 +398,7 @@ kk_status enqueue_logits(kk_ctx* c, int B, const float* h32, const kk::Routing& 
   KK_HIP(timed(c, ws13 ? K_LOGITS_SHARED : K_LOGITS, s,
                [&] {
                  return kk::launch_router_logits(c->shape, c->dev, B, h32, c->w.w_r, logit_part,
-                                                 ws13, rt, As, s);
+                                                 ws13, rt, As, c->norm, s);
                }),
          "router logits launch");
   return KK_OK;
@@ -379,8 +408,10 @@ kk_status enqueue_shared_gateup(kk_ctx* c, int B, const float* h32, const kk::Ro
                                 float* As, hipStream_t s) {
   KK_HIP(timed(c, K_GU_SHARED, s,
                [&] {
+                 kk::GateupExtras x;
+                 x.norm = c->norm;
                  return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.ws13, true, rt, As,
-                                               kk::GateupExtras{}, s);
+                                               x, s);
                }),
          "shared gate/up launch");
   return KK_OK;
@@ -401,6 +432,7 @@ kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const k
   x.ws2 = c->w.ws2;
   x.As = p.As;
   x.ys = p.ys;
+  x.norm = c->norm;
   KK_HIP(timed(c, logit_part ? K_TOPK_GU : K_GU_ROUTED, s,
                [&] {
                  return kk::launch_gateup_gemv(c->shape, c->dev, B, h32, c->w.w13, false, rt, p.A,
@@ -421,12 +453,13 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
   WsPtrs p = carve(c, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act};
-  kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, path, s);
+  kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
   if (path == KK_PATH_SPLITK_MFMA) {
-    st = enqueue_router_mfma(c, B, p.h32, rt, p.logit_part, s);
+    const float* u = c->norm.gamma ? p.u32 : p.h32;
+    st = enqueue_router_mfma(c, B, u, rt, p.logit_part, s);
     if (st != KK_OK) return st;
-    return enqueue_experts_mfma(c, B, p.h32, rt, p, out, s);
+    return enqueue_experts_mfma(c, B, u, p.h32, rt, p, out, s);
   }
   if (!two_stream) {
     // the shared expert's gate/up streams with the router logits, its down-projection
@@ -496,10 +529,14 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     KK_PTR(w->w2, "w2");
     KK_PTR(w->ws13, "ws13");
     KK_PTR(w->ws2, "ws2");
+    if (w->norm_weight && misaligned(w->norm_weight))
+      return fail(KK_ERR_INVALID_ARG, "norm_weight is not 16-byte aligned");
     kk_ctx* c = new kk_ctx();
     c->cfg = *cfg;
     c->shape = to_shape(*cfg);
     c->w = kk::Weights{w->w_o, w->w_r, w->router_bias, w->w13, w->w2, w->ws13, w->ws2};
+    c->norm.gamma = w->norm_weight;
+    c->norm.eps = cfg->norm_eps;
     c->max_batch = max_batch;
     c->L = make_layout(*cfg, max_batch);
     auto bail = [&](hipError_t e, const char* what) {
@@ -563,7 +600,8 @@ kk_status kk_oproj_residual(kk_ctx* c, int32_t B, const void* x, const void* res
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     WsPtrs p = carve(c, ws);
-    return enqueue_oproj(c, B, x, resid, h32, h_out, p.oproj_part, plan.path, (hipStream_t)stream);
+    return enqueue_oproj(c, B, x, resid, h32, h_out, p.oproj_part, nullptr, plan.path,
+                         (hipStream_t)stream);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_oproj_residual");
   }
@@ -584,8 +622,11 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     WsPtrs p = carve(c, ws);
     kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
-    if (plan.path == KK_PATH_SPLITK_MFMA)
-      return enqueue_router_mfma(c, B, h32, rt, p.logit_part, (hipStream_t)stream);
+    if (plan.path == KK_PATH_SPLITK_MFMA) {
+      const float* u = enqueue_norm_from_h32(c, B, h32, p.u32, (hipStream_t)stream, &st);
+      if (st != KK_OK) return st;
+      return enqueue_router_mfma(c, B, u, rt, p.logit_part, (hipStream_t)stream);
+    }
     // GEMV path on its own: logits, then the top-k rows and the tables
     hipStream_t s = (hipStream_t)stream;
     st = enqueue_logits(c, B, h32, rt, p.logit_part, nullptr, nullptr, s);
@@ -616,7 +657,11 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
                    (int32_t*)perm, p.inv_perm, p.act, p.n_act};
     KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
            "moe prep launch");
-    if (plan.path == KK_PATH_SPLITK_MFMA) return enqueue_experts_mfma(c, B, h32, rt, p, out, s);
+    if (plan.path == KK_PATH_SPLITK_MFMA) {
+      const float* u = enqueue_norm_from_h32(c, B, h32, p.u32, s, &st);
+      if (st != KK_OK) return st;
+      return enqueue_experts_mfma(c, B, u, h32, rt, p, out, s);
+    }
     st = enqueue_shared_gateup(c, B, h32, rt, p.As, s);
     if (st != KK_OK) return st;
     return enqueue_routed_and_combine(c, B, h32, rt, p, nullptr, out, s);

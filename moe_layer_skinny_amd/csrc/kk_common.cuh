@@ -45,6 +45,11 @@ struct Elem<uint16_t> {  // bf16 bit patterns
     return __uint_as_float((uint32_t)p[i] << 16);
   }
   __device__ static __forceinline__ void store(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  // elements i..i+3 (i % 4 == 0)
+  __device__ static __forceinline__ float4 load4(const uint16_t* p, size_t i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y));
+  }
 };
 
 template <>
@@ -58,6 +63,9 @@ struct Elem<float> {
   }
   __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
   __device__ static __forceinline__ void store(float* p, size_t i, float v) { p[i] = v; }
+  __device__ static __forceinline__ float4 load4(const float* p, size_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+  }
 };
 
 // Sum over the SEG lanes of each aligned lane segment (SEG a power of two <= 64).

@@ -278,6 +278,54 @@ struct Stage {
     for (int j = 0; j < Q; ++j) dst[min((int)(threadIdx.x + j * blockDim.x), n4 - 1)] = v[j];
     for (int i = threadIdx.x + Q * blockDim.x; i < n4; i += blockDim.x) dst[i] = src[i];
   }
+  // Instead of h, stores u = h * gamma / sqrt(mean(h^2) + eps) for each token row of H floats
+  // (H % 4 == 0; the Q float4s of the block cover all rows, NT of them at most).  Sums of
+  // squares go per thread, per wave (DPP), then over the waves in wave order through
+  // red[NT * waves], so every block of one launch shape writes the same bits.
+  template <typename T, int NT>
+  __device__ __forceinline__ void store_rmsnorm(float* d, const T* __restrict__ gamma, float eps,
+                                                int H, float* red) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+    const int h4 = H / 4;
+    float ss[NT];
+    float4 g[Q];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ss[t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      const int i = threadIdx.x + j * blockDim.x;
+      const int ic = min(i, n4 - 1);
+      const int t = NT == 1 ? 0 : ic / h4;
+      g[j] = Elem<T>::load4(gamma, (size_t)(ic - t * h4) * 4);
+      const float4 x = v[j];
+      const float sq = i < n4 ? x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w : 0.f;
+#pragma unroll
+      for (int q = 0; q < NT; ++q) ss[q] += q == t ? sq : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      ss[t] = seg_sum_dpp<64>(ss[t]);
+      if (lane == 63) red[wave * NT + t] = ss[t];
+    }
+    __syncthreads();
+    float inv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float sum = 0.f;
+      for (int w = 0; w < nwv; ++w) sum += red[w * NT + t];
+      inv[t] = 1.f / sqrtf(sum / (float)H + eps);
+    }
+    float4* dst = reinterpret_cast<float4*>(d);
+#pragma unroll
+    for (int j = 0; j < Q; ++j) {
+      // past the end the last float4 is written again with its own value
+      const int ic = min((int)(threadIdx.x + j * blockDim.x), n4 - 1);
+      const float r = inv[NT == 1 ? 0 : ic / h4];
+      const float4 x = v[j];
+      dst[ic] = make_float4(x.x * r * g[j].x, x.y * r * g[j].y, x.z * r * g[j].z,
+                            x.w * r * g[j].w);
+    }
+  }
 };
 
 // float4s per thread that cover `rows` fp32 rows of K elements with kGemvThreads threads.
@@ -312,11 +360,12 @@ template <typename T, int CPS, int CPRH, int NT>
 __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
     const float* __restrict__ h32, const T* __restrict__ w_r, int H, int E, int B, int splits,
     float* __restrict__ part, const T* __restrict__ ws13, int Is, int k, Routing rt,
-    float* __restrict__ As) {
+    float* __restrict__ As, const T* __restrict__ gamma, float eps) {
   using G = Geo<T, CPS>;
   using GH = Geo<T, CPRH>;
   constexpr int MAXU = 2;  // (expert, slice) units per wave; the host checks E * splits
   extern __shared__ float lds[];  // u [B][H]
+  __shared__ float nred[(kGemvThreads / 64) * NT];
   const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
@@ -334,7 +383,10 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   if (shared && gw < Is) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
   Stage<stage_q(NT, GH::K)> st;
   st.load(h32, B * H);
-  st.store(lds);
+  if (gamma)
+    st.template store_rmsnorm<T, NT>(lds, gamma, eps, H, nred);
+  else
+    st.store(lds);
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < MAXU; ++j) {
@@ -477,11 +529,13 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     const float* __restrict__ u, const T* __restrict__ w13, int I, int k, int B, int shared,
     Routing rt, float* __restrict__ A, const float* __restrict__ part, int splits,
     const float* __restrict__ bias, int E, float routed_scale, const T* __restrict__ ws2,
-    const float* __restrict__ As, float* __restrict__ ys, int H) {
+    const float* __restrict__ As, float* __restrict__ ys, int H, const T* __restrict__ gamma,
+    float eps) {
   using G = Geo<T, CPR>;
   static_assert(G::SEG == 64 && G::EXACT, "gate/up rows must span the wave exactly");
   constexpr int HA = (G::CPL + 1) / 2, HB = G::CPL - HA;
   extern __shared__ float lds[];  // u [B][K]
+  __shared__ float nred[(kGemvThreads / 64) * NT];
   __shared__ TopkScratch sm;
   __shared__ LdsTables tb;
   __shared__ float lg[TOPK ? 2 * kMaxExperts : 1];
@@ -502,7 +556,10 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   if (ws2 && wave > 0)
     shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, blockIdx.x * (wpb - 1) + wave - 1,
                                      gridDim.x * (wpb - 1), lane);
-  st.store(lds);
+  if (gamma)
+    st.template store_rmsnorm<T, NT>(lds, gamma, eps, G::K, nred);
+  else
+    st.store(lds);
   __syncthreads();
   if (TOPK) {
     Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
@@ -903,7 +960,7 @@ hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const 
 template <typename T, int CPS, int CPRH>
 hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* h32,
                            const void* w_r, float* part, const void* ws13, const Routing& rt,
-                           float* As, hipStream_t st) {
+                           float* As, const Norm& nm, hipStream_t st) {
   const int splits = s.H / Geo<T, CPS>::K;
   const int nw = d.num_cu * (kGemvThreads / 64);
   if (s.E * splits > 2 * nw) return hipErrorInvalidValue;
@@ -911,7 +968,8 @@ hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* 
   auto kern = B == 1 ? router_logits_kernel<T, CPS, CPRH, 1> : router_logits_kernel<T, CPS, CPRH, 2>;
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, h32, (const T*)w_r, s.H,
-                     s.E, B, splits, part, (const T*)ws13, s.Is, s.k, rt, As);
+                     s.E, B, splits, part, (const T*)ws13, s.Is, s.k, rt, As,
+                     (const T*)nm.gamma, nm.eps);
   return hipGetLastError();
 }
 
@@ -930,7 +988,7 @@ hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, cons
   const int inter = shared ? s.Is : s.I;
   hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, u, (const T*)w13, inter,
                      s.k, B, shared ? 1 : 0, rt, A, x.part, x.splits, x.bias, s.E, s.routed_scale,
-                     (const T*)x.ws2, x.As, x.ys, s.H);
+                     (const T*)x.ws2, x.As, x.ys, s.H, (const T*)x.norm.gamma, x.norm.eps);
   return hipGetLastError();
 }
 
@@ -1012,11 +1070,11 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
                                 const void* w_r, float* part, const void* ws13, const Routing& rt,
-                                float* As, hipStream_t st) {
+                                float* As, const Norm& nm, hipStream_t st) {
   if (s.dtype == 1 && s.H == 7168)
-    return router_logits_t<uint16_t, 128, 896>(s, d, B, h32, w_r, part, ws13, rt, As, st);
+    return router_logits_t<uint16_t, 128, 896>(s, d, B, h32, w_r, part, ws13, rt, As, nm, st);
   if (s.dtype == 0 && s.H == 256)
-    return router_logits_t<float, 64, 64>(s, d, B, h32, w_r, part, ws13, rt, As, st);
+    return router_logits_t<float, 64, 64>(s, d, B, h32, w_r, part, ws13, rt, As, nm, st);
   return hipErrorInvalidValue;
 }
 

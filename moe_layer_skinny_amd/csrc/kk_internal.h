@@ -34,6 +34,13 @@ struct Routing {
   int32_t* n_act;      // [1]
 };
 
+// RMSNorm between the residual add and the router / experts:
+// u = h * gamma / sqrt(mean(h^2) + eps); gamma == nullptr: none, u = h.
+struct Norm {
+  const void* gamma = nullptr;  // [H] in the config dtype
+  float eps = 0.f;
+};
+
 // Launch configuration facts gathered once per context.
 struct Device {
   int num_cu;
@@ -52,9 +59,10 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 // nullptr the same launch computes the shared expert's gate/up,
 // As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  The top-k runs in the routed gate/up
 // launch (GateupExtras::part) or, on its own, in launch_topk_rows + launch_tables.
+// With a norm every block stages u = norm(h32) in its LDS from h32.
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
                                 const void* w_r, float* partials, const void* ws13,
-                                const Routing& rt, float* As, hipStream_t st);
+                                const Routing& rt, float* As, const Norm& nm, hipStream_t st);
 int router_gemv_splits(const Shape& s);
 
 // Optional work of the routed gate/up launch.
@@ -65,6 +73,7 @@ struct GateupExtras {
   const void* ws2 = nullptr;    // shared expert's down-projection ys = Ws2 . As in the launch
   const float* As = nullptr;
   float* ys = nullptr;
+  Norm norm;                    // stage u = norm(u) (every block from the rows it reads)
 };
 
 // Routed gate/up over the active experts (act/n_act) or the shared expert (shared=true):
@@ -105,6 +114,10 @@ hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void*
                              const void* w_o, hipStream_t st);
 hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const void* r,
                                float* h32, void* h_out, hipStream_t st);
+// One block per token: u32 = norm(h) with h = r + sum of the o-proj partials (also written to
+// h32 / h_out) when part != nullptr, else h read from h32.
+hipError_t launch_norm_rows(const Shape& s, int B, const float* part, const void* r, float* h32,
+                            void* h_out, const Norm& nm, float* u32, hipStream_t st);
 // Router logit partials from h32 (three bf16 terms per fp32 value).
 hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w_r, float* part, hipStream_t st);

@@ -81,6 +81,70 @@ __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restri
   if (h_out) Elem<T>::store(h_out, i, hv);
 }
 
+// One token row per block: h = r + the o-proj K-split partials summed in slice order (as
+// oproj_reduce_kernel), written to h32 / h_out, or h read from h32 when part is null; then
+// u32 = h * gamma / sqrt(mean(h^2) + eps).  The sum of squares goes per thread, per wave (DPP),
+// then over the waves in order.  Each thread holds columns threadIdx.x + j * blockDim.x.
+template <typename T, int MAXS, int MAXJ>
+__global__ __launch_bounds__(1024) void norm_rows_kernel(const float* __restrict__ part,
+                                                        int splits, const T* __restrict__ r,
+                                                        int B, int H, float* __restrict__ h32,
+                                                        T* __restrict__ h_out,
+                                                        const T* __restrict__ gamma, float eps,
+                                                        float* __restrict__ u32) {
+  __shared__ float red[16];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nwv = blockDim.x >> 6;
+  const size_t row = (size_t)t * H;
+  float hv[MAXJ], g[MAXJ];
+  if (part) {
+    float v[MAXJ][MAXS], rv[MAXJ];
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      const int c = min((int)(threadIdx.x + j * blockDim.x), H - 1);
+#pragma unroll
+      for (int sp = 0; sp < MAXS; ++sp)
+        v[j][sp] = part[(size_t)min(sp, splits - 1) * B * H + row + c];
+      rv[j] = Elem<T>::load(r, row + c);
+    }
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < MAXS; ++sp) acc += sp < splits ? v[j][sp] : 0.f;
+      hv[j] = rv[j] + acc;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < MAXJ; ++j)
+      hv[j] = h32[row + min((int)(threadIdx.x + j * blockDim.x), H - 1)];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = threadIdx.x + j * blockDim.x;
+    g[j] = Elem<T>::load(gamma, min(c, H - 1));
+    ss += c < H ? hv[j] * hv[j] : 0.f;
+  }
+  ss = seg_sum_dpp<64>(ss);
+  if (lane == 63) red[wave] = ss;
+  __syncthreads();
+  float sum = 0.f;
+  for (int w = 0; w < nwv; ++w) sum += red[w];
+  const float inv = 1.f / sqrtf(sum / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < MAXJ; ++j) {
+    const int c = threadIdx.x + j * blockDim.x;
+    if (c < H) {
+      if (part) {
+        h32[row + c] = hv[j];
+        if (h_out) Elem<T>::store(h_out, row + c, hv[j]);
+      }
+      u32[row + c] = hv[j] * inv * g[j];
+    }
+  }
+}
+
 // As[t][i] = silu(sum_c P[c][t][i]) * sum_c P[c][t][Is + i] over `chunks` K-chunk partials of
 // the shared expert's gate/up rows (fixed chunk order).
 template <int MAXC>
@@ -514,6 +578,24 @@ hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const v
   const int n = B * s.H;
   hipLaunchKernelGGL((oproj_reduce_kernel<uint16_t, 8>), dim3((n + 255) / 256), dim3(256), 0, st,
                      part, mfma_oproj_splits(s), (const uint16_t*)r, B, s.H, h32, (uint16_t*)h_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_rows(const Shape& s, int B, const float* part, const void* r, float* h32,
+                            void* h_out, const Norm& nm, float* u32, hipStream_t st) {
+  constexpr int MAXS = 8, MAXJ = 8;
+  const int threads = s.H >= 1024 ? 1024 : (s.H + 63) / 64 * 64;
+  if (!nm.gamma || s.H % 4 || s.H > MAXJ * threads || (part && mfma_oproj_splits(s) > MAXS))
+    return hipErrorInvalidValue;
+  const int splits = part ? mfma_oproj_splits(s) : 1;
+  if (s.dtype == 1)
+    hipLaunchKernelGGL((norm_rows_kernel<uint16_t, MAXS, MAXJ>), dim3(B), dim3(threads), 0, st,
+                       part, splits, (const uint16_t*)r, B, s.H, h32, (uint16_t*)h_out,
+                       (const uint16_t*)nm.gamma, nm.eps, u32);
+  else
+    hipLaunchKernelGGL((norm_rows_kernel<float, MAXS, MAXJ>), dim3(B), dim3(threads), 0, st,
+                       part, splits, (const float*)r, B, s.H, h32, (float*)h_out,
+                       (const float*)nm.gamma, nm.eps, u32);
   return hipGetLastError();
 }
 

@@ -26,11 +26,13 @@ class KKConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("oproj_in", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("routed_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("norm_eps", ctypes.c_float)]
 
 
 class KKWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_o", "w_r", "router_bias", "w13", "w2", "ws13", "ws2")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_o", "w_r", "router_bias", "w13", "w2", "ws13", "ws2",
+                                               "norm_weight")]
 
 
 class KKPlan(ctypes.Structure):
@@ -100,9 +102,12 @@ def _check(status: int) -> None:
         raise KKError(status, last_error())
 
 
-def make_config(hidden, oproj_in, n_experts, top_k, inter, shared_inter, dtype, routed_scale=1.0):
+def make_config(hidden, oproj_in, n_experts, top_k, inter, shared_inter, dtype, routed_scale=1.0,
+                norm_eps=1e-6):
+    """norm_eps applies only to a layer created with a norm weight ("norm_w")."""
     dt = {"f32": KK_F32, "bf16": KK_BF16}.get(dtype, dtype)
-    return KKConfig(hidden, oproj_in, n_experts, top_k, inter, shared_inter, dt, routed_scale)
+    return KKConfig(hidden, oproj_in, n_experts, top_k, inter, shared_inter, dt, routed_scale,
+                    norm_eps)
 
 
 def validate(cfg: KKConfig, max_batch: int) -> int:
@@ -125,13 +130,15 @@ def _stream(stream) -> int | None:
 
 
 class Layer:
-    """One decode layer bound to device-resident weights (torch tensors, out-major)."""
+    """One decode layer bound to device-resident weights (torch tensors, out-major); an optional
+    "norm_w" [H] adds the RMSNorm before the router and the experts."""
 
     def __init__(self, cfg: KKConfig, weights: dict, max_batch: int):
         self.cfg, self.max_batch = cfg, max_batch
         self._weights = weights  # keep the tensors alive
         w = KKWeights(*(weights[n].data_ptr() for n in
-                        ("w_o", "w_r", "router_bias", "w13", "w2", "ws13", "ws2")))
+                        ("w_o", "w_r", "router_bias", "w13", "w2", "ws13", "ws2")),
+                      _ptr(weights.get("norm_w")))
         h = ctypes.c_void_p()
         _check(lib().kk_create(ctypes.byref(cfg), ctypes.byref(w), max_batch, ctypes.byref(h)))
         self._h = h

@@ -47,7 +47,7 @@ def gpu_layer(name: str):
     log(f"[gpu_layer] {name}: filling weights on device (shared={share is not None})")
     w = sd.device_weights(cfg, share_from=share)
     kcfg = kk.make_config(cfg.hidden, cfg.oproj_in, cfg.n_experts, cfg.top_k, cfg.inter,
-                          cfg.shared_inter, cfg.dtype)
+                          cfg.shared_inter, cfg.dtype, norm_eps=synth.NORM_EPS)
     layer = kk.Layer(kcfg, w, cfg.max_batch)
     _layers[name] = (cfg, w, layer)
     return _layers[name]
@@ -58,7 +58,8 @@ def host_layer_weights(name: str) -> O.LayerWeights:
     cfg = synth.CONFIGS[name]
     return O.LayerWeights(synth.host_weight(cfg, "w_o"), synth.host_weight(cfg, "w_r"),
                           synth.host_bias(cfg), lambda e: synth.host_expert(cfg, e),
-                          synth.host_weight(cfg, "ws13"), synth.host_weight(cfg, "ws2"))
+                          synth.host_weight(cfg, "ws13"), synth.host_weight(cfg, "ws2"),
+                          norm_weight=synth.host_norm_weight(cfg))
 
 
 @functools.lru_cache(maxsize=None)
@@ -66,7 +67,8 @@ def oracle_step(name: str, B: int, out_tokens: tuple | None = None) -> dict:
     cfg = synth.CONFIGS[name]
     x, r = synth.host_tokens(cfg, B)
     return O.layer_step(x, r, host_layer_weights(name), cfg.top_k,
-                        out_tokens=None if out_tokens is None else list(out_tokens))
+                        out_tokens=None if out_tokens is None else list(out_tokens),
+                        norm_eps=synth.NORM_EPS)
 
 
 def as_f64_out(t) -> np.ndarray:

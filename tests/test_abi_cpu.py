@@ -101,3 +101,26 @@ def test_status_strings():
 def test_workspace_grows_with_batch():
     cfg = _cfg("full_b64")
     assert kk.workspace_bytes(cfg, 64) > kk.workspace_bytes(cfg, 8) > kk.workspace_bytes(cfg, 1)
+
+
+def test_norm_eps_must_be_finite_and_non_negative():
+    for bad in (-1e-6, float("nan"), float("inf")):
+        assert kk.validate(_cfg(norm_eps=bad), 1) == kk.KK_ERR_INVALID_ARG
+    for ok in (0.0, 1e-6, 1.0):
+        assert kk.validate(_cfg(norm_eps=ok), 1) == kk.KK_OK
+
+
+def _header_struct_fields(name: str) -> list[str]:
+    import re
+    text = open(kk.HEADER).read()
+    body = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + r";", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return [re.findall(r"(\w+)\s*;", d)[0] for d in body.split(";") if d.strip()
+            for d in [d + ";"]]
+
+
+@pytest.mark.parametrize("cname,pystruct", [("kk_config", kk.KKConfig), ("kk_weights", kk.KKWeights),
+                                            ("kk_plan", kk.KKPlan)])
+def test_binding_structs_match_header(cname, pystruct):
+    """The ctypes structures list the header's fields in the header's order."""
+    assert [f for f, _ in pystruct._fields_] == _header_struct_fields(cname)
