@@ -10,10 +10,13 @@ See ``oracle.layer`` for the definitions and the passages they follow.
 from .layer import (  # noqa: F401
     LayerWeights,
     as_f64,
+    chain_step,
     gates_for,
     layer_step,
     oproj_residual,
     rms_norm,
+    round_to_bf16,
+    round_to_f32,
     router_logits,
     routing_tables,
     selection_keys,

@@ -41,6 +41,27 @@ def as_f64(a) -> np.ndarray:
     return a.astype(np.float64)
 
 
+def round_to_bf16(v) -> np.ndarray:
+    """Each value rounded to the nearest bf16 number (8 significant bits, fp32 exponent range),
+    ties to the even significand; returned as float64.  Overflow past the largest bf16 gives
+    +-inf.  (The layer's output in a bf16 layer; the residual stream of the next layer.)"""
+    v = np.asarray(v, dtype=np.float64)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    _, e = np.frexp(v[fin])  # v = m * 2**e with 0.5 <= |m| < 1
+    e = np.maximum(e, -125)  # below the normal range the spacing stays 2**-133
+    q = np.ldexp(v[fin], 8 - e)  # one unit of q = one bf16 step at this exponent
+    out[fin] = np.ldexp(np.round(q), e - 8)  # numpy rounds halves to even
+    big = np.abs(out) > 3.3895313892515355e38
+    out[big] = np.sign(out[big]) * np.inf
+    return out
+
+
+def round_to_f32(v) -> np.ndarray:
+    """Each value rounded to the nearest fp32 number (ties to even), as float64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def oproj_residual(x, r, w_o) -> np.ndarray:
     """h = r + x W_o^T: attention output projection plus the residual add.
 
@@ -230,3 +251,26 @@ def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
     out[tokens] = h[tokens] + routed[tokens] + ys[tokens]
     return {"h": h, "u": u, "logits": logits, "scores": s, "key": key, "topk_idx": idx,
             "topk_gate": gates, **tables, "out": out, "tokens": tokens}
+
+
+def chain_step(xs, r0, ws, top_k: int, out_dtype: str, routed_scale: float = 1.0,
+               norm_eps: float = 1e-6) -> list:
+    """Several layers in sequence, each with its own weights: layer l reads x_l and the
+    residual stream r_l; r_0 is given and r_{l+1} is layer l's output as stored in the layer
+    dtype (rounded to nearest-even bf16, or fp32), the next layer's input.
+
+    READING of consecutive decode layers ([P2 "What's Optimized"] and [P3 "Recovering time
+    between operators"] load the next operation's weights into cache from a side stream
+    while the current one runs; prefetching changes timing only, never values): the layers
+    here have no attention between them, so x_l is a given input per layer.  Returns
+    layer_step's result per layer, each with "out_stored" (its output after rounding).
+    """
+    rnd = round_to_bf16 if out_dtype == "bf16" else round_to_f32
+    r = as_f64(r0)
+    res = []
+    for x, w in zip(xs, ws):
+        step = layer_step(x, r, w, top_k, routed_scale, norm_eps=norm_eps)
+        step["out_stored"] = rnd(step["out"])
+        res.append(step)
+        r = step["out_stored"]
+    return res

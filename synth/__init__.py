@@ -25,7 +25,7 @@ import json
 import math
 import os
 import subprocess
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -37,9 +37,11 @@ ATTEMPTS_JSON = os.path.join(_ROOT, "tests", "golden", "attempts.json")
 
 # Tensor stream ids (key1) for weights; key0 is the layer seed.
 T_WO, T_WR, T_BIAS, T_W13, T_W2, T_WS13, T_WS2, T_PERM, T_NORM = 1, 2, 3, 4, 5, 6, 7, 8, 9
-# Token streams: key0 = token seed, key1 = TOKEN_BASE + 16 * attempt + kind.
+# Token streams: key0 = token seed, key1 = TOKEN_BASE + 16 * attempt + kind (+ LAYER_STRIDE *
+# layer for the attention-output stand-in x of layer >= 1 of a chain).
 TOKEN_BASE = 0x100
 KIND_X, KIND_R = 0, 1
+LAYER_STRIDE = 0x1000
 # Speculative-verify tokens (one sequence): a component shared by all tokens, stream
 # (VERIFY_SEED, TOKEN_BASE + kind), mixed with each token's own stream as
 # sqrt(VERIFY_RHO) * shared + sqrt(1 - VERIFY_RHO) * own.
@@ -79,6 +81,7 @@ class LayerConfig:
     description: str = ""
     tokens: str = "independent"  # "independent" | "verify" (correlated tokens of one sequence)
     norm: bool = False  # RMSNorm (weight [H], eps NORM_EPS) between the residual add and experts
+    layers: int = 1  # > 1: a chain of layers, layer l with weights of layer seed layer_seed + l
 
     @property
     def wbytes(self) -> int:
@@ -115,8 +118,23 @@ CONFIGS = {
         LayerConfig("tp_norm", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8, 64), "zipf", "key",
                     description="one TP16 rank's share with RMSNorm before router and experts",
                     norm=True),
+        # chained layers carry the RMSNorm: without it the residual stream of random layers
+        # grows layer by layer until the sigmoid scores saturate
+        LayerConfig("chain_tp", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8), "zipf", "key",
+                    description="four consecutive TP16-rank layers with distinct weights, "
+                                "RMSNorm before router and experts", norm=True, layers=4),
+        LayerConfig("chain_full", 7168, 7168, 384, 8, 2048, 2048, "bf16", (1, 8), "normal",
+                    "key", description="two consecutive full-size layers with distinct weights, "
+                                       "RMSNorm before router and experts", norm=True, layers=2),
     ]
 }
+
+
+def layer_of(cfg: LayerConfig, l: int) -> LayerConfig:
+    """Layer l of a chain as a one-layer config (its own weights: layer seed + l)."""
+    if not 0 <= l < cfg.layers:
+        raise ValueError(f"{cfg.name} has {cfg.layers} layers")
+    return replace(cfg, name=f"{cfg.name}.{l}", layer_seed=cfg.layer_seed + l, layers=1)
 
 
 # ----------------------------------------------------------------------------- host library
@@ -253,8 +271,8 @@ def host_bias(cfg: LayerConfig):
     raise ValueError(cfg.bias)
 
 
-def token_key(attempt: int, kind: int) -> int:
-    return TOKEN_BASE + 16 * int(attempt) + kind
+def token_key(attempt: int, kind: int, layer: int = 0) -> int:
+    return TOKEN_BASE + LAYER_STRIDE * int(layer) + 16 * int(attempt) + kind
 
 
 def f32_to_bf16_bits(a) -> np.ndarray:
@@ -287,6 +305,25 @@ def host_token(cfg: LayerConfig, t: int, attempt: int):
              np.sqrt(1.0 - VERIFY_RHO) * own.astype(np.float64)).astype(np.float32)
         out.append(f32_to_bf16_bits(v) if cfg.dtype == "bf16" else v)
     return out[0], out[1]
+
+
+def host_chain_x(cfg: LayerConfig, l: int, t: int, attempt: int):
+    """x_l [Ko] of token seed t for layer l >= 1 of a chain (the stand-in for that layer's
+    attention output), resample attempt `attempt`."""
+    if cfg.tokens != "independent" or l < 1:
+        raise ValueError("chain inputs past layer 0 are independent per-layer draws")
+    return host_stream(cfg.oproj_in, t, token_key(attempt, KIND_X, l), ACT_SIGMA, cfg.dtype)
+
+
+def host_chain_tokens(cfg: LayerConfig, B: int, table: dict | None = None):
+    """([x_0 .. x_{L-1}] each [B][Ko], r_0 [B][H]) of a chain for token seeds 0..B-1."""
+    x0, r0 = host_tokens(cfg, B, attempts_for(cfg, B, table))
+    xs = [x0]
+    table = load_attempts() if table is None else table
+    per_layer = table["configs"][cfg.name]["layer_attempts"]
+    for l in range(1, cfg.layers):
+        xs.append(np.stack([host_chain_x(cfg, l, t, per_layer[l - 1][t]) for t in range(B)]))
+    return xs, r0
 
 
 def load_attempts(path: str = ATTEMPTS_JSON) -> dict:

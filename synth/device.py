@@ -44,6 +44,14 @@ def host_to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+def device_chain_tokens(cfg: LayerConfig, B: int, device="cuda"):
+    """([x_l device tensors], r_0 device tensor) of a chain and their host copies."""
+    from . import host_chain_tokens
+    xs, r0 = host_chain_tokens(cfg, B)
+    return ([host_to_device(x, cfg.dtype, device) for x in xs], host_to_device(r0, cfg.dtype, device),
+            xs, r0)
+
+
 def device_tokens(cfg: LayerConfig, B: int, attempts=None, device="cuda"):
     """(x [B][Ko], r [B][H]) device tensors and their host bits/values."""
     x, r = host_tokens(cfg, B, attempts)

@@ -419,3 +419,62 @@ def test_norm_layer_scale_invariance():
     np.testing.assert_array_equal(a["topk_idx"], b["topk_idx"])
     np.testing.assert_allclose(b["h"], 4.0 * a["h"], rtol=1e-14)
     np.testing.assert_allclose(b["out"] - b["h"], a["out"] - a["h"], rtol=1e-11, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- chained layers
+def test_round_to_bf16_hand_values_and_bit_rounding():
+    """Ties go to the even significand; values agree with an independent bit-level RNE of
+    fp32 inputs (synth's converter); overflow past the largest bf16 gives inf."""
+    import synth
+    v = np.array([1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -(1.0 + 2.0**-8 + 2.0**-30), 3.0, 0.0,
+                  2.0**-133 * 0.5, 2.0**-133 * 1.5, 3.4e38])
+    want = [1.0, 1.0 + 2.0**-6, -(1.0 + 2.0**-7), 3.0, 0.0, 0.0, 2.0**-132, np.inf]
+    assert O.round_to_bf16(v).tolist() == want
+    rng = np.random.default_rng(50)
+    a = (rng.normal(size=20000) * np.exp(rng.uniform(-60, 60, 20000))).astype(np.float32)
+    ref = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(a)).astype(np.float64)
+    np.testing.assert_array_equal(O.round_to_bf16(a.astype(np.float64)), ref)
+
+
+def test_chain_of_one_is_the_layer_and_rounds_its_output():
+    rng = np.random.default_rng(51)
+    H, E, k, I = 16, 8, 2, 6
+    w, _, _ = _rand_weights(H, H, E, I, I, rng)
+    x, r = rng.normal(size=(2, H)), rng.normal(size=(2, H))
+    one = O.layer_step(x, r, w, k)
+    ch = O.chain_step([x], r, [w], k, "bf16")
+    np.testing.assert_array_equal(ch[0]["out"], one["out"])
+    np.testing.assert_array_equal(ch[0]["out_stored"], O.round_to_bf16(one["out"]))
+    assert not np.array_equal(ch[0]["out_stored"], one["out"])
+
+
+def test_chain_without_experts_accumulates_projections():
+    """All expert weights 0: each layer adds only its projection, so the stored stream after
+    layer l is the rounded running sum r + x_0 W_0^T + ... in that order."""
+    rng = np.random.default_rng(52)
+    H, E, k, I, L = 12, 6, 2, 4, 3
+    ws, xs = [], []
+    for _ in range(L):
+        w, _, _ = _rand_weights(H, H, E, I, I, rng)
+        z13, z2 = np.zeros((2 * I, H)), np.zeros((H, I))
+        ws.append(O.LayerWeights(w.w_o, w.w_r, w.bias, lambda e, a=z13, b=z2: (a, b),
+                                 np.zeros((2 * I, H)), np.zeros((H, I))))
+        xs.append(rng.normal(size=(3, H)))
+    r0 = rng.normal(size=(3, H))
+    res = O.chain_step(xs, r0, ws, k, "bf16")
+    r = r0
+    for l in range(L):
+        r = O.round_to_bf16(r + xs[l] @ ws[l].w_o.T)
+        np.testing.assert_allclose(res[l]["out_stored"], r, rtol=0, atol=0)
+
+
+def test_chain_feeds_each_layer_the_previous_stored_output():
+    rng = np.random.default_rng(53)
+    H, E, k, I = 16, 8, 2, 6
+    w0, _, _ = _rand_weights(H, H, E, I, I, rng)
+    w1, _, _ = _rand_weights(H, H, E, I, I, rng)
+    x0, x1, r0 = rng.normal(size=(2, H)), rng.normal(size=(2, H)), rng.normal(size=(2, H))
+    ch = O.chain_step([x0, x1], r0, [w0, w1], k, "f32")
+    second = O.layer_step(x1, O.round_to_f32(O.layer_step(x0, r0, w0, k)["out"]), w1, k)
+    np.testing.assert_array_equal(ch[1]["out"], second["out"])
+    np.testing.assert_array_equal(ch[1]["topk_idx"], second["topk_idx"])
