@@ -170,6 +170,58 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
     return out
 
 
+def chain_sweep(main_cfg, main_w, args, s, flush) -> dict:
+    """Consecutive layers with distinct weights (kk_chain_decode), eager, with and without the
+    next layer's weight prefetch on the auxiliary stream: us per chained step and per layer."""
+    import torch
+
+    import synth
+    import synth.device as sd
+    from moe_layer_skinny_amd import kk
+
+    out = {}
+    for name, B in (("chain_full", 1), ("chain_tp", 1), ("chain_tp", 8)):
+        cfg = synth.CONFIGS[name]
+        layers, keep = [], []
+        for l in range(cfg.layers):
+            lc = synth.layer_of(cfg, l)
+            same = (lc.hidden, lc.oproj_in, lc.inter, lc.layer_seed) == (
+                main_cfg.hidden, main_cfg.oproj_in, main_cfg.inter, main_cfg.layer_seed)
+            w = sd.device_weights(lc, share_from=main_w if same else None)
+            keep.append(w)
+            layers.append(kk.Layer(kk.make_config(lc.hidden, lc.oproj_in, lc.n_experts, lc.top_k,
+                                                  lc.inter, lc.shared_inter, lc.dtype,
+                                                  norm_eps=synth.NORM_EPS), w, B))
+        xs, r0, _, _ = sd.device_chain_tokens(cfg, B)
+        outs = [torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda") for _ in layers]
+        ws = layers[0].new_workspace()
+        for prefetch in (False, True):
+            with torch.cuda.stream(s):
+                for _ in range(max(2, args.warmup)):
+                    flush.add_(1.0)
+                    kk.chain_decode(layers, B, xs, r0, outs, ws, stream=s, prefetch=prefetch)
+            s.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            with torch.cuda.stream(s):
+                for a, b in evs:
+                    flush.add_(1.0)
+                    a.record(s)
+                    kk.chain_decode(layers, B, xs, r0, outs, ws, stream=s, prefetch=prefetch)
+                    b.record(s)
+            s.synchronize()
+            us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
+            key = f"{name}@{B}" + ("+prefetch" if prefetch else "")
+            out[key] = {"layers": cfg.layers, "us_per_step": round(us, 3),
+                        "us_per_layer": round(us / cfg.layers, 3)}
+            log(f"[bench] {key}: {out[key]}")
+        for layer in layers:
+            layer.close()
+        del keep
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +392,7 @@ def main():
         del src, dst
     if not args.no_sweep:
         res["batch_sweep"] = sweep(cfg, w, args, s, flush)
+        res["chain_sweep"] = chain_sweep(cfg, w, args, s, flush)
     if not args.no_cpu:
         log("[bench] timing the oracle on the host cores")
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_reps)

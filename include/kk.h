@@ -73,6 +73,9 @@ typedef enum {
 #define KK_GRAPH 1u      /* capture the step once per (B, buffers, stream, flags), replay it */
 #define KK_TWO_STREAM 2u /* shared expert's gate/up on the context's auxiliary stream instead
                             of inside the top-k launch (kept for comparison) */
+#define KK_PREFETCH 4u   /* kk_chain_decode: after layer l's o-proj, the first context's
+                            auxiliary stream reads layer l+1's o-proj, router and shared gate/up
+                            weights once, so that layer finds them in the memory-side cache */
 
 typedef struct {
   int32_t hidden;       /* H  */
@@ -156,6 +159,19 @@ kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* res
                           int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
                           uint32_t flags);
 
+/* Consecutive layers, each with its own context and weights: layer l reads x[l] [B][Ko] and the
+ * residual stream r_l (resid for l = 0, out[l-1] after it) and writes out[l] [B][H]; every
+ * layer's output is kept.  All L contexts must have the same kk_config, max_batch >= B and
+ * the current device; ws (kk_workspace_bytes of the largest max_batch among them) is used by
+ * the layers in turn.  x, out: host arrays of L device pointers; no out[l] may overlap an
+ * x[j], resid or another out.  Flags: KK_GRAPH (the whole chain is captured once per
+ * (contexts, B, pointers, stream, flags) and replayed; the graphs are kept by ctx[0]) and
+ * KK_PREFETCH.  "What's Optimized" (a side kernel preloads the next operation's weights into
+ * cache) and "Recovering time between operators" (an auxiliary stream loads weights before
+ * their consumer starts, in the idle intervals of the current work). */
+kk_status kk_chain_decode(kk_ctx* const* ctx, int32_t L, int32_t B, const void* const* x,
+                          const void* resid, void* const* out, void* ws, kk_stream stream,
+                          uint32_t flags);
 /* Per-kernel timing of eager (non-graph) launches: when enabled, every kernel the context
  * launches is bracketed by HIP events on its own stream.  kk_read_kernel_timing waits for
  * the recorded events and returns up to `cap` (name, milliseconds) records of the launches

@@ -8,6 +8,7 @@
 // visible to callers and tests: no silent fallback to another implementation).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -131,11 +132,11 @@ const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_log
                               "down_combine_gemv", "moe_prep",    "combine",    "oproj_mfma",
                               "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
                               "topk_rows",   "tables", "topk_tables", "oproj_reduce_norm",
-                              "norm_rows"};
+                              "norm_rows", "prefetch"};
 enum KName {
   K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
   K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
-  K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS
+  K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS, K_PREFETCH
 };
 
 struct TimingRec {
@@ -152,9 +153,19 @@ struct GraphEntry {
   unsigned long long uses;
 };
 
+// A captured chain of layers (kept by its first context).
+struct ChainGraph {
+  std::vector<uintptr_t> key;  // context serials, x[], out[], resid, ws, stream
+  int B;
+  uint32_t flags;
+  hipGraphExec_t exec;
+  unsigned long long uses;
+};
+
 }  // namespace
 
 struct kk_ctx {
+  unsigned long long serial;  // never reused: chain graphs of other contexts key on it
   kk_config cfg;
   kk::Shape shape;
   kk::Weights w;
@@ -166,6 +177,7 @@ struct kk_ctx {
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   std::vector<GraphEntry> graphs;
+  std::vector<ChainGraph> chains;
   unsigned long long clock = 0;
   bool timing = false;
   std::vector<TimingRec> trecs;
@@ -448,13 +460,42 @@ kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const k
   return KK_OK;
 }
 
+// Prefetch of the next layer's first weights on `owner`'s auxiliary stream, forked from s
+// after this layer's o-proj (the join is left to the caller).
+struct PrefetchNext {
+  kk_ctx* owner;
+  const kk_ctx* next;
+};
+
+kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
+  kk_ctx* o = pf.owner;
+  const kk::Shape& sh = pf.next->shape;
+  const size_t eb = sh.dtype == 1 ? 2 : 4;
+  KK_HIP(hipEventRecord(o->ev_fork, s), "prefetch fork event");
+  KK_HIP(hipStreamWaitEvent(o->aux, o->ev_fork, 0), "prefetch fork wait");
+  const struct {
+    const void* p;
+    size_t bytes;
+  } parts[] = {{pf.next->w.w_o, eb * sh.H * sh.Ko},
+               {pf.next->w.w_r, eb * sh.E * sh.H},
+               {pf.next->w.ws13, eb * 2 * sh.Is * sh.H}};
+  for (const auto& q : parts)
+    KK_HIP(timed(o, K_PREFETCH, o->aux,
+                 [&] { return kk::launch_prefetch(o->dev, q.p, q.bytes, o->aux); }),
+           "prefetch launch");
+  KK_HIP(hipEventRecord(o->ev_join, o->aux), "prefetch join event");
+  return KK_OK;
+}
+
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
-                        float* gate, void* ws, hipStream_t s, bool two_stream, int path) {
+                        float* gate, void* ws, hipStream_t s, bool two_stream, int path,
+                        const PrefetchNext* pf = nullptr) {
   WsPtrs p = carve(c, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act};
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
+  if (pf && (st = enqueue_prefetch(*pf, s)) != KK_OK) return st;
   if (path == KK_PATH_SPLITK_MFMA) {
     const float* u = c->norm.gamma ? p.u32 : p.h32;
     st = enqueue_router_mfma(c, B, u, rt, p.logit_part, s);
@@ -483,6 +524,25 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
 void destroy_graphs(kk_ctx* c) {
   for (auto& g : c->graphs) (void)hipGraphExecDestroy(g.exec);
   c->graphs.clear();
+  for (auto& g : c->chains) (void)hipGraphExecDestroy(g.exec);
+  c->chains.clear();
+}
+
+// The layers in order on s; with prefetch, each layer but the last forks the next layer's
+// weight prefetch after its o-proj, and s joins the auxiliary stream at the end.
+kk_status enqueue_chain(kk_ctx* const* ctx, int L, int B, const void* const* x, const void* resid,
+                        void* const* out, void* ws, hipStream_t s, bool prefetch) {
+  for (int l = 0; l < L; ++l) {
+    kk_plan plan;
+    kk_status st = plan_for(ctx[l], B, &plan);
+    if (st != KK_OK) return st;
+    const PrefetchNext pf{ctx[0], l + 1 < L ? ctx[l + 1] : nullptr};
+    st = enqueue_layer(ctx[l], B, x[l], l == 0 ? resid : out[l - 1], out[l], nullptr, nullptr, ws,
+                       s, false, plan.path, prefetch && l + 1 < L ? &pf : nullptr);
+    if (st != KK_OK) return st;
+  }
+  if (prefetch && L > 1) KK_HIP(hipStreamWaitEvent(s, ctx[0]->ev_join, 0), "prefetch join wait");
+  return KK_OK;
 }
 
 }  // namespace
@@ -531,7 +591,9 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     KK_PTR(w->ws2, "ws2");
     if (w->norm_weight && misaligned(w->norm_weight))
       return fail(KK_ERR_INVALID_ARG, "norm_weight is not 16-byte aligned");
+    static std::atomic<unsigned long long> serials{0};
     kk_ctx* c = new kk_ctx();
+    c->serial = ++serials;
     c->cfg = *cfg;
     c->shape = to_shape(*cfg);
     c->w = kk::Weights{w->w_o, w->w_r, w->router_bias, w->w13, w->w2, w->ws13, w->ws2};
@@ -727,6 +789,74 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     return KK_OK;
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_layer_decode");
+  }
+}
+
+kk_status kk_chain_decode(kk_ctx* const* ctx, int32_t L, int32_t B, const void* const* x,
+                          const void* resid, void* const* out, void* ws, kk_stream stream,
+                          uint32_t flags) {
+  try {
+    if (!ctx || !x || !out) return fail(KK_ERR_INVALID_ARG, "ctx, x and out arrays must be non-NULL");
+    if (L < 1 || L > 1024) return fail(KK_ERR_INVALID_ARG, "layer count %d outside 1..1024", L);
+    if (flags & ~(KK_GRAPH | KK_PREFETCH))
+      return fail(KK_ERR_INVALID_ARG, "unknown flags 0x%x for a chain", flags);
+    KK_PTR(resid, "resid");
+    for (int l = 0; l < L; ++l) {
+      kk_status st = check_common(ctx[l], B, ws);
+      if (st != KK_OK) return st;
+      if (std::memcmp(&ctx[l]->cfg, &ctx[0]->cfg, sizeof(kk_config)) != 0)
+        return fail(KK_ERR_INVALID_ARG, "context %d has another kk_config than context 0", l);
+      for (int j = 0; j < l; ++j)
+        if (ctx[j] == ctx[l]) return fail(KK_ERR_INVALID_ARG, "context %d repeats context %d", l, j);
+      KK_PTR(x[l], "x[l]");
+      KK_PTR(out[l], "out[l]");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const bool prefetch = (flags & KK_PREFETCH) != 0;
+    if (!(flags & KK_GRAPH)) return enqueue_chain(ctx, L, B, x, resid, out, ws, s, prefetch);
+    if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
+    kk_ctx* c0 = ctx[0];
+    std::vector<uintptr_t> key;
+    key.reserve(3 * L + 3);
+    for (int l = 0; l < L; ++l) key.push_back((uintptr_t)ctx[l]->serial);
+    for (int l = 0; l < L; ++l) key.push_back((uintptr_t)x[l]);
+    for (int l = 0; l < L; ++l) key.push_back((uintptr_t)out[l]);
+    key.push_back((uintptr_t)resid);
+    key.push_back((uintptr_t)ws);
+    key.push_back((uintptr_t)s);
+    ++c0->clock;
+    for (auto& g : c0->chains) {
+      if (g.B == B && g.flags == flags && g.key == key) {
+        g.uses = c0->clock;
+        KK_HIP(hipGraphLaunch(g.exec, s), "chain graph launch");
+        return KK_OK;
+      }
+    }
+    if (c0->chains.size() >= 8) {  // evict the least recently used chain graph
+      size_t lru = 0;
+      for (size_t i = 1; i < c0->chains.size(); ++i)
+        if (c0->chains[i].uses < c0->chains[lru].uses) lru = i;
+      (void)hipGraphExecDestroy(c0->chains[lru].exec);
+      c0->chains.erase(c0->chains.begin() + lru);
+    }
+    KK_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "begin capture");
+    kk_status st = enqueue_chain(ctx, L, B, x, resid, out, ws, s, prefetch);
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &graph);
+    if (st != KK_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return st;
+    }
+    if (e != hipSuccess) return hip_fail(e, "end capture");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+    c0->chains.push_back(ChainGraph{std::move(key), B, flags, exec, c0->clock});
+    KK_HIP(hipGraphLaunch(exec, s), "chain graph launch");
+    return KK_OK;
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_chain_decode");
   }
 }
 

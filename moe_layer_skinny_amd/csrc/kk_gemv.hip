@@ -403,6 +403,19 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   if (shared) shared_rows<T, CPRH, NT>(ws13, Is, 0, Is, gw, nw, wg, wu, lds, k, B, rt, As, lane);
 }
 
+// ------------------------------------------------------------------------------ prefetch
+// Reads n 16-byte chunks once with plain loads, which allocate in the caches on their way, and
+// keeps nothing: a later launch that reads the same bytes is served from the memory-side cache.
+__global__ __launch_bounds__(256) void prefetch_kernel(const u32x4* __restrict__ p, size_t n) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const u32x4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  asm volatile("" ::"v"(acc));  // the loads stay; nothing is stored
+}
+
 // ------------------------------------------------------------------------------ top-k, large batch
 // One wave per token (grid = B): topk_idx / topk_gate rows.
 __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ part, int splits,
@@ -1136,6 +1149,14 @@ hipError_t launch_topk_tables(const Shape& s, int B, const float* part, int spli
 
 hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t st) {
   hipLaunchKernelGGL(tables_kernel, dim3(1), dim3(256), 0, st, s.E, s.k, B, rt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStream_t st) {
+  if (bytes % 16) return hipErrorInvalidValue;
+  if (!bytes) return hipSuccess;
+  hipLaunchKernelGGL(prefetch_kernel, dim3(d.num_cu), dim3(256), 0, st, (const u32x4*)p,
+                     bytes / 16);
   return hipGetLastError();
 }
 

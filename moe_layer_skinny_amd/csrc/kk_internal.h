@@ -102,6 +102,9 @@ hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t s
 hipError_t launch_topk_tables(const Shape& s, int B, const float* part, int splits,
                               const float* bias, const Routing& rt, hipStream_t st);
 
+// Reads `bytes` (a multiple of 16) at p once with cache-allocating loads and discards them.
+hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStream_t st);
+
 // act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
 

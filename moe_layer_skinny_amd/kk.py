@@ -19,6 +19,7 @@ KK_F32, KK_BF16 = 0, 1
 KK_PATH_GEMV, KK_PATH_SPLITK_MFMA = 0, 1
 KK_GRAPH = 1
 KK_TWO_STREAM = 2
+KK_PREFETCH = 4
 PATH_NAMES = {KK_PATH_GEMV: "gemv", KK_PATH_SPLITK_MFMA: "splitk_mfma"}
 
 
@@ -69,6 +70,8 @@ def lib():
             "kk_router_topk": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "kk_moe_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kk_layer_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, u32]),
+            "kk_chain_decode": (i32, [ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp), vp,
+                                      ctypes.POINTER(vp), vp, vp, u32]),
             "kk_set_kernel_timing": (i32, [vp, i32]),
             "kk_read_kernel_timing": (i32, [vp, ctypes.POINTER(ctypes.c_char_p),
                                             ctypes.POINTER(ctypes.c_float), i32,
@@ -196,3 +199,16 @@ class Layer:
         n = ctypes.c_int32()
         _check(lib().kk_read_kernel_timing(self._h, names, ms, cap, ctypes.byref(n)))
         return [(names[i].decode(), ms[i]) for i in range(min(n.value, cap))]
+
+
+def chain_decode(layers, B, xs, resid, outs, ws, stream=None, graph=False, prefetch=False):
+    """kk_chain_decode over Layer objects: layer l reads xs[l] and the previous layer's output
+    (resid for the first) and writes outs[l]."""
+    n = len(layers)
+    if not (len(xs) == len(outs) == n):
+        raise ValueError("one x and one out per layer")
+    ctxs = (ctypes.c_void_p * n)(*[layer._h.value for layer in layers])
+    xa = (ctypes.c_void_p * n)(*[t.data_ptr() for t in xs])
+    oa = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    flags = (KK_GRAPH if graph else 0) | (KK_PREFETCH if prefetch else 0)
+    _check(lib().kk_chain_decode(ctxs, n, B, xa, _ptr(resid), oa, _ptr(ws), _stream(stream), flags))

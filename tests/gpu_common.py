@@ -31,13 +31,14 @@ def torch_mod():
     return torch
 
 
-def gpu_layer(name: str):
-    """(cfg, weights dict, kk.Layer) for a workload; full-size workloads share weights."""
+def gpu_layer(name: str, cfg=None):
+    """(cfg, weights dict, kk.Layer) for a workload (or a given one-layer config under `name`);
+    workloads with the same shapes and layer seed share weight tensors."""
     if name in _layers:
         return _layers[name]
     import synth.device as sd
     from moe_layer_skinny_amd import kk
-    cfg = synth.CONFIGS[name]
+    cfg = synth.CONFIGS[name] if cfg is None else cfg
     share = None
     for other, (ocfg, ow, _) in _layers.items():
         if (ocfg.hidden, ocfg.oproj_in, ocfg.n_experts, ocfg.inter, ocfg.dtype, ocfg.layer_seed) == (
@@ -101,3 +102,29 @@ def assert_routing_equal(got: dict, ref: dict, B: int, k: int, what: str) -> Non
         np.testing.assert_array_equal(got["offsets"], ref["offsets"], err_msg=f"{what}: offsets")
     if "perm" in got:
         np.testing.assert_array_equal(got["perm"], ref["perm"], err_msg=f"{what}: perm")
+
+
+def gpu_chain(name: str):
+    """(chain cfg, [kk.Layer per layer]) for a chain workload; layer l is registered as
+    "<name>.<l>" (its own weights, layer seed + l)."""
+    cfg = synth.CONFIGS[name]
+    layers = []
+    for l in range(cfg.layers):
+        lc = synth.layer_of(cfg, l)
+        lc = synth.replace(lc, batches=cfg.batches)
+        layers.append(gpu_layer(lc.name, lc)[2])
+    return cfg, layers
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_chain(name: str, B: int) -> list:
+    cfg = synth.CONFIGS[name]
+    xs, r0 = synth.host_chain_tokens(cfg, B)
+    ws = []
+    for l in range(cfg.layers):
+        lc = synth.layer_of(cfg, l)
+        ws.append(O.LayerWeights(synth.host_weight(lc, "w_o"), synth.host_weight(lc, "w_r"),
+                                 synth.host_bias(lc), lambda e, lc=lc: synth.host_expert(lc, e),
+                                 synth.host_weight(lc, "ws13"), synth.host_weight(lc, "ws2"),
+                                 norm_weight=synth.host_norm_weight(lc)))
+    return O.chain_step(xs, r0, ws, cfg.top_k, cfg.dtype, norm_eps=synth.NORM_EPS)

@@ -124,3 +124,9 @@ def _header_struct_fields(name: str) -> list[str]:
 def test_binding_structs_match_header(cname, pystruct):
     """The ctypes structures list the header's fields in the header's order."""
     assert [f for f, _ in pystruct._fields_] == _header_struct_fields(cname)
+
+
+def test_chain_rejects_null_arrays_without_device():
+    L = kk.lib()
+    assert L.kk_chain_decode(None, 1, 1, None, None, None, None, None, 0) == kk.KK_ERR_INVALID_ARG
+    assert kk.last_error()
