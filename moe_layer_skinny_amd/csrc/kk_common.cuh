@@ -190,17 +190,26 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Maximum of v over the 64 lanes, returned to every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));
-  v = max_u64(v, dpp_u64<0x4E>(v));
-  v = max_u64(v, dpp_u64<0x141>(v));
-  v = max_u64(v, dpp_u64<0x140>(v));
-  v = max_u64(v, dpp_u64<0x142, 0xA>(v));
-  v = max_u64(v, dpp_u64<0x143, 0xC>(v));
-  return readlane_u64(v, 63);
+// Maximum of v over the 64 lanes, returned to every lane: each step is one DPP-fed max
+// (lanes outside a step's rows combine with 0, the identity); lane 63 ends with the total.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Maximum of a 64-bit v over the 64 lanes in two 32-bit passes: the high words first, then
+// the low words of the lanes that hold the maximal high word.
+__device__ __forceinline__ uint64_t wave_max_u64_2pass(uint64_t v) {
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // Sum of v over the 64 lanes in a fixed combining order, returned to every lane.

@@ -33,36 +33,55 @@ __device__ __forceinline__ uint64_t rank_key(double key, int e) {
   return (u & ~0x1FFull) | (uint64_t)(511 - e);
 }
 
-// One token's selection on one wave from its logits (lane l holds experts l + 64 m in
-// l_[m]): sigmoid scores, fp64 keys, k rounds of wave arg-max, renormalised gates;
-// topk_idx / topk_gate rows written in ascending expert order, and the selected experts
-// returned through sel (nullable).
+// One token's selection on one wave from its logits and the bias (lane l holds expert
+// l + 64 m in l_[m] and bv[m]): sigmoid scores, fp64 keys, then k rounds of wave arg-max,
+// renormalised gates; topk_idx / topk_gate rows written in ascending expert order, and the
+// selected experts returned through sel (nullable).  Each lane sorts its packed keys once
+// (descending), so a round reduces only the lanes' heads and the winner pops its own.
 constexpr int kMaxM = kMaxExperts / 64;
-__device__ inline void topk_select(const float (&l_)[kMaxM], const float* __restrict__ bias, int E,
-                                   int k, float routed_scale, int t, const Routing& rt, int* sel) {
+__device__ inline void topk_select(const float (&l_)[kMaxM], const float (&bv)[kMaxM], int E, int k,
+                                   float routed_scale, int t, const Routing& rt, int* sel) {
   const int lane = threadIdx.x & 63;
-  float bv[kMaxM];
-#pragma unroll
-  for (int m = 0; m < kMaxM; ++m) bv[m] = bias[min(lane + 64 * m, E - 1)];
   double sc[kMaxM];
   uint64_t rk[kMaxM];
 #pragma unroll
   for (int m = 0; m < kMaxM; ++m) {
-    const int e = lane + 64 * m;
-    const double sv = 1.0 / (1.0 + exp(-(double)l_[m]));
-    sc[m] = sv;
-    rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
+    sc[m] = 0.0;
+    rk[m] = 0ull;
+    if (64 * m < E) {  // uniform: slots past the last expert cost nothing
+      const int e = lane + 64 * m;
+      const double sv = 1.0 / (1.0 + exp(-(double)l_[m]));
+      sc[m] = sv;
+      rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
+    }
   }
-  // k rounds of wave arg-max on the packed keys; the winner's entry drops out
+  // per-lane sort, descending (19-comparator odd-even merge network over 8 keys)
+  uint64_t sk[kMaxM];
+#pragma unroll
+  for (int m = 0; m < kMaxM; ++m) sk[m] = rk[m];
+  static_assert(kMaxM == 8, "the sorting network is written for 8 keys per lane");
+  auto ce = [&](int i, int j) {
+    const uint64_t a = sk[i], b = sk[j];
+    const bool sw = b > a;
+    sk[i] = sw ? b : a;
+    sk[j] = sw ? a : b;
+  };
+  ce(0, 1); ce(2, 3); ce(4, 5); ce(6, 7);
+  ce(0, 2); ce(1, 3); ce(4, 6); ce(5, 7);
+  ce(1, 2); ce(5, 6);
+  ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
+  ce(2, 4); ce(3, 5);
+  ce(1, 2); ce(3, 4); ce(5, 6);
+  // k rounds: the wave maximum of the heads wins; its lane drops it
   uint32_t selmask = 0;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int m = 0; m < kMaxM; ++m)
-      if (!((selmask >> m) & 1u)) best = max_u64(best, rk[m]);
-    best = wave_max_u64(best);
+    const uint64_t best = wave_max_u64_2pass(sk[0]);
     const int win = 511 - (int)(best & 0x1FFull);
-    if ((win & 63) == lane) selmask |= 1u << (win >> 6);
+    const bool mine = (win & 63) == lane;
+    if (mine) selmask |= 1u << (win >> 6);
+#pragma unroll
+    for (int m = 0; m < kMaxM - 1; ++m) sk[m] = mine ? sk[m + 1] : sk[m];
+    sk[kMaxM - 1] = mine ? 0ull : sk[kMaxM - 1];
   }
   double ssum = 0.0;
 #pragma unroll
@@ -85,22 +104,31 @@ __device__ inline void topk_select(const float (&l_)[kMaxM], const float* __rest
   }
 }
 
+// The bias of this lane's experts (lane l: expert l + 64 m), clamped loads.
+__device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E, float (&bv)[kMaxM]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 0; m < kMaxM; ++m) bv[m] = bias[min(lane + 64 * m, E - 1)];
+}
+
 // One token's top-k on one wave from logit partials part[splits][B][E] (splits <=
-// kMaxTopkSplits), summed in slice order.  All global loads are issued before any is used
-// (addresses clamped instead of branched around, so nothing waits on a join).
+// kMaxTopkSplits), summed in slice order.  All global loads (partials and bias) are issued
+// before any is used (addresses clamped instead of branched around, so nothing waits on a
+// join).
 constexpr int kMaxTopkSplits = 8;
 __device__ inline void topk_row(const float* part, int splits, const float* __restrict__ bias,
                                 int B, int E, int k, float routed_scale, int t, const Routing& rt,
                                 int* sel) {
   constexpr int MAXS = kMaxTopkSplits;
   const int lane = threadIdx.x & 63;
-  float pv[kMaxM][MAXS];
+  float pv[kMaxM][MAXS], bv[kMaxM];
 #pragma unroll
   for (int m = 0; m < kMaxM; ++m) {
     const int ec = min(lane + 64 * m, E - 1);
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) pv[m][s] = part[((size_t)min(s, splits - 1) * B + t) * E + ec];
   }
+  load_bias(bias, E, bv);
   float l_[kMaxM];
 #pragma unroll
   for (int m = 0; m < kMaxM; ++m) {
@@ -109,7 +137,7 @@ __device__ inline void topk_row(const float* part, int splits, const float* __re
     for (int s = 0; s < MAXS; ++s) l += s < splits ? pv[m][s] : 0.f;
     l_[m] = l;
   }
-  topk_select(l_, bias, E, k, routed_scale, t, rt, sel);
+  topk_select(l_, bv, E, k, routed_scale, t, rt, sel);
 }
 
 // Block-wide: logits lg[t * E + e] of all B tokens summed from part[splits][B][E] in slice
@@ -139,14 +167,14 @@ __device__ inline void logits_to_lds(const float* part, int splits, int B, int E
   }
 }
 
-// One token's top-k on one wave from its logits in LDS.
-__device__ inline void topk_row_lds(const float* lg, const float* __restrict__ bias, int E, int k,
+// One token's top-k on one wave from its logits in LDS; bv holds the lane's bias values.
+__device__ inline void topk_row_lds(const float* lg, const float (&bv)[kMaxM], int E, int k,
                                     float routed_scale, int t, const Routing& rt, int* sel) {
   const int lane = threadIdx.x & 63;
   float l_[kMaxM];
 #pragma unroll
   for (int m = 0; m < kMaxM; ++m) l_[m] = lg[t * E + min(lane + 64 * m, E - 1)];
-  topk_select(l_, bias, E, k, routed_scale, t, rt, sel);
+  topk_select(l_, bv, E, k, routed_scale, t, rt, sel);
 }
 
 // Routing tables from the selected experts of all B tokens (sm.sel filled, block-wide):
