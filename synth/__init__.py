@@ -118,6 +118,9 @@ CONFIGS = {
         LayerConfig("tp_norm", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8, 64), "zipf", "key",
                     description="one TP16 rank's share with RMSNorm before router and experts",
                     norm=True),
+        LayerConfig("tp_max", 7168, 448, 512, 16, 128, 128, "bf16", (1, 2, 64), "zipf", "key",
+                    description="the largest routing the kernels take: 512 experts, top-16, "
+                                "up to 64 tokens (1024 slots), TP16-rank expert shapes"),
         # chained layers carry the RMSNorm: without it the residual stream of random layers
         # grows layer by layer until the sigmoid scores saturate
         LayerConfig("chain_tp", 7168, 448, 384, 8, 128, 128, "bf16", (1, 2, 8), "zipf", "key",

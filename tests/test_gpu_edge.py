@@ -85,3 +85,38 @@ def test_zero_experts_leave_the_residual_stream(name, B):
         torch.cuda.empty_cache()
     assert torch.equal(out, h_out)
     assert (idx.cpu().numpy() >= 0).all()
+
+
+MAX_CASES = [("tp_max", 1), ("tp_max", 2), ("tp_max", 64)]
+
+
+@pytest.mark.parametrize("name,B", MAX_CASES)
+def test_largest_routing(name, B):
+    """512 experts, top-16 and 64 tokens (1024 slots): the routing-table and on-chip limits of
+    both paths, through the whole step and through the three ops on their own."""
+    log(f"[max] {name} B={B}")
+    import torch
+    import synth.device as sd
+    from tests.gpu_common import assert_routing_equal, oracle_step
+    cfg, _, L = gpu_layer(name)
+    assert (cfg.n_experts, cfg.top_k) == (512, 16)
+    ref = oracle_step(name, B)
+    out, idx, gate, _ = _run(L, cfg, B)
+    rep = assert_close(as_f64_out(out), ref["out"], "layer out")
+    assert_routing_equal({"topk_idx": idx.cpu().numpy(), "topk_gate": gate.cpu().numpy()}, ref, B,
+                         cfg.top_k, "layer routing")
+    log(f"[max] {name} B={B} layer: {rep}")
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    h32 = torch.empty(B, cfg.hidden, dtype=torch.float32, device="cuda")
+    offsets = torch.full((cfg.n_experts + 1,), -1, dtype=torch.int32, device="cuda")
+    perm = torch.full((B * cfg.top_k,), -1, dtype=torch.int32, device="cuda")
+    out2 = torch.empty_like(out)
+    ws = L.new_workspace()
+    L.oproj_residual(B, x, r, h32, ws)
+    L.router_topk(B, h32, idx, gate, offsets, perm, ws)
+    L.moe_decode(B, h32, idx, gate, offsets, perm, out2, ws)
+    torch.cuda.synchronize()
+    assert_routing_equal({"topk_idx": idx.cpu().numpy(), "topk_gate": gate.cpu().numpy(),
+                          "offsets": offsets.cpu().numpy(), "perm": perm.cpu().numpy()}, ref, B,
+                         cfg.top_k, "router tables")
+    assert_close(as_f64_out(out2), ref["out"], "moe out")
