@@ -252,7 +252,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     else if (MODE == 1)
       src = shared ? jj : p0 + jj;
     else
-      src = jj;
+      src = p0 + jj;
     const void* base = (MODE == 1 && shared) ? (const void*)x.act_shared : x.act_routed;
     const size_t off = (size_t)src * K + kbase + ch * 8;
     asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
@@ -382,7 +382,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       }
       float* o;
       if (MODE == 2)
-        o = outp + ((size_t)chunk * x.B + j) * out_rows + row0 + 4 * gg;
+        o = outp + ((size_t)chunk * x.B + p0 + j) * out_rows + row0 + 4 * gg;
       else
         o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
       if (MODE == 0) {
@@ -452,6 +452,24 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   }
 }
 
+// Split-K product with the tokens split as well: units (row tile, K chunk, 16-token quarter),
+// so that a launch over many tokens but few row tiles (the router: 12 row tiles x 7 chunks)
+// still fills the chip.  A unit's weights are read once per quarter (the later reads are
+// served by the caches); the quarters of one (tile, chunk) are consecutive units.
+template <int KS, int NTERM, bool BF16SRC>
+__global__ __launch_bounds__(256) void mfma_token_split_kernel(UnitArgs x) {
+  extern __shared__ u32x4 lds[];
+  const int tiles = x.N / 32, nq = (x.B + 15) / 16;
+  const int units = tiles * x.chunks * nq;
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int q = unit % nq, rest = unit / nq;
+    const int tile = rest / x.chunks, chunk = rest - tile * x.chunks;
+    const int p0 = 16 * q;
+    staged_unit<2, 1, KS, NTERM, BF16SRC, 1>(x, lds, tile, chunk, p0, min(16, x.B - p0), x.w_routed,
+                                             false);
+  }
+}
+
 // Grouped launch (gate/up or down) for batches over 16 tokens: groups of more than 16 tokens
 // (the shared expert, and any routed expert that hot) use TTB-wide token tiles, the rest one
 // tile, in the same launch; the groups are walked from the last (the shared expert) down, so
@@ -506,6 +524,17 @@ hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream
   if (lds > 64 * 1024) allow_lds_mfma(kern);
   static thread_local int bpc = 0;
   hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, max_units, &bpc)), dim3(256), lds, st, x);
+  return hipGetLastError();
+}
+
+template <int KS, int NTERM, bool BF16SRC>
+hipError_t token_split_t(const Device& d, const UnitArgs& x, hipStream_t st) {
+  auto kern = mfma_token_split_kernel<KS, NTERM, BF16SRC>;
+  constexpr size_t lds = staged_lds(1, KS, NTERM);
+  if (lds > 64 * 1024) allow_lds_mfma(kern);
+  static thread_local int bpc = 0;
+  const int units = (x.N / 32) * x.chunks * ((x.B + 15) / 16);
+  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, x);
   return hipGetLastError();
 }
 
@@ -609,6 +638,8 @@ hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const floa
   a.N = s.E;
   a.K = s.H;
   a.chunks = mfma_router_splits(s);  // 7 x 1024 k
+  // over 16 tokens the 12 x 7 (row tile, chunk) units alone would leave most of the chip idle
+  if (B > 16) return token_split_t<256, 3, false>(d, a, st);
   return staged_dispatch<2, 3, false>(d, a, (s.E / 32) * a.chunks, st);
 }
 
