@@ -224,3 +224,33 @@ def test_invalid_tables_leave_routed_part_out(B):
     expect = ref["h"] + O.swiglu_expert(ref["h"], ws13, ws2)
     rep = assert_close(as_f64_out(b["out"]), expect, "out without routed experts")
     log(f"[invalid-tables] B={B}: {rep}")
+
+
+@pytest.mark.parametrize("B", [1, 8, 64])
+def test_kernel_timing_lists_the_plan(B):
+    """With timing on, an eager step records one (name, ms) per launch of the plan; a captured
+    step records nothing."""
+    log(f"[timing] tp_rank B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer("tp_rank")
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    L.set_kernel_timing(True)
+    try:
+        L.read_kernel_timing()
+        L.layer_decode(B, x, r, b["out"], ws)
+        recs = L.read_kernel_timing()
+        # over 32 tokens one gate/up record spans its four launches (shared split-K, SwiGLU,
+        # two routed widths)
+        want = L.query_plan(B)["kernels_per_step"] - (3 if B > 32 else 0)
+        assert len(recs) == want, recs
+        assert all(ms > 0 for _, ms in recs), recs
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, stream=s, graph=True)
+        s.synchronize()
+        assert L.read_kernel_timing() == []
+    finally:
+        L.set_kernel_timing(False)
