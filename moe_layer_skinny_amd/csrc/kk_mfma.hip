@@ -661,7 +661,8 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.I / 16);
   if (B <= 32) return grouped_dispatch<0>(d, a, max_units, st);
   // over 32 tokens the shared expert's gate/up is a split-K product of its own (its group
-  // alone has too few row tiles to fill the chip), summed by the SwiGLU launch
+  // alone has too few row tiles to fill the chip), its units split by 16-token quarter as
+  // well, summed by the SwiGLU launch
   UnitArgs sh{};
   sh.w_routed = (const uint16_t*)ws13;
   sh.act_routed = h32;
@@ -670,7 +671,7 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   sh.N = 2 * s.Is;
   sh.K = s.H;
   sh.chunks = kSharedSplits;
-  hipError_t e = staged_dispatch<2, 2, false>(d, sh, (sh.N / 32) * sh.chunks, st);
+  hipError_t e = token_split_t<256, 2, false>(d, sh, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((swiglu_reduce_kernel<kSharedSplits>), dim3((B * s.Is + 255) / 256), dim3(256),
                      0, st, scratch, kSharedSplits, B, s.Is, As);
