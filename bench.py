@@ -344,11 +344,12 @@ def main():
         kernels = {k: statistics.mean(v) for k, v in kernels.items()}
 
     # dominant kernel and the weight bytes one launch of it must read: on the GEMV path the
-    # routed gate/up launch also runs the top-k and streams the shared expert's down rows
+    # routed gate/up launch also runs the top-k and streams the shared expert's down rows; on
+    # the split-K path the gate/up record covers the routed and the shared expert's rows
     if plan["path_name"] == "gemv":
         dom_name, dom_bytes = "topk_gateup_gemv_routed", by["routed_gateup"] + by["shared_down"]
     else:
-        dom_name, dom_bytes = "gateup_mfma_routed", by["routed_gateup"]
+        dom_name, dom_bytes = "gateup_mfma", by["routed_gateup"] + by["shared_gateup"]
     roofline = None
     if dom_name in kernels:
         ach = dom_bytes / (kernels[dom_name] * 1e-6) / 1e9

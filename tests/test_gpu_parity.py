@@ -182,8 +182,12 @@ def test_device_side_argument_errors():
     ws = L.new_workspace()
     x = torch.zeros(2, cfg.oproj_in, dtype=torch.bfloat16, device="cuda")
     r = torch.zeros(2, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    for bad_b in (0, -1, 65):  # an empty batch is rejected like an oversized one
+        with pytest.raises(kk.KKError) as e:
+            L.layer_decode(bad_b, x, r, b["out"], ws)
+        assert e.value.status == kk.KK_ERR_INVALID_ARG
     with pytest.raises(kk.KKError) as e:
-        L.layer_decode(65, x, r, b["out"], ws)
+        L.query_plan(0)
     assert e.value.status == kk.KK_ERR_INVALID_ARG
     xm = torch.zeros(2 * cfg.oproj_in + 8, dtype=torch.bfloat16, device="cuda")[1:]
     with pytest.raises(kk.KKError) as e:
