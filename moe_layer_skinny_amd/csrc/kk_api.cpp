@@ -224,6 +224,9 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   // down, combine; B > 32 adds the shared expert's split-K gate/up and its SwiGLU, and a
   // launch for routed groups of more than 16 tokens
   p->kernels_per_step = B > 32 ? 11 : (B > 16 ? 8 : 7);
+  // up to 16 tokens with a small intermediate, the gate/up runs over K chunks and a SwiGLU
+  // launch sums them
+  if (B <= 16 && kk::mfma_gateup_split(c->shape, B)) p->kernels_per_step += 1;
   return KK_OK;
 }
 

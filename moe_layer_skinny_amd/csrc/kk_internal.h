@@ -128,6 +128,9 @@ hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const floa
 // shared expert's gate/up is split over K; its partials use `scratch`
 // (mfma_scratch_floats floats).
 size_t mfma_scratch_floats(const Shape& s, int B);
+// Whether batch B's gate/up also splits every group over K chunks (small intermediates), with
+// a SwiGLU launch of its own after it.
+bool mfma_gateup_split(const Shape& s, int B);
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
                               float* As, float* scratch, hipStream_t st);

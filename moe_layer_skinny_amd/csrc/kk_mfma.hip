@@ -31,6 +31,9 @@ namespace {
 
 // K chunks of the shared expert's split-K gate/up over more than 32 tokens.
 constexpr int kSharedSplits = 7;
+// Gate/up K chunks for experts with a small intermediate: their groups have only I/16 row tiles
+// (8 at I = 128), too few units to fill the chip, so each unit also takes one K chunk.
+constexpr int kGateupSplits = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -145,30 +148,39 @@ __global__ __launch_bounds__(1024) void norm_rows_kernel(const float* __restrict
   }
 }
 
-// As[t][i] = silu(sum_c P[c][t][i]) * sum_c P[c][t][Is + i] over `chunks` K-chunk partials of
-// the shared expert's gate/up rows (fixed chunk order).
+// SwiGLU of K-chunk partials of gate/up rows: for each row r of a region,
+// dst[r][i] = silu(sum_c P_c[r][i]) * sum_c P_c[r][I + i], chunks summed in order, with
+// P_c = base + c * cstride and rows of 2I floats (gate values, then up values).  One launch
+// covers two regions (the routed positions into A, the shared expert's tokens into As).
+struct SwigluRegion {
+  const float* base;
+  size_t cstride;
+  int rows, chunks;
+  float* dst;
+};
 template <int MAXC>
-__global__ __launch_bounds__(256) void swiglu_reduce_kernel(const float* __restrict__ part,
-                                                            int chunks, int B, int Is,
-                                                            float* __restrict__ As) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= B * Is) return;
-  const int t = i / Is, n = i - t * Is;
-  const size_t cs = (size_t)B * 2 * Is;
+__global__ __launch_bounds__(256) void swiglu_reduce_kernel(SwigluRegion r0, SwigluRegion r1,
+                                                            int I) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool second = i >= r0.rows * I;
+  const SwigluRegion R = second ? r1 : r0;
+  if (second) i -= r0.rows * I;
+  if (i >= R.rows * I) return;
+  const int t = i / I, n = i - t * I;
   float g[MAXC], u[MAXC];
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const size_t o = (size_t)min(c, chunks - 1) * cs + (size_t)t * 2 * Is + n;
-    g[c] = part[o];
-    u[c] = part[o + Is];
+    const size_t o = (size_t)min(c, R.chunks - 1) * R.cstride + (size_t)t * 2 * I + n;
+    g[c] = R.base[o];
+    u[c] = R.base[o + I];
   }
   float zg = 0.f, zu = 0.f;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    zg += c < chunks ? g[c] : 0.f;
-    zu += c < chunks ? u[c] : 0.f;
+    zg += c < R.chunks ? g[c] : 0.f;
+    zu += c < R.chunks ? u[c] : 0.f;
   }
-  As[i] = silu_f32(zg) * zu;
+  R.dst[i] = silu_f32(zg) * zu;
 }
 
 // Arguments of the grouped / split-K launches.
@@ -180,8 +192,13 @@ struct UnitArgs {
   float* out_routed;         // MODE 0: A; MODE 1: Y [B*k][H]; MODE 2: part [chunks][B][N]
   float* out_shared;         // MODE 0: As; MODE 1: ys [B][H]
   int H, I, k, B;
-  int N, K, chunks;          // MODE 2
+  int N, K, chunks;          // MODE 2 (and MODE 0 with gu_part)
   Routing rt;
+  // MODE 0 split over `chunks` K chunks: the gate and up sums of chunk c, position p go to
+  // gu_part[(c * gu_P + p) * 2I + i] and [.. + I + i] (the shared expert's tokens at
+  // positions gu_P - B ..) instead of the SwiGLU into A / As
+  float* gu_part;
+  int gu_P;
 };
 
 // ------------------------------------------------------------------------------ LDS-staged
@@ -224,7 +241,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
   const int g = lane >> 4, c = lane & 15;
   const int K = MODE == 0 ? x.H : (MODE == 1 ? x.I : x.K);
   const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
-  const int chunks = MODE == 2 ? x.chunks : 1;
+  const int chunks = (MODE == 2 || (MODE == 0 && x.gu_part)) ? x.chunks : 1;
   const int kchunk = K / chunks;
   const int nst = kchunk / KS;
   const int ntt = (cnt + 15) / 16;
@@ -385,7 +402,12 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
         o = outp + ((size_t)chunk * x.B + p0 + j) * out_rows + row0 + 4 * gg;
       else
         o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
-      if (MODE == 0) {
+      if (MODE == 0 && x.gu_part) {
+        const int pos = shared ? x.gu_P - x.B + j : p0 + j;
+        float* q = x.gu_part + ((size_t)chunk * x.gu_P + pos) * 2 * x.I + row0 + 4 * gg;
+        *reinterpret_cast<float4*>(q) = float4{s0[0], s0[1], s0[2], s0[3]};
+        *reinterpret_cast<float4*>(q + x.I) = float4{s1[0], s1[1], s1[2], s1[3]};
+      } else if (MODE == 0) {
         *reinterpret_cast<float4*>(o) =
             float4{silu_f32(s0[0]) * s1[0], silu_f32(s0[1]) * s1[1], silu_f32(s0[2]) * s1[2],
                    silu_f32(s0[3]) * s1[3]};
@@ -437,7 +459,7 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
   const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
   const int tiles = MODE == 0 ? x.I / 16 : out_rows / 32;
-  const int chunks = MODE == 2 ? x.chunks : 1;
+  const int chunks = (MODE == 2 || (MODE == 0 && x.gu_part)) ? x.chunks : 1;
   const int units = n_groups * tiles * chunks;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int a = unit / (tiles * chunks);
@@ -583,7 +605,16 @@ bool mfma_supported(const Shape& s, int B) {
 
 // K chunks of the split-K launches (the partials the reduce / top-k launches sum).
 int mfma_oproj_splits(const Shape& s) { return s.Ko == 7168 ? 7 : 1; }
-size_t mfma_scratch_floats(const Shape& s, int B) { return (size_t)kSharedSplits * B * 2 * s.Is; }
+bool mfma_gateup_split(const Shape& s, int B) {
+  return s.I <= 256 && (B <= 16 || B > 32) && s.H % (kGateupSplits * 256) == 0;
+}
+
+// Routed (and, up to 16 tokens, shared) gate/up partials of the split launch, then the shared
+// expert's split-K partials over 32 tokens.
+size_t mfma_scratch_floats(const Shape& s, int B) {
+  const size_t routed = s.I <= 256 ? (size_t)kGateupSplits * (B * s.k + B) * 2 * s.I : 0;
+  return routed + (size_t)kSharedSplits * B * 2 * s.Is;
+}
 int mfma_router_splits(const Shape& s) { return 7; }
 
 hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x,
@@ -659,26 +690,56 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   a.B = B;
   a.rt = rt;
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.I / 16);
+  const bool split = mfma_gateup_split(s, B);
+  const int nslot = B * s.k;
+  auto reduce = [&](const SwigluRegion& r0, const SwigluRegion& r1) {
+    const int n = (r0.rows + r1.rows) * s.I;
+    hipLaunchKernelGGL((swiglu_reduce_kernel<8>), dim3((n + 255) / 256), dim3(256), 0, st, r0, r1,
+                       s.I);
+    return hipGetLastError();
+  };
+  if (B <= 16 && split) {
+    // every group (the shared expert's tokens at positions nslot ..) over K chunks, then the
+    // SwiGLU of the summed chunks
+    a.gu_part = scratch;
+    a.gu_P = nslot + B;
+    a.chunks = kGateupSplits;
+    hipError_t e = staged_t<0, 1, 256, 2, false, 0>(d, a, max_units * kGateupSplits, st);
+    if (e != hipSuccess) return e;
+    const size_t cs = (size_t)a.gu_P * 2 * s.I;
+    return reduce(SwigluRegion{scratch, cs, nslot, kGateupSplits, A},
+                  SwigluRegion{scratch + (size_t)nslot * 2 * s.I, cs, B, kGateupSplits, As});
+  }
   if (B <= 32) return grouped_dispatch<0>(d, a, max_units, st);
   // over 32 tokens the shared expert's gate/up is a split-K product of its own (its group
   // alone has too few row tiles to fill the chip), its units split by 16-token quarter as
-  // well, summed by the SwiGLU launch
+  // well; the routed groups follow (over K chunks too when split), and one launch applies
+  // the SwiGLU to the summed partials of both
+  float* shared_part = scratch + (split ? (size_t)kGateupSplits * (nslot + B) * 2 * s.I : 0);
   UnitArgs sh{};
   sh.w_routed = (const uint16_t*)ws13;
   sh.act_routed = h32;
-  sh.out_routed = scratch;
+  sh.out_routed = shared_part;
   sh.B = B;
   sh.N = 2 * s.Is;
   sh.K = s.H;
   sh.chunks = kSharedSplits;
   hipError_t e = token_split_t<256, 2, false>(d, sh, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((swiglu_reduce_kernel<kSharedSplits>), dim3((B * s.Is + 255) / 256), dim3(256),
-                     0, st, scratch, kSharedSplits, B, s.Is, As);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  e = staged_t<0, 1, 256, 2, false, 1>(d, a, max_units, st);
+  if (split) {
+    a.gu_part = scratch;
+    a.gu_P = nslot;
+    a.chunks = kGateupSplits;
+  }
+  const int units = max_units * (split ? kGateupSplits : 1);
+  e = staged_t<0, 1, 256, 2, false, 1>(d, a, units, st);
   if (e != hipSuccess) return e;
-  return staged_t<0, 4, 128, 2, false, 3>(d, a, max_units, st);
+  e = staged_t<0, 4, 128, 2, false, 3>(d, a, units, st);
+  if (e != hipSuccess) return e;
+  const SwigluRegion routed = split ? SwigluRegion{scratch, (size_t)nslot * 2 * s.I, nslot,
+                                                   kGateupSplits, A}
+                                    : SwigluRegion{scratch, 0, 0, 1, A};
+  return reduce(routed, SwigluRegion{shared_part, (size_t)B * 2 * s.Is, B, kSharedSplits, As});
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,

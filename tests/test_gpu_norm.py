@@ -107,5 +107,5 @@ def test_norm_plan_launch_counts_unchanged():
     log("[norm-plan] tp_norm")
     _, _, L = gpu_layer("tp_norm")
     assert L.query_plan(1)["kernels_per_step"] == 4
-    assert L.query_plan(8)["kernels_per_step"] == 7
+    assert L.query_plan(8)["kernels_per_step"] == 8  # K-split gate/up + its SwiGLU launch
     assert L.query_plan(64)["kernels_per_step"] == 11
