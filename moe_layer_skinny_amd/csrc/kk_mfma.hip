@@ -474,6 +474,90 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   }
 }
 
+// Down-projection of experts with a short K (K = I = 128): a unit is 128 output rows of one
+// group, one 32-row tile pair per wave.  Its weights (32 KB) are staged once; each wave runs
+// the whole K for its own tile pair, token tile by token tile, so a unit costs one weight round
+// trip and needs no cross-wave reduction; the next unit's weights are requested as soon as
+// this unit's are in LDS.  (The general unit splits K over the four waves, which for K = 128
+// leaves one 32-wide step per wave and a reduction per 8 KB of weights.)
+template <int K>
+__global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
+  constexpr int K8 = K / 8, WP = K8 + 1, ROWS = 128, WLD = ROWS * K8 / 256;
+  static_assert(16 * K8 == 256, "one activation chunk per thread and token tile");
+  extern __shared__ u32x4 lds[];
+  u32x4* lw = lds;              // [ROWS][WP]
+  u32x4* la = lds + ROWS * WP;  // [2 terms][K8][16 tokens]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int n_groups = *x.rt.n_act + 1;
+  const int tiles = x.H / ROWS;
+  const int units = n_groups * tiles;
+  u32x4 wreg[WLD];
+  auto load_w = [&](int un) {
+    const int u = min(un, units - 1);  // past the end: a valid unit's rows, never used
+    const int a = u / tiles, tile = u - a * tiles;
+    const Group gr = group_of<1>(x, a, n_groups);
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+      wreg[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(gr.wbase + (size_t)(tile * ROWS + rr) * K + ch * 8));
+    }
+  };
+  int unit = blockIdx.x;
+  if (unit >= units) return;
+  load_w(unit);
+  for (; unit < units; unit += gridDim.x) {
+    const int a = unit / tiles, tile = unit - a * tiles;
+    const Group gr = group_of<1>(x, a, n_groups);
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+      lw[rr * WP + ch] = wreg[i];
+    }
+    load_w(unit + gridDim.x);
+    const int ntt = (gr.cnt + 15) / 16;
+    const float* asrc = gr.shared ? x.act_shared : reinterpret_cast<const float*>(x.act_routed);
+    float* outp = gr.shared ? x.out_shared : x.out_routed;
+    for (int tt = 0; tt < ntt; ++tt) {
+      {
+        const int j = tid / K8, ch = tid - j * K8, jt = tt * 16 + j;
+        const bool ok = jt < gr.cnt;
+        const int row = ok ? (gr.shared ? jt : gr.p0 + jt) : 0;
+        const float4* src = reinterpret_cast<const float4*>(asrc + (size_t)row * K + ch * 8);
+        const float4 v0 = src[0], v1 = src[1];
+        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        if (!ok)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = 0.f;
+        u32x4 terms[2];
+        split_terms<2>(v, terms);
+        la[(0 * K8 + ch) * 16 + j] = terms[0];
+        la[(1 * K8 + ch) * 16 + j] = terms[1];
+      }
+      __syncthreads();
+      f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < K / 32; ++ks) {
+        const u32x4 a0 = lw[(wave * 32 + c) * WP + ks * 4 + g];
+        const u32x4 a1 = lw[(wave * 32 + 16 + c) * WP + ks * 4 + g];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const u32x4 b = la[(q2 * K8 + ks * 4 + g) * 16 + c];
+          acc0 = mfma(a0, b, acc0);
+          acc1 = mfma(a1, b, acc1);
+        }
+      }
+      const int j = tt * 16 + c;
+      if (j < gr.cnt) {
+        float* o = outp + (size_t)((gr.shared ? 0 : gr.p0) + j) * x.H + tile * ROWS + wave * 32 + 4 * g;
+        *reinterpret_cast<float4*>(o) = float4{acc0[0], acc0[1], acc0[2], acc0[3]};
+        *reinterpret_cast<float4*>(o + 16) = float4{acc1[0], acc1[1], acc1[2], acc1[3]};
+      }
+      __syncthreads();  // la (next token tile) and lw (next unit) are rewritten after this
+    }
+  }
+}
+
 // Split-K product with the tokens split as well: units (row tile, K chunk, 16-token quarter),
 // so that a launch over many tokens but few row tiles (the router: 12 row tiles x 7 chunks)
 // still fills the chip.  A unit's weights are read once per quarter (the later reads are
@@ -759,7 +843,14 @@ hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float*
   a.rt = rt;
   const int max_units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.H / 32);
   if (s.I == 2048) return grouped_dispatch<1>(d, a, max_units, st);
-  if (s.I == 128) return grouped_dispatch<1, 128>(d, a, max_units, st);
+  if (s.I == 128 && s.H % 128 == 0) {
+    auto kern = mfma_down_shortk_kernel<128>;
+    constexpr size_t lds = (size_t)(128 * (128 / 8 + 1) + 2 * (128 / 8) * 16) * 16;
+    static thread_local int bpc = 0;
+    const int units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.H / 128);
+    hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, a);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 
