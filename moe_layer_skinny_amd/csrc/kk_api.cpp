@@ -47,8 +47,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace carve-up (offsets in bytes from ws, each 256-byte aligned).
 struct Layout {
-  size_t h32, u32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, A, As, Y,
-      ys, oproj_part, total;
+  size_t h32, u32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, vg, n_vg,
+      A, As, Y, ys, oproj_part, total;
 };
 
 kk::Shape to_shape(const kk_config& c) {
@@ -75,6 +75,8 @@ Layout make_layout(const kk_config& c, int Bm) {
   L.inv_perm = take(slots * 4);
   L.act = take((size_t)std::max(c.n_experts, 64) * 4);  // read 64 lanes at a time
   L.n_act = take(16);
+  L.vg = take((size_t)(c.n_experts + 64) * 4);  // pieces of <= 16 positions (<= E + B*k/16)
+  L.n_vg = take(16);
   L.A = take(slots * c.inter * 4);
   L.As = take((size_t)Bm * c.shared_inter * 4);
   L.Y = take(slots * c.hidden * 4);
@@ -221,9 +223,8 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
   // oproj, reduce, router logits, top-k rows + tables (one launch up to 16 tokens), gate/up,
-  // down, combine; B > 32 adds the shared expert's split-K gate/up and its SwiGLU, and a
-  // launch for routed groups of more than 16 tokens
-  p->kernels_per_step = B > 32 ? 11 : (B > 16 ? 8 : 7);
+  // down, combine; B > 32 adds the shared expert's split-K gate/up and its SwiGLU
+  p->kernels_per_step = B > 32 ? 10 : (B > 16 ? 8 : 7);
   // up to 16 tokens with a small intermediate, the gate/up runs over K chunks and a SwiGLU
   // launch sums them
   if (B <= 16 && kk::mfma_gateup_split(c->shape, B)) p->kernels_per_step += 1;
@@ -270,6 +271,8 @@ struct WsPtrs {
   int32_t* inv_perm;
   int32_t* act;
   int32_t* n_act;
+  int32_t* vg;
+  int32_t* n_vg;
   float* A;
   float* As;
   float* Y;
@@ -283,6 +286,7 @@ WsPtrs carve(const kk_ctx* c, void* ws) {
   return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.u32),        (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
                 (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
                 (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
+                (int32_t*)(b + L.vg),       (int32_t*)(b + L.n_vg),
                 (float*)(b + L.A),         (float*)(b + L.As),         (float*)(b + L.Y),
                 (float*)(b + L.ys),         (float*)(b + L.oproj_part)};
 }
@@ -495,7 +499,7 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
                         const PrefetchNext* pf = nullptr) {
   WsPtrs p = carve(c, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
-                 p.inv_perm, p.act, p.n_act};
+                 p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
   if (pf && (st = enqueue_prefetch(*pf, s)) != KK_OK) return st;
@@ -686,7 +690,8 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     WsPtrs p = carve(c, ws);
-    kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act};
+    kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act, p.vg,
+                   p.n_vg};
     if (plan.path == KK_PATH_SPLITK_MFMA) {
       const float* u = enqueue_norm_from_h32(c, B, h32, p.u32, (hipStream_t)stream, &st);
       if (st != KK_OK) return st;
@@ -719,7 +724,7 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
     hipStream_t s = (hipStream_t)stream;
     WsPtrs p = carve(c, ws);
     kk::Routing rt{(int32_t*)topk_idx, (float*)topk_gate, (int32_t*)expert_offsets,
-                   (int32_t*)perm, p.inv_perm, p.act, p.n_act};
+                   (int32_t*)perm, p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
     KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
            "moe prep launch");
     if (plan.path == KK_PATH_SPLITK_MFMA) {

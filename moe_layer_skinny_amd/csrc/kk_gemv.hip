@@ -891,10 +891,11 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
 }
 
 // ------------------------------------------------------------------------------ prep
-// act / n_act / inv_perm from expert_offsets + perm supplied by the caller.  Tables that are
-// not a valid routing of nslots slots (offsets not non-decreasing from 0 to nslots, perm not
-// a permutation) set n_act = 0, so no kernel indexes through them.
-__global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, Routing rt) {
+// act / n_act / inv_perm (and the pieces of at most 16 positions) from expert_offsets + perm
+// supplied by the caller.  Tables that are not a valid routing of nslots slots of B tokens
+// (offsets not non-decreasing from 0 to nslots, more than B positions for one expert, perm
+// entries out of range) set n_act = 0 and no pieces, so no kernel indexes through them.
+__global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, int B, Routing rt) {
   const int lane = threadIdx.x;
   const int per = (E + 63) / 64;
   bool ok = true;
@@ -903,7 +904,7 @@ __global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, Routing
     const int e = lane * per + q;
     if (e < E) {
       const int a = rt.offsets[e], b = rt.offsets[e + 1];
-      ok = ok && a >= 0 && b >= a && b <= nslots;
+      ok = ok && a >= 0 && b >= a && b <= nslots && b - a <= B;  // <= B tokens per expert
       if (b > a) ++lf;
     }
   }
@@ -927,6 +928,29 @@ __global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, Routing
     for (int p = lane; p < nslots; p += 64) rt.inv_perm[rt.perm[p]] = p;
   }
   if (lane == 63) *rt.n_act = all_ok ? inc : 0;
+  if (rt.vg) {
+    // pieces of at most 16 positions per active expert, in expert order (none if invalid)
+    int vt = 0;
+    for (int q = 0; q < per; ++q) {
+      const int e = lane * per + q;
+      if (all_ok && e < E) vt += (rt.offsets[e + 1] - rt.offsets[e] + 15) >> 4;
+    }
+    int vinc = vt;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(vinc, off, 64);
+      if (lane >= off) vinc += v;
+    }
+    int vpos = vinc - vt, a = inc - lf;
+    for (int q = 0; q < per; ++q) {
+      const int e = lane * per + q;
+      if (all_ok && e < E) {
+        const int c = rt.offsets[e + 1] - rt.offsets[e];
+        for (int pc = 0; pc < (c + 15) >> 4; ++pc) rt.vg[vpos++] = (a << 2) | pc;
+        if (c > 0) ++a;
+      }
+    }
+    if (lane == 63) *rt.n_vg = vinc;
+  }
 }
 
 // ------------------------------------------------------------------------------ dispatch
@@ -1164,7 +1188,7 @@ hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStre
 }
 
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st) {
-  hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(64), 0, st, s.E, B * s.k, rt);
+  hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(64), 0, st, s.E, B * s.k, B, rt);
   return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@ struct Routing {
   int32_t* inv_perm;   // [B*k]  slot -> position
   int32_t* act;        // [E]    active experts, ascending
   int32_t* n_act;      // [1]
+  // optional: the active experts cut into pieces of at most 16 positions, in expert order;
+  // entry = (index into act) << 2 | piece (positions offsets[e] + 16 piece ..)
+  int32_t* vg = nullptr;    // [E + 64]
+  int32_t* n_vg = nullptr;  // [1]
 };
 
 // RMSNorm between the residual add and the router / experts:

@@ -265,9 +265,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     const int jj = aok[i] ? j : 0;
     int src;
     if (MODE == 0)
-      src = shared ? jj : x.rt.perm[p0 + jj] / x.k;
-    else if (MODE == 1)
-      src = shared ? jj : p0 + jj;
+      src = shared ? p0 + jj : x.rt.perm[p0 + jj] / x.k;
     else
       src = p0 + jj;
     const void* base = (MODE == 1 && shared) ? (const void*)x.act_shared : x.act_routed;
@@ -401,9 +399,9 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       if (MODE == 2)
         o = outp + ((size_t)chunk * x.B + p0 + j) * out_rows + row0 + 4 * gg;
       else
-        o = outp + (size_t)((shared ? 0 : p0) + j) * out_rows + row0 + 4 * gg;
+        o = outp + (size_t)(p0 + j) * out_rows + row0 + 4 * gg;
       if (MODE == 0 && x.gu_part) {
-        const int pos = shared ? x.gu_P - x.B + j : p0 + j;
+        const int pos = shared ? x.gu_P - x.B + p0 + j : p0 + j;
         float* q = x.gu_part + ((size_t)chunk * x.gu_P + pos) * 2 * x.I + row0 + 4 * gg;
         *reinterpret_cast<float4*>(q) = float4{s0[0], s0[1], s0[2], s0[3]};
         *reinterpret_cast<float4*>(q + x.I) = float4{s1[0], s1[1], s1[2], s1[3]};
@@ -452,7 +450,9 @@ __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups
 
 // All MFMA launches of one token-tile width: units (group, tile pair, K chunk) over a
 // persistent grid.  GSEL picks the groups a launch covers: 0 all, 1 those with <= 16
-// tokens, 2 the others, 3 the routed ones with more than 16 tokens.
+// tokens, 2 the others, 3 the routed ones with more than 16 tokens; 4 the routed experts cut
+// into pieces of at most 16 positions (rt.vg), 5 those plus the shared expert's tokens in
+// pieces of 16 (one-tile launches over any batch).
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
@@ -460,6 +460,32 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
   const int tiles = MODE == 0 ? x.I / 16 : out_rows / 32;
   const int chunks = (MODE == 2 || (MODE == 0 && x.gu_part)) ? x.chunks : 1;
+  if constexpr (GSEL >= 4) {
+    static_assert(TT == 1 && MODE != 2, "pieces are one token tile of a grouped launch");
+    const int nv = *x.rt.n_vg;
+    const int pieces = nv + (GSEL == 5 ? (x.B + 15) / 16 : 0);
+    const int units = pieces * tiles * chunks;
+    for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+      const int v = unit / (tiles * chunks);
+      const int rem = unit - v * tiles * chunks;
+      const int tile = rem / chunks, chunk = rem - tile * chunks;
+      int p0, cnt;
+      Group gr;
+      if (v < nv) {
+        const int ent = x.rt.vg[v], pc = ent & 3;
+        gr = group_of<MODE>(x, ent >> 2, n_groups);
+        p0 = gr.p0 + 16 * pc;
+        cnt = min(16, gr.cnt - 16 * pc);
+      } else {
+        gr = group_of<MODE>(x, n_groups - 1, n_groups);
+        p0 = 16 * (v - nv);
+        cnt = min(16, x.B - p0);
+      }
+      staged_unit<MODE, 1, KS, NTERM, BF16SRC, DEPTH>(x, lds, tile, chunk, p0, cnt, gr.wbase,
+                                                      gr.shared);
+    }
+    return;
+  }
   const int units = n_groups * tiles * chunks;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int a = unit / (tiles * chunks);
@@ -794,7 +820,12 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
     return reduce(SwigluRegion{scratch, cs, nslot, kGateupSplits, A},
                   SwigluRegion{scratch + (size_t)nslot * 2 * s.I, cs, B, kGateupSplits, As});
   }
-  if (B <= 32) return grouped_dispatch<0>(d, a, max_units, st);
+  if (B > 16 && B <= 32) {
+    // every routed expert and the shared one cut into pieces of 16 positions, one-tile units
+    const int units = (s.E + B * s.k / 16 + (B + 15) / 16) * (s.I / 16);
+    return staged_t<0, 1, 256, 2, false, 5>(d, a, units, st);
+  }
+  if (B <= 16) return grouped_dispatch<0>(d, a, max_units, st);
   // over 32 tokens the shared expert's gate/up is a split-K product of its own (its group
   // alone has too few row tiles to fill the chip), its units split by 16-token quarter as
   // well; the routed groups follow (over K chunks too when split), and one launch applies
@@ -815,10 +846,9 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
     a.gu_P = nslot;
     a.chunks = kGateupSplits;
   }
-  const int units = max_units * (split ? kGateupSplits : 1);
-  e = staged_t<0, 1, 256, 2, false, 1>(d, a, units, st);
-  if (e != hipSuccess) return e;
-  e = staged_t<0, 4, 128, 2, false, 3>(d, a, units, st);
+  // every routed expert, hot ones cut into pieces of 16 positions, in one one-tile launch
+  const int units = (s.E + B * s.k / 16 + 1) * (s.I / 16) * (split ? kGateupSplits : 1);
+  e = staged_t<0, 1, 256, 2, false, 4>(d, a, units, st);
   if (e != hipSuccess) return e;
   const SwigluRegion routed = split ? SwigluRegion{scratch, (size_t)nslot * 2 * s.I, nslot,
                                                    kGateupSplits, A}

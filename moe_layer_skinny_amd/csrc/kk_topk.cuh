@@ -194,8 +194,12 @@ __device__ inline void build_tables(int B, int E, int k, const Routing& rt, Topk
       rt.act[j] = sm.sel[j];
       rt.perm[j] = j;
       rt.inv_perm[j] = j;
+      if (rt.vg) rt.vg[j] = j << 2;
     }
-    if (threadIdx.x == 0) *rt.n_act = k;
+    if (threadIdx.x == 0) {
+      *rt.n_act = k;
+      if (rt.n_vg) *rt.n_vg = k;
+    }
     return;
   }
   for (int e = threadIdx.x; e < E; e += blockDim.x) sm.mask[e] = 0ull;
@@ -230,6 +234,25 @@ __device__ inline void build_tables(int B, int E, int k, const Routing& rt, Topk
     if (lane == 63) {
       rt.offsets[E] = (int)(inc & 0xFFFFu);
       *rt.n_act = (int)(inc >> 16);
+    }
+    if (rt.vg) {
+      // pieces of at most 16 positions per active expert, in expert order
+      uint32_t vt = 0;
+      for (int q = 0; q < per; ++q) {
+        const int e = lane * per + q;
+        if (e < E) vt += ((uint32_t)__popcll(sm.mask[e]) + 15u) >> 4;
+      }
+      const uint32_t vinc = wave_incl_scan_u32(vt);
+      uint32_t vpos = vinc - vt, a = (inc - loc) >> 16;
+      for (int q = 0; q < per; ++q) {
+        const int e = lane * per + q;
+        if (e < E) {
+          const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
+          for (uint32_t pc = 0; pc < (c + 15u) >> 4; ++pc) rt.vg[vpos++] = (int)((a << 2) | pc);
+          if (c > 0) ++a;
+        }
+      }
+      if (lane == 63) *rt.n_vg = (int)vinc;
     }
   }
   __syncthreads();

@@ -51,7 +51,7 @@ def test_plan_is_mfma(name, B):
     assert p["path_name"] == "splitk_mfma" and p["forced"] == 0
     # up to 16 tokens a small intermediate adds the SwiGLU launch of the K-split gate/up
     split = B <= 16 and synth.CONFIGS[name].inter <= 256
-    assert p["kernels_per_step"] == (11 if B > 32 else (8 if B > 16 else 7 + split))
+    assert p["kernels_per_step"] == (10 if B > 32 else (8 if B > 16 else 7 + split))
     assert p["oproj_splitk"] == (7 if synth.CONFIGS[name].oproj_in == 7168 else 1)
     assert p["router_splitk"] == 7
 

@@ -246,10 +246,10 @@ def test_kernel_timing_lists_the_plan(B):
         L.read_kernel_timing()
         L.layer_decode(B, x, r, b["out"], ws)
         recs = L.read_kernel_timing()
-        # one gate/up record spans its launches: over 32 tokens four (shared split-K, two
-        # routed widths, SwiGLU); up to 16 tokens with this small intermediate two (K-split
-        # gate/up, SwiGLU)
-        gu_launches = 4 if B > 32 else (2 if 2 < B <= 16 else 1)
+        # one gate/up record spans its launches: over 32 tokens three (shared split-K, routed
+        # pieces, SwiGLU); up to 16 tokens with this small intermediate two (K-split gate/up,
+        # SwiGLU)
+        gu_launches = 3 if B > 32 else (2 if 2 < B <= 16 else 1)
         want = L.query_plan(B)["kernels_per_step"] - (gu_launches - 1)
         assert len(recs) == want, recs
         assert all(ms > 0 for _, ms in recs), recs
