@@ -81,8 +81,8 @@ Layout make_layout(const kk_config& c, int Bm) {
   L.As = take((size_t)Bm * c.shared_inter * 4);
   L.Y = take(slots * c.hidden * 4);
   L.ys = take((size_t)Bm * c.hidden * 4);
-  // o-proj partials of the split-K path; reused afterwards by the shared expert's split-K
-  // gate/up partials
+  // o-proj partials of the split-K path; reused afterwards by the gate/up partials (K chunks,
+  // or the shared expert's split-K product)
   L.oproj_part = take(std::max((size_t)kMaxOprojSplits * Bm * c.hidden,
                                kk::mfma_scratch_floats(to_shape(c), Bm)) * 4);
   L.total = o;
@@ -223,11 +223,10 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   p->oproj_splitk = kk::mfma_oproj_splits(c->shape);
   p->router_splitk = kk::mfma_router_splits(c->shape);
   // oproj, reduce, router logits, top-k rows + tables (one launch up to 16 tokens), gate/up,
-  // down, combine; B > 32 adds the shared expert's split-K gate/up and its SwiGLU
-  p->kernels_per_step = B > 32 ? 10 : (B > 16 ? 8 : 7);
-  // up to 16 tokens with a small intermediate, the gate/up runs over K chunks and a SwiGLU
-  // launch sums them
-  if (B <= 16 && kk::mfma_gateup_split(c->shape, B)) p->kernels_per_step += 1;
+  // down, combine; a gate/up over K chunks adds the SwiGLU launch that sums them, and over 32
+  // tokens an unsplit gate/up adds the shared expert's split-K launch and its SwiGLU
+  const bool split = kk::mfma_gateup_split(c->shape, B);
+  p->kernels_per_step = (B > 16 ? 8 : 7) + (split ? 1 : 0) + (B > 32 && !split ? 2 : 0);
   return KK_OK;
 }
 

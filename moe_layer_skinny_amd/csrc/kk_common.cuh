@@ -203,15 +203,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Maximum of a 64-bit v over the 64 lanes in two 32-bit passes: the high words first, then
-// the low words of the lanes that hold the maximal high word.
-__device__ __forceinline__ uint64_t wave_max_u64_2pass(uint64_t v) {
-  const uint32_t hi = (uint32_t)(v >> 32);
-  const uint32_t mh = wave_max_u32(hi);
-  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
-  return ((uint64_t)mh << 32) | ml;
-}
-
 // Sum of v over the 64 lanes in a fixed combining order, returned to every lane.
 __device__ __forceinline__ double wave_sum_f64_dpp(double v) {
   auto step = [](double x, uint64_t moved) { return x + __longlong_as_double((long long)moved); };

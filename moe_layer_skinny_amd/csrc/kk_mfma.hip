@@ -719,11 +719,12 @@ bool mfma_gateup_split(const Shape& s, int B) {
   return s.I <= 256 && (B <= 16 || B > 32) && s.H % (kGateupSplits * 256) == 0;
 }
 
-// Routed (and, up to 16 tokens, shared) gate/up partials of the split launch, then the shared
-// expert's split-K partials over 32 tokens.
+// Gate/up K-chunk partials of the split launches (routed and shared), or the shared expert's
+// split-K partials over 32 tokens when the gate/up is not split.
 size_t mfma_scratch_floats(const Shape& s, int B) {
-  const size_t routed = s.I <= 256 ? (size_t)kGateupSplits * (B * s.k + B) * 2 * s.I : 0;
-  return routed + (size_t)kSharedSplits * B * 2 * s.Is;
+  const size_t chunked = s.I <= 256 ? (size_t)kGateupSplits * (B * s.k + B) * 2 * s.I : 0;
+  const size_t shared = (size_t)kSharedSplits * B * 2 * s.Is;
+  return chunked > shared ? chunked : shared;
 }
 int mfma_router_splits(const Shape& s) { return 7; }
 
@@ -808,13 +809,17 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
                        s.I);
     return hipGetLastError();
   };
-  if (B <= 16 && split) {
-    // every group (the shared expert's tokens at positions nslot ..) over K chunks, then the
-    // SwiGLU of the summed chunks
+  if (split) {
+    // every group over K chunks (the shared expert's tokens at positions nslot ..), then the
+    // SwiGLU of the summed chunks: up to 16 tokens one unit per (group, tile, chunk); over 32
+    // the routed experts cut into pieces of at most 16 positions and the shared expert's
+    // tokens in pieces of 16
     a.gu_part = scratch;
     a.gu_P = nslot + B;
     a.chunks = kGateupSplits;
-    hipError_t e = staged_t<0, 1, 256, 2, false, 0>(d, a, max_units * kGateupSplits, st);
+    const int piece_units = (s.E + nslot / 16 + (B + 15) / 16) * (s.I / 16) * kGateupSplits;
+    hipError_t e = B <= 16 ? staged_t<0, 1, 256, 2, false, 0>(d, a, max_units * kGateupSplits, st)
+                           : staged_t<0, 1, 256, 2, false, 5>(d, a, piece_units, st);
     if (e != hipSuccess) return e;
     const size_t cs = (size_t)a.gu_P * 2 * s.I;
     return reduce(SwigluRegion{scratch, cs, nslot, kGateupSplits, A},
@@ -826,34 +831,25 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
     return staged_t<0, 1, 256, 2, false, 5>(d, a, units, st);
   }
   if (B <= 16) return grouped_dispatch<0>(d, a, max_units, st);
-  // over 32 tokens the shared expert's gate/up is a split-K product of its own (its group
-  // alone has too few row tiles to fill the chip), its units split by 16-token quarter as
-  // well; the routed groups follow (over K chunks too when split), and one launch applies
-  // the SwiGLU to the summed partials of both
-  float* shared_part = scratch + (split ? (size_t)kGateupSplits * (nslot + B) * 2 * s.I : 0);
+  // over 32 tokens (not split) the shared expert's gate/up is a split-K product of its own
+  // (its group alone has too few row tiles to fill the chip), its units split by 16-token
+  // quarter as well; then every routed expert, hot ones cut into pieces of 16 positions, in
+  // one one-tile launch, and one launch applies the SwiGLU to the shared partials
   UnitArgs sh{};
   sh.w_routed = (const uint16_t*)ws13;
   sh.act_routed = h32;
-  sh.out_routed = shared_part;
+  sh.out_routed = scratch;
   sh.B = B;
   sh.N = 2 * s.Is;
   sh.K = s.H;
   sh.chunks = kSharedSplits;
   hipError_t e = token_split_t<256, 2, false>(d, sh, st);
   if (e != hipSuccess) return e;
-  if (split) {
-    a.gu_part = scratch;
-    a.gu_P = nslot;
-    a.chunks = kGateupSplits;
-  }
-  // every routed expert, hot ones cut into pieces of 16 positions, in one one-tile launch
-  const int units = (s.E + B * s.k / 16 + 1) * (s.I / 16) * (split ? kGateupSplits : 1);
+  const int units = (s.E + nslot / 16 + 1) * (s.I / 16);
   e = staged_t<0, 1, 256, 2, false, 4>(d, a, units, st);
   if (e != hipSuccess) return e;
-  const SwigluRegion routed = split ? SwigluRegion{scratch, (size_t)nslot * 2 * s.I, nslot,
-                                                   kGateupSplits, A}
-                                    : SwigluRegion{scratch, 0, 0, 1, A};
-  return reduce(routed, SwigluRegion{shared_part, (size_t)B * 2 * s.Is, B, kSharedSplits, As});
+  return reduce(SwigluRegion{scratch, 0, 0, 1, A},
+                SwigluRegion{scratch, (size_t)B * 2 * s.Is, B, kSharedSplits, As});
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,

@@ -72,11 +72,17 @@ __device__ inline void topk_select(const float (&l_)[kMaxM], const float (&bv)[k
   ce(0, 4); ce(1, 5); ce(2, 6); ce(3, 7);
   ce(2, 4); ce(3, 5);
   ce(1, 2); ce(3, 4); ce(5, 6);
-  // k rounds: the wave maximum of the heads wins; its lane drops it
+  // k rounds: the wave maximum of the heads wins; its lane drops it.  The high words decide
+  // unless several heads share the maximal one; only then are their low words compared.
   uint32_t selmask = 0;
   for (int r = 0; r < k; ++r) {
-    const uint64_t best = wave_max_u64_2pass(sk[0]);
-    const int win = 511 - (int)(best & 0x1FFull);
+    const uint32_t hi = (uint32_t)(sk[0] >> 32), lo = (uint32_t)sk[0];
+    const uint32_t mh = wave_max_u32(hi);
+    const uint64_t tied = __ballot(hi == mh);
+    const uint32_t ml = __popcll(tied) == 1
+                            ? (uint32_t)__builtin_amdgcn_readlane((int)lo, __builtin_ctzll(tied))
+                            : wave_max_u32(hi == mh ? lo : 0u);
+    const int win = 511 - (int)(ml & 0x1FFu);
     const bool mine = (win & 63) == lane;
     if (mine) selmask |= 1u << (win >> 6);
 #pragma unroll
@@ -88,6 +94,7 @@ __device__ inline void topk_select(const float (&l_)[kMaxM], const float (&bv)[k
   for (int m = 0; m < kMaxM; ++m)
     if ((selmask >> m) & 1u) ssum += sc[m];
   ssum = wave_sum_f64_dpp(ssum);
+  const double gscale = (double)routed_scale / ssum;
   int base = 0;
 #pragma unroll
   for (int m = 0; m < kMaxM; ++m) {
@@ -97,7 +104,7 @@ __device__ inline void topk_select(const float (&l_)[kMaxM], const float (&bv)[k
       const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
       const int e = lane + 64 * m;
       rt.topk_idx[t * k + pos] = e;
-      rt.topk_gate[t * k + pos] = (float)((double)routed_scale * sc[m] / ssum);
+      rt.topk_gate[t * k + pos] = (float)(sc[m] * gscale);
       if (sel) sel[t * k + pos] = e;
     }
     base += __popcll(bal);
@@ -116,7 +123,7 @@ __device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E,
 // before any is used (addresses clamped instead of branched around, so nothing waits on a
 // join).
 constexpr int kMaxTopkSplits = 8;
-__device__ inline void topk_row(const float* part, int splits, const float* __restrict__ bias,
+__device__ __forceinline__ void topk_row(const float* part, int splits, const float* __restrict__ bias,
                                 int B, int E, int k, float routed_scale, int t, const Routing& rt,
                                 int* sel) {
   constexpr int MAXS = kMaxTopkSplits;
@@ -208,51 +215,43 @@ __device__ inline void build_tables(int B, int E, int k, const Routing& rt, Topk
     atomicOr(&sm.mask[sm.sel[i]], 1ull << (i / k));
   __syncthreads();
   if (wave == 0) {
-    // lane l owns experts l*per .. l*per+per-1; counts (<= 64) and active flags are scanned
-    // together as (count | flag << 16)
+    // lane l owns experts l*per .. l*per+per-1 (per <= kMaxM); their counts (<= 64) are read
+    // from the masks once.  Counts and active flags are scanned together as
+    // (count | flag << 16), and the pieces of at most 16 positions in a second scan.
     const int per = (E + 63) / 64;
-    uint32_t loc = 0;
-    for (int q = 0; q < per; ++q) {
+    uint32_t cnt[kMaxM];
+    uint32_t loc = 0, vt = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxM; ++q) {
       const int e = lane * per + q;
-      if (e < E) {
-        const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
-        loc += c | ((c > 0 ? 1u : 0u) << 16);
-      }
+      cnt[q] = q < per && e < E ? (uint32_t)__popcll(sm.mask[e]) : 0u;
+      loc += cnt[q] | ((cnt[q] > 0 ? 1u : 0u) << 16);
+      vt += (cnt[q] + 15u) >> 4;
     }
     const uint32_t inc = wave_incl_scan_u32(loc);
-    uint32_t ec = (inc - loc) & 0xFFFFu, ef = (inc - loc) >> 16;
-    for (int q = 0; q < per; ++q) {
+    const uint32_t vinc = rt.vg ? wave_incl_scan_u32(vt) : 0u;
+    uint32_t ec = (inc - loc) & 0xFFFFu, ef = (inc - loc) >> 16, vpos = vinc - vt;
+#pragma unroll
+    for (int q = 0; q < kMaxM; ++q) {
       const int e = lane * per + q;
-      if (e < E) {
-        const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
+      if (q < per && e < E) {
         sm.start[e] = (int)ec;
         rt.offsets[e] = (int)ec;
-        if (c > 0) rt.act[ef++] = e;
-        ec += c;
+        ec += cnt[q];
+        if (cnt[q] > 0) {
+          if (rt.vg) {
+#pragma unroll
+            for (uint32_t pc = 0; pc < 4; ++pc)
+              if (16u * pc < cnt[q]) rt.vg[vpos++] = (int)((ef << 2) | pc);
+          }
+          rt.act[ef++] = e;
+        }
       }
     }
     if (lane == 63) {
       rt.offsets[E] = (int)(inc & 0xFFFFu);
       *rt.n_act = (int)(inc >> 16);
-    }
-    if (rt.vg) {
-      // pieces of at most 16 positions per active expert, in expert order
-      uint32_t vt = 0;
-      for (int q = 0; q < per; ++q) {
-        const int e = lane * per + q;
-        if (e < E) vt += ((uint32_t)__popcll(sm.mask[e]) + 15u) >> 4;
-      }
-      const uint32_t vinc = wave_incl_scan_u32(vt);
-      uint32_t vpos = vinc - vt, a = (inc - loc) >> 16;
-      for (int q = 0; q < per; ++q) {
-        const int e = lane * per + q;
-        if (e < E) {
-          const uint32_t c = (uint32_t)__popcll(sm.mask[e]);
-          for (uint32_t pc = 0; pc < (c + 15u) >> 4; ++pc) rt.vg[vpos++] = (int)((a << 2) | pc);
-          if (c > 0) ++a;
-        }
-      }
-      if (lane == 63) *rt.n_vg = (int)vinc;
+      if (rt.n_vg) *rt.n_vg = (int)vinc;
     }
   }
   __syncthreads();

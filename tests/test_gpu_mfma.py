@@ -49,9 +49,12 @@ def test_plan_is_mfma(name, B):
     _, _, L = gpu_layer(name)
     p = L.query_plan(B)
     assert p["path_name"] == "splitk_mfma" and p["forced"] == 0
-    # up to 16 tokens a small intermediate adds the SwiGLU launch of the K-split gate/up
-    split = B <= 16 and synth.CONFIGS[name].inter <= 256
-    assert p["kernels_per_step"] == (10 if B > 32 else (8 if B > 16 else 7 + split))
+    # a small intermediate (up to 16 tokens and over 32) adds the SwiGLU launch of the K-split
+    # gate/up; over 32 tokens an unsplit gate/up adds the shared expert's split-K launch and
+    # its SwiGLU
+    split = (B <= 16 or B > 32) and synth.CONFIGS[name].inter <= 256
+    want = (8 if B > 16 else 7) + split + (2 if B > 32 and not split else 0)
+    assert p["kernels_per_step"] == want
     assert p["oproj_splitk"] == (7 if synth.CONFIGS[name].oproj_in == 7168 else 1)
     assert p["router_splitk"] == 7
 
