@@ -368,7 +368,9 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   __shared__ float nred[(kGemvThreads / 64) * NT];
   const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * wpb + wave, nw = gridDim.x * wpb;
+  // worker ids run across the blocks first, so a short list of units (the shared expert's
+  // row pairs when its intermediate is small) is spread over the CUs
+  const int gw = wave * gridDim.x + blockIdx.x, nw = gridDim.x * wpb;
   const bool shared = ws13 != nullptr;
   const int units = E * splits;
   // router slices of this wave's units (a missing second unit re-reads the last one)
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     for (int t = 0; t < B; ++t) topk_row_lds(lg, bv, E, k, routed_scale, t, rl, sm.sel);
   }
   if (ws2 && wave > 0)
-    shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, blockIdx.x * (wpb - 1) + wave - 1,
+    shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, (wave - 1) * gridDim.x + blockIdx.x,
                                      gridDim.x * (wpb - 1), lane);
   if (gamma)
     st.template store_rmsnorm<T, NT>(lds, gamma, eps, G::K, nred);
@@ -662,7 +664,8 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     }
   };
 
-  int cur = blockIdx.x * wpb + wave;
+  // units run across the blocks first: with fewer units than waves every CU still streams
+  int cur = wave * gridDim.x + blockIdx.x;
   issue_a(cur);
   issue_b(cur);
   for (; cur < units; cur += stride) {
