@@ -739,8 +739,12 @@ hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void*
   a.K = s.Ko;
   a.chunks = mfma_oproj_splits(s);
   const int units = (s.H / 32) * a.chunks;
-  if (s.Ko == 7168) return staged_dispatch<2, 1, true>(d, a, units, st);     // 7 x 1024 k
-  if (s.Ko == 448) return staged_dispatch<2, 1, true, 64>(d, a, units, st);  // 448 = 7 x 64
+  if (s.Ko == 7168) return staged_dispatch<2, 1, true>(d, a, units, st);  // 7 x 1024 k
+  if (s.Ko == 448) {  // up to 32 tokens the whole 448 k in one stage (one weight round trip)
+    if (B <= 16) return staged_t<2, 1, 448, 1, true>(d, a, units, st);
+    if (B <= 32) return staged_t<2, 2, 448, 1, true>(d, a, units, st);
+    return staged_t<2, 4, 64, 1, true>(d, a, units, st);  // 448 = 7 x 64
+  }
   return hipErrorInvalidValue;
 }
 
