@@ -5,7 +5,8 @@
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering time
 // between operators" (router scores in MoE preparation).  Reading of the unstated math:
 // sigmoid scores, selection on score + per-expert bias (lower index first on equal keys;
-// keys are ranked on their fp64 value truncated to 43 mantissa bits),
+// a key is formed in fp64 as (1 + bias) - sigmoid(-logit), the sigmoid taken in fp32, and
+// ranked on its value truncated to 43 mantissa bits),
 // gates = selected unbiased scores / their sum * routed_scale, experts of a token listed in
 // ascending index; perm orders slots (t*k + j) by (expert, token).
 #pragma once
@@ -16,7 +17,8 @@
 namespace kk {
 
 constexpr int kMaxExperts = 512;
-constexpr int kMaxSlots = 64 * 16;  // max batch * max top-k
+constexpr int kMaxTopK = 16;
+constexpr int kMaxSlots = 64 * kMaxTopK;  // max batch * max top-k
 
 struct TopkScratch {
   int sel[kMaxSlots];                      // selected expert of each slot
@@ -50,9 +52,11 @@ __device__ inline void topk_select(const float (&l_)[kMaxM], const float (&bv)[k
     rk[m] = 0ull;
     if (64 * m < E) {  // uniform: slots past the last expert cost nothing
       const int e = lane + 64 * m;
-      const double sv = 1.0 / (1.0 + exp(-(double)l_[m]));
-      sc[m] = sv;
-      rk[m] = e < E ? rank_key(sv + (double)bv[m], e) : 0ull;
+      // t = 1 - s = sigmoid(-l) in fp32 keeps its relative precision where s saturates
+      // towards 1; the score and the key are then formed in fp64
+      const float t = 1.0f / (1.0f + expf(l_[m]));
+      sc[m] = 1.0 - (double)t;
+      rk[m] = e < E ? rank_key((1.0 + (double)bv[m]) - (double)t, e) : 0ull;
     }
   }
   // per-lane sort, descending (19-comparator odd-even merge network over 8 keys)
@@ -192,9 +196,13 @@ __device__ inline void build_tables(int B, int E, int k, const Routing& rt, Topk
   if (B == 1) {
     // one token: its k experts (ascending, one slot each) are the active list in order, and
     // positions are slots
+    int sv[kMaxTopK];  // the selected experts in registers (k <= kMaxTopK)
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) sv[j] = j < k ? sm.sel[j] : 0x7fffffff;
     for (int e = threadIdx.x; e <= E; e += blockDim.x) {
       int c = 0;
-      for (int j = 0; j < k; ++j) c += sm.sel[j] < e ? 1 : 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) c += sv[j] < e ? 1 : 0;
       rt.offsets[e] = c;
     }
     for (int j = threadIdx.x; j < k; j += blockDim.x) {
