@@ -529,10 +529,18 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
           reinterpret_cast<const u32x4*>(gr.wbase + (size_t)(tile * ROWS + rr) * K + ch * 8));
     }
   };
-  int unit = blockIdx.x;
-  if (unit >= units) return;
-  load_w(unit);
-  for (; unit < units; unit += gridDim.x) {
+  // Up to 16 tokens (every group one token tile) each block takes a contiguous run of units,
+  // so consecutive units mostly share a group, which stages its activations once per run.
+  // Beyond, units are dealt out across the blocks, which spreads the multi-tile groups.
+  const bool runs = x.B <= 16;
+  const int per = (units + gridDim.x - 1) / gridDim.x;
+  const int u0 = runs ? blockIdx.x * per : blockIdx.x;
+  const int u1 = runs ? min(units, u0 + per) : units;
+  const int step = runs ? 1 : gridDim.x;
+  if (u0 >= u1) return;
+  load_w(u0);
+  int staged = -1;  // group whose (single) token tile la holds
+  for (int unit = u0; unit < u1; unit += step) {
     const int a = unit / tiles, tile = unit - a * tiles;
     const Group gr = group_of<1>(x, a, n_groups);
 #pragma unroll
@@ -540,12 +548,13 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
       lw[rr * WP + ch] = wreg[i];
     }
-    load_w(unit + gridDim.x);
+    if (unit + step < u1) load_w(unit + step);
     const int ntt = (gr.cnt + 15) / 16;
     const float* asrc = gr.shared ? x.act_shared : reinterpret_cast<const float*>(x.act_routed);
     float* outp = gr.shared ? x.out_shared : x.out_routed;
     for (int tt = 0; tt < ntt; ++tt) {
-      {
+      if (ntt > 1 || staged != a) {
+        staged = ntt > 1 ? -1 : a;
         const int j = tid / K8, ch = tid - j * K8, jt = tt * 16 + j;
         const bool ok = jt < gr.cnt;
         const int row = ok ? (gr.shared ? jt : gr.p0 + jt) : 0;
