@@ -111,7 +111,7 @@ def test_layer_parity_mfma(name, B):
         assert torch.equal(b["out"], eager), f"replay {rep_i} differs (bitwise)"
 
 
-@pytest.mark.parametrize("B", [3, 5])
+@pytest.mark.parametrize("B", [3, 5, 16, 17, 24, 32, 33])
 def test_odd_batches_mfma(B):
     log(f"[odd-mfma] tp_rank B={B}")
     torch = _torch()
