@@ -558,18 +558,19 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nslot = B * k;
   // the logits first, by the whole block, before any weight stream competes with their loads;
-  // wave 0 requests its bias values with them
+  // the waves that run a token's selection (wave t: token t) request their bias values with
+  // them
   float bv[kMaxM];
-  if (TOPK && wave == 0) load_bias(bias, E, bv);
+  if (TOPK && wave < B) load_bias(bias, E, bv);
   if (TOPK) {
     logits_to_lds<false>(part, splits, B, E, lg);
     __syncthreads();
   }
   Stage<stage_q(NT, G::K)> st;
   st.load(u, B * G::K);
-  if (TOPK && wave == 0) {
+  if (TOPK && wave < B) {
     Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
-    for (int t = 0; t < B; ++t) topk_row_lds(lg, bv, E, k, routed_scale, t, rl, sm.sel);
+    topk_row_lds(lg, bv, E, k, routed_scale, wave, rl, sm.sel);
   }
   if (ws2 && wave > 0)
     shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, (wave - 1) * gridDim.x + blockIdx.x,
