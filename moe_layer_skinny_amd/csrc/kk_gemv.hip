@@ -781,6 +781,17 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
   // activation rows (up to 8 slots per token in registers; more are copied by a loop)
   Stage<stage_q(8 * NT, G::K)> sta;
   sta.load(A, nslot * G::K);
+  // the residual and shared-expert values of this thread's combine item, requested now (every
+  // block has at most one item per thread at these shapes; otherwise the tail loads them)
+  const bool pre = B * RB <= (int)blockDim.x;
+  float pre_h, pre_y;
+  {
+    const int i = min((int)threadIdx.x, B * RB - 1);
+    const int t = i / RB, nl = i - t * RB;
+    const size_t o = (size_t)t * H + min(row_of(nl / G::RPW, nl % G::RPW), H - 1);
+    pre_h = h32[o];
+    pre_y = ys[o];
+  }
   const int t_e = lane < n_act ? t_a : 0;  // entries past n_act are not expert ids
   const int t_lo = rt.offsets[t_e];
   const int t_cnt = rt.offsets[t_e + 1] - t_lo;
@@ -886,10 +897,10 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
     const int t = i / RB, nl = i - t * RB;
     const int n = row_of(nl / G::RPW, nl % G::RPW);
     if (n < H) {
-      float acc = h32[(size_t)t * H + n];
+      float acc = pre ? pre_h : h32[(size_t)t * H + n];
       if (n_act > 0)
         for (int j = 0; j < k; ++j) acc = fmaf(sG[t * k + j], part[sQ[t * k + j] * RB + nl], acc);
-      Elem<T>::store(out, (size_t)t * H + n, acc + ys[(size_t)t * H + n]);
+      Elem<T>::store(out, (size_t)t * H + n, acc + (pre ? pre_y : ys[(size_t)t * H + n]));
     }
   }
 }
