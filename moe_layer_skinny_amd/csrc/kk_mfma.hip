@@ -223,7 +223,7 @@ struct UnitArgs {
 // p0 + cnt - 1, `shared`) over K chunk `chunk`.  DEPTH stages of loads are kept in flight
 // (registers); a stage past the end reads the activation buffer instead (small and cache-
 // resident), so no load is branched around.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int DEPTH>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int DEPTH, bool NTW = true>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
                                             int p0, int cnt, const uint16_t* wbase,
                                             bool shared) {
@@ -280,7 +280,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     for (int i = 0; i < WLD; ++i) {
       const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
                             : reinterpret_cast<const u32x4*>(dummy);
-      wreg[slot][i] = __builtin_nontemporal_load(p);
+      wreg[slot][i] = NTW ? __builtin_nontemporal_load(p) : *p;
     }
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
@@ -595,19 +595,25 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
 
 // Split-K product with the tokens split as well: units (row tile, K chunk, 16-token quarter),
 // so that a launch over many tokens but few row tiles (the router: 12 row tiles x 7 chunks)
-// still fills the chip.  A unit's weights are read once per quarter (the later reads are
-// served by the caches); the quarters of one (tile, chunk) are consecutive units.
+// still fills the chip.  Each quarter reads the unit's weights; the quarters of one (tile,
+// chunk) run on one XCD, so all but the first are served by its L2.
 template <int KS, int NTERM, bool BF16SRC>
 __global__ __launch_bounds__(256) void mfma_token_split_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];
+  // Units run in groups of 8 (tile, chunk) pairs x nq quarters, the quarters of one pair 8
+  // units apart: blocks b and b + 8 share an XCD, so the quarters read the pair's weights
+  // through one L2 (plain loads, which allocate there) instead of once each from HBM.
   const int tiles = x.N / 32, nq = (x.B + 15) / 16;
-  const int units = tiles * x.chunks * nq;
+  const int pairs = tiles * x.chunks;
+  const int units = (pairs + 7) / 8 * 8 * nq;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int q = unit % nq, rest = unit / nq;
-    const int tile = rest / x.chunks, chunk = rest - tile * x.chunks;
+    const int grp = unit / (8 * nq), r = unit - grp * 8 * nq;
+    const int q = r / 8, tc = grp * 8 + (r & 7);
+    if (tc >= pairs) continue;
+    const int tile = tc / x.chunks, chunk = tc - tile * x.chunks;
     const int p0 = 16 * q;
-    staged_unit<2, 1, KS, NTERM, BF16SRC, 1>(x, lds, tile, chunk, p0, min(16, x.B - p0), x.w_routed,
-                                             false);
+    staged_unit<2, 1, KS, NTERM, BF16SRC, 1, false>(x, lds, tile, chunk, p0, min(16, x.B - p0),
+                                                    x.w_routed, false);
   }
 }
 
@@ -674,7 +680,7 @@ hipError_t token_split_t(const Device& d, const UnitArgs& x, hipStream_t st) {
   constexpr size_t lds = staged_lds(1, KS, NTERM);
   if (lds > 64 * 1024) allow_lds_mfma(kern);
   static thread_local int bpc = 0;
-  const int units = (x.N / 32) * x.chunks * ((x.B + 15) / 16);
+  const int units = ((x.N / 32) * x.chunks + 7) / 8 * 8 * ((x.B + 15) / 16);
   hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, x);
   return hipGetLastError();
 }
