@@ -120,3 +120,32 @@ def test_largest_routing(name, B):
                           "offsets": offsets.cpu().numpy(), "perm": perm.cpu().numpy()}, ref, B,
                          cfg.top_k, "router tables")
     assert_close(as_f64_out(out2), ref["out"], "moe out")
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_every_expert_selected(B):
+    """k = E (the dense special case): every expert is selected for every token, in index
+    order, with gates s / sum of all s; the layer output matches the oracle run with k = E."""
+    log(f"[dense] tiny_fp32 k=E B={B}")
+    import torch
+    import synth.device as sd
+    from moe_layer_skinny_amd import kk
+    cfg, w, _ = gpu_layer("tiny_fp32")
+    E = cfg.n_experts
+    kcfg = kk.make_config(cfg.hidden, cfg.oproj_in, E, E, cfg.inter, cfg.shared_inter, cfg.dtype)
+    L = kk.Layer(kcfg, w, 2)
+    try:
+        # with k = E no top-k boundary exists, so the first draw of every token serves
+        x, r, xh, rh = sd.device_tokens(cfg, B, attempts=[0] * B)
+        out = torch.empty(B, cfg.hidden, dtype=torch.float32, device="cuda")
+        idx = torch.full((B, E), -1, dtype=torch.int32, device="cuda")
+        gate = torch.zeros(B, E, dtype=torch.float32, device="cuda")
+        ws = L.new_workspace()
+        L.layer_decode(B, x, r, out, ws, idx, gate)
+        torch.cuda.synchronize()
+    finally:
+        L.close()
+    ref = O.layer_step(xh, rh, host_layer_weights("tiny_fp32"), E)
+    np.testing.assert_array_equal(idx.cpu().numpy(), np.tile(np.arange(E, dtype=np.int32), (B, 1)))
+    np.testing.assert_allclose(gate.cpu().numpy(), ref["topk_gate"], rtol=0, atol=1e-5)
+    assert_close(as_f64_out(out), ref["out"], "dense-case out")
