@@ -76,12 +76,6 @@ __device__ __forceinline__ float seg_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 // Weight-row geometry of a GEMV over rows of CPR 16-byte chunks.  A wave covers RPW rows
 // at once, SEG lanes per row (SEG = 64 for rows of >= 33 chunks); lane `sub` of a segment
 // holds chunks sub, sub + SEG, ... (CPL of them), so every wave-wide load instruction

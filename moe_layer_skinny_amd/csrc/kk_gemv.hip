@@ -95,132 +95,6 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WP
   }
 }
 
-// Rows spanning whole waves (SEG = 64): a unit is two rows whose K halves alternate with
-// their consumption, as in the routed gate/up launch (one half in flight while the other is
-// consumed; a unit past the end fetches x instead, so no load is branched around); x is
-// staged in LDS as fp32.
-template <typename T, int CPR, int NT>
-__global__ __launch_bounds__(kGemvThreads) void oproj_pipe_kernel(
-    const T* __restrict__ x, const T* __restrict__ r, const T* __restrict__ w_o,
-    float* __restrict__ h32, T* __restrict__ h_out, int H) {
-  using G = Geo<T, CPR>;
-  static_assert(G::SEG == 64 && G::EXACT, "rows must span the wave exactly");
-  constexpr int HA = (G::CPL + 1) / 2, HB = G::CPL - HA, HBX = HB > 0 ? HB : 1;
-  extern __shared__ float lds[];  // x as fp32 [NT][K]
-  const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int units = (H + 1) / 2;
-  const int stride = gridDim.x * wpb;
-  // x: the block's threads load it as 16-byte chunks first, convert after the weights are
-  // requested
-  constexpr int XQ = (NT * CPR + kGemvThreads - 1) / kGemvThreads;
-  u32x4 xv[XQ];
-#pragma unroll
-  for (int j = 0; j < XQ; ++j)
-    xv[j] = reinterpret_cast<const u32x4*>(x)[min((int)(threadIdx.x + j * blockDim.x), NT * CPR - 1)];
-
-  u32x4 ga[HA], ua[HA], gb[HBX], ub[HBX];
-  auto rows = [&](int un, const T*& p0, const T*& p1) {
-    const int n0 = 2 * un;
-    p0 = un < units ? w_o + (size_t)n0 * G::K : x;
-    p1 = (un < units && n0 + 1 < H) ? p0 + G::K : x;
-  };
-  auto issue_a = [&](int un) {
-    const T *p0, *p1;
-    rows(un, p0, p1);
-#pragma unroll
-    for (int i = 0; i < HA; ++i) {
-      ga[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p0) + lane + 64 * i);
-      ua[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p1) + lane + 64 * i);
-    }
-  };
-  auto issue_b = [&](int un) {
-    const T *p0, *p1;
-    rows(un, p0, p1);
-#pragma unroll
-    for (int i = 0; i < HB; ++i) {
-      gb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p0) + lane + 64 * (HA + i));
-      ub[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p1) + lane + 64 * (HA + i));
-    }
-  };
-  int cur = blockIdx.x * wpb + wave;
-  issue_a(cur);
-  issue_b(cur);
-#pragma unroll
-  for (int j = 0; j < XQ; ++j) {
-    const int c = threadIdx.x + j * blockDim.x;
-    if (c < NT * CPR) {
-      float f[G::EPC];
-      Elem<T>::unpack(xv[j], f);
-#pragma unroll
-      for (int h = 0; h < G::EPC / 4; ++h)
-        reinterpret_cast<float4*>(lds)[c * (G::EPC / 4) + h] =
-            float4{f[4 * h + 0], f[4 * h + 1], f[4 * h + 2], f[4 * h + 3]};
-    }
-  }
-  __syncthreads();
-  float z0[NT], z1[NT];
-  auto eat = [&](const u32x4& w0, const u32x4& w1, int j) {
-    float f0[G::EPC], f1[G::EPC];
-    Elem<T>::unpack(w0, f0);
-    Elem<T>::unpack(w1, f1);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float4* xp = reinterpret_cast<const float4*>(lds + t * G::K + (lane + 64 * j) * G::EPC);
-#pragma unroll
-      for (int h = 0; h < G::EPC / 4; ++h) {
-        const float4 v = xp[h];
-        z0[t] = fmaf(f0[4 * h + 0], v.x, z0[t]);
-        z1[t] = fmaf(f1[4 * h + 0], v.x, z1[t]);
-        z0[t] = fmaf(f0[4 * h + 1], v.y, z0[t]);
-        z1[t] = fmaf(f1[4 * h + 1], v.y, z1[t]);
-        z0[t] = fmaf(f0[4 * h + 2], v.z, z0[t]);
-        z1[t] = fmaf(f1[4 * h + 2], v.z, z1[t]);
-        z0[t] = fmaf(f0[4 * h + 3], v.w, z0[t]);
-        z1[t] = fmaf(f1[4 * h + 3], v.w, z1[t]);
-      }
-    }
-  };
-  for (; cur < units; cur += stride) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) z0[t] = z1[t] = 0.f;
-#pragma unroll
-    for (int j = 0; j < HA; ++j) {
-      eat(ga[j], ua[j], j);
-      if (NT > 1) __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    issue_a(cur + stride);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < HB; ++j) {
-      eat(gb[j], ub[j], HA + j);
-      if (NT > 1) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(z0[t]), "+v"(z1[t]));
-    __builtin_amdgcn_sched_barrier(0);
-    issue_b(cur + stride);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float v0 = seg_sum_dpp<64>(z0[t]);
-      const float v1 = seg_sum_dpp<64>(z1[t]);
-      if (lane == 63) {
-        const int n0 = 2 * cur;
-        const size_t o = (size_t)t * H + n0;
-        const float h0 = Elem<T>::load(r, o) + v0;
-        h32[o] = h0;
-        if (h_out) Elem<T>::store(h_out, o, h0);
-        if (n0 + 1 < H) {
-          const float h1 = Elem<T>::load(r, o + 1) + v1;
-          h32[o + 1] = h1;
-          if (h_out) Elem<T>::store(h_out, o + 1, h1);
-        }
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------------------ gate / up helpers
 // One gate/up row pair of one expert for the positions [p0, p1) of that expert:
 // A[p][i] = silu(W1[i] . u_t) * (W3[i] . u_t), u_t an fp32 row in LDS.
