@@ -222,7 +222,9 @@ struct UnitArgs {
 // One unit of the LDS-staged product: the tile pair `tile` of group (wbase, positions p0 ..
 // p0 + cnt - 1, `shared`) over K chunk `chunk`.  DEPTH stages of loads are kept in flight
 // (registers); a stage past the end reads the activation buffer instead (small and cache-
-// resident), so no load is branched around.
+// resident), so no load is branched around.  Weights are read with non-temporal loads, or
+// with plain (cached) loads when NTW is false, for units whose weights other blocks of the
+// same XCD read again.
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int DEPTH, bool NTW = true>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
                                             int p0, int cnt, const uint16_t* wbase,
