@@ -218,14 +218,13 @@ struct UnitArgs {
 // the end of the unit.
 //   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
 //   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
-// GSEL picks the groups a launch covers: 0 all, 1 those with <= 16 tokens, 2 the others.
 // One unit of the LDS-staged product: the tile pair `tile` of group (wbase, positions p0 ..
-// p0 + cnt - 1, `shared`) over K chunk `chunk`.  DEPTH stages of loads are kept in flight
-// (registers); a stage past the end reads the activation buffer instead (small and cache-
+// p0 + cnt - 1, `shared`) over K chunk `chunk`.  The next stage's loads are kept in flight in
+// registers; a stage past the end reads the activation buffer instead (small and cache-
 // resident), so no load is branched around.  Weights are read with non-temporal loads, or
 // with plain (cached) loads when NTW is false, for units whose weights other blocks of the
 // same XCD read again.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int DEPTH, bool NTW = true>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
                                             int p0, int cnt, const uint16_t* wbase,
                                             bool shared) {
@@ -274,15 +273,15 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     const size_t off = (size_t)src * K + kbase + ch * 8;
     asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
   }
-  u32x4 wreg[DEPTH][WLD], areg[DEPTH][ALD][AW];
+  u32x4 wreg[WLD], areg[ALD][AW];
   const void* dummy = x.act_routed;
-  auto load_stage = [&](int st, int slot) {
+  auto load_stage = [&](int st) {
     const bool live = st < nst;
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
                             : reinterpret_cast<const u32x4*>(dummy);
-      wreg[slot][i] = NTW ? __builtin_nontemporal_load(p) : *p;
+      wreg[i] = NTW ? __builtin_nontemporal_load(p) : *p;
     }
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
@@ -290,7 +289,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
                                : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
       if (!live) p = reinterpret_cast<const u32x4*>(dummy);
 #pragma unroll
-      for (int w = 0; w < AW; ++w) areg[slot][i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
+      for (int w = 0; w < AW; ++w) areg[i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
     }
   };
   f32x4 acc[2][TT];
@@ -299,11 +298,11 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto store_stage = [&](int slot) {
+  auto store_stage = [&]() {
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
-      if (q < 32 * K8) lw[rr * WP + ch] = wreg[slot][i];
+      if (q < 32 * K8) lw[rr * WP + ch] = wreg[i];
     }
     // only the group's own token slots: the others were zeroed at the start of the unit
 #pragma unroll
@@ -311,13 +310,13 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
       if (q < NTOK * K8 && aok[i]) {
         if constexpr (BF16SRC) {
-          la[ch * NTOK + j] = areg[slot][i][0];
+          la[ch * NTOK + j] = areg[i][0];
         } else {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[e] = __uint_as_float(areg[slot][i][0][e]);
-            v[4 + e] = __uint_as_float(areg[slot][i][1][e]);
+            v[e] = __uint_as_float(areg[i][0][e]);
+            v[4 + e] = __uint_as_float(areg[i][1][e]);
           }
           u32x4 terms[NTERM];
           split_terms<NTERM>(v, terms);
@@ -351,32 +350,13 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     }
   };
 
-  if constexpr (DEPTH == 1) {
-    load_stage(0, 0);
-    for (int st = 0; st < nst; ++st) {
-      store_stage(0);
-      __syncthreads();
-      if (st + 1 < nst) load_stage(st + 1, 0);
-      compute_stage();
-      __syncthreads();
-    }
-  } else {
-    load_stage(0, 0);
-    load_stage(1, 1);
-    for (int st = 0; st < nst; st += 2) {
-      store_stage(0);
-      __syncthreads();
-      load_stage(st + 2, 0);
-      compute_stage();
-      __syncthreads();
-      if (st + 1 < nst) {
-        store_stage(1);
-        __syncthreads();
-        load_stage(st + 3, 1);
-        compute_stage();
-        __syncthreads();
-      }
-    }
+  load_stage(0);
+  for (int st = 0; st < nst; ++st) {
+    store_stage();
+    __syncthreads();
+    if (st + 1 < nst) load_stage(st + 1);
+    compute_stage();
+    __syncthreads();
   }
   // sum the four waves' partial tiles in wave order, then the epilogue
   f32x4* red = reinterpret_cast<f32x4*>(lds);
@@ -451,11 +431,10 @@ __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups
 }
 
 // All MFMA launches of one token-tile width: units (group, tile pair, K chunk) over a
-// persistent grid.  GSEL picks the groups a launch covers: 0 all, 1 those with <= 16
-// tokens, 2 the others, 3 the routed ones with more than 16 tokens; 4 the routed experts cut
+// persistent grid.  GSEL picks what a launch covers: 0 every group; 4 the routed experts cut
 // into pieces of at most 16 positions (rt.vg), 5 those plus the shared expert's tokens in
 // pieces of 16 (one-tile launches over any batch).
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL, int DEPTH = 1>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
   const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
@@ -483,8 +462,7 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
         p0 = 16 * (v - nv);
         cnt = min(16, x.B - p0);
       }
-      staged_unit<MODE, 1, KS, NTERM, BF16SRC, DEPTH>(x, lds, tile, chunk, p0, cnt, gr.wbase,
-                                                      gr.shared);
+      staged_unit<MODE, 1, KS, NTERM, BF16SRC>(x, lds, tile, chunk, p0, cnt, gr.wbase, gr.shared);
     }
     return;
   }
@@ -494,11 +472,8 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
     const int rem = unit - a * tiles * chunks;
     const int tile = rem / chunks, chunk = rem - tile * chunks;
     const Group gr = group_of<MODE>(x, a, n_groups);
-    if ((GSEL == 1 && gr.cnt > 16) || (GSEL == 2 && gr.cnt <= 16) ||
-        (GSEL == 3 && (gr.cnt <= 16 || gr.shared)))
-      continue;  // block-uniform
-    staged_unit<MODE, TT, KS, NTERM, BF16SRC, DEPTH>(x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
-                                                    gr.shared);
+    staged_unit<MODE, TT, KS, NTERM, BF16SRC>(x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
+                                             gr.shared);
   }
 }
 
@@ -614,8 +589,8 @@ __global__ __launch_bounds__(256) void mfma_token_split_kernel(UnitArgs x) {
     if (tc >= pairs) continue;
     const int tile = tc / x.chunks, chunk = tc - tile * x.chunks;
     const int p0 = 16 * q;
-    staged_unit<2, 1, KS, NTERM, BF16SRC, 1, false>(x, lds, tile, chunk, p0, min(16, x.B - p0),
-                                                    x.w_routed, false);
+    staged_unit<2, 1, KS, NTERM, BF16SRC, false>(x, lds, tile, chunk, p0, min(16, x.B - p0),
+                                                 x.w_routed, false);
   }
 }
 
@@ -634,9 +609,9 @@ __global__ __launch_bounds__(256) void mfma_grouped_kernel(UnitArgs x) {
     const int tile = unit - (n_groups - 1 - a) * tiles;
     const Group gr = group_of<MODE>(x, a, n_groups);
     if (gr.cnt > 16)
-      staged_unit<MODE, TTB, KSB, 2, false, 1>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
+      staged_unit<MODE, TTB, KSB, 2, false>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
     else
-      staged_unit<MODE, 1, KS1, 2, false, 1>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
+      staged_unit<MODE, 1, KS1, 2, false>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
   }
 }
 
@@ -666,9 +641,9 @@ int resident_grid(const Device& d, Kern kern, size_t lds, int max_units, int* ca
   return grid > max_units ? max_units : grid;
 }
 
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0, int DEPTH = 1>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL = 0>
 hipError_t staged_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
-  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL, DEPTH>;
+  auto kern = mfma_staged_kernel<MODE, TT, KS, NTERM, BF16SRC, GSEL>;
   constexpr size_t lds = staged_lds(TT, KS, NTERM);
   if (lds > 64 * 1024) allow_lds_mfma(kern);
   static thread_local int bpc = 0;
