@@ -8,9 +8,11 @@ Generator: Philox4x32-10 (Salmon et al., SC'11), implemented twice from its publ
 definition -- in C for the host (``philox_host.c``) and in HIP for the device
 (``fill_device.hip``) -- so that the ~34 GB of routed-expert weights can be filled in HBM
 while the oracle regenerates exactly the experts it needs on the host.  Element n of the
-stream (key0, key1) sums the four 32-bit Philox words of counter (n, 0, 0) (an Irwin-Hall
-approximation of a normal draw), centres and scales the sum in double to the requested
-standard deviation, then rounds RNE to fp32 and, for bf16 tensors, RNE to bf16.
+stream (key0, key1) is one normal draw N(0, sigma^2): the Box-Muller transform (Box and
+Muller, 1958) of two uniforms taken from the Philox words of counter (n, 0, 0), with its
+logarithm, square root and cosine written out from single IEEE double operations in the same
+order on both sides (no fused multiply-add), so host and device give the same bits; the draw
+is rounded RNE to fp32 and, for bf16 tensors, RNE to bf16.
 
 Workload shapes follow the layer description (hidden 7168, 384 experts top-8, SwiGLU
 intermediate 2048, a tensor-parallel rank's share with o-proj slice 448 and intermediate 128,
@@ -56,12 +58,10 @@ NORM_SIGMA = 0.1
 NORM_EPS = 1e-6
 ZIPF_S = 1.2
 
-# std of the sum of four independent uniform 32-bit words
-_SUM_STD = math.sqrt((2.0**64 - 1.0) / 3.0)
-
 
 def scale_for(sigma: float) -> float:
-    return float(sigma) / _SUM_STD
+    """The generators' scale argument: the standard deviation of the normal draw itself."""
+    return float(sigma)
 
 
 @dataclass(frozen=True)
@@ -147,7 +147,8 @@ _host = None
 def _build_host_lib() -> None:
     src = os.path.join(_HERE, "philox_host.c")
     tmp = HOST_LIB + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", src, "-o", tmp])
+    subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", src,
+                           "-o", tmp])
     os.replace(tmp, HOST_LIB)
 
 
@@ -159,6 +160,7 @@ def build(force: bool = True) -> None:
         src = os.path.join(_HERE, "fill_device.hip")
         tmp = DEV_LIB + ".tmp"
         subprocess.check_call(["hipcc", "--offload-arch=gfx950", "-O3", "-shared", "-fPIC",
+                               "-ffp-contract=off",
                                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                                src, "-o", tmp], stderr=subprocess.DEVNULL)
         os.replace(tmp, DEV_LIB)
