@@ -58,8 +58,10 @@ def round_to_bf16(v) -> np.ndarray:
 
 
 def round_to_f32(v) -> np.ndarray:
-    """Each value rounded to the nearest fp32 number (ties to even), as float64."""
-    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    """Each value rounded to the nearest fp32 number (ties to even), as float64; past the
+    largest fp32 the result is +-inf."""
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
 
 
 def oproj_residual(x, r, w_o) -> np.ndarray:
@@ -231,7 +233,8 @@ def layer_step(x, r, w: LayerWeights, top_k: int, routed_scale: float = 1.0,
     gates = gates_for(s, idx, routed_scale)
     tables = routing_tables(idx, as_f64(w.bias).shape[0])
 
-    tokens = np.arange(B) if out_tokens is None else np.asarray(sorted(set(out_tokens)))
+    tokens = (np.arange(B) if out_tokens is None
+              else np.asarray(sorted(set(out_tokens)), dtype=np.int64))
     want = np.zeros(B, dtype=bool)
     want[tokens] = True
     routed = np.zeros((B, H), dtype=np.float64)

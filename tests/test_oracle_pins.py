@@ -436,6 +436,43 @@ def test_round_to_bf16_hand_values_and_bit_rounding():
     np.testing.assert_array_equal(O.round_to_bf16(a.astype(np.float64)), ref)
 
 
+def _f64_to_f32_bits_rne(v: np.ndarray) -> np.ndarray:
+    """Round float64 values in the fp32 normal range to fp32 by integer work on the float64
+    bit pattern: keep 23 of the 52 fraction bits, round the dropped 29 to nearest, ties to an
+    even kept part (a carry out of the fraction moves to the next binade by itself)."""
+    u = v.view(np.uint64)
+    sign = (u >> np.uint64(63)).astype(np.uint64)
+    exp = ((u >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64) - 1023
+    frac = u & np.uint64((1 << 52) - 1)
+    kept = frac >> np.uint64(29)
+    rest = frac & np.uint64((1 << 29) - 1)
+    half = np.uint64(1 << 28)
+    up = (rest > half) | ((rest == half) & ((kept & np.uint64(1)) == np.uint64(1)))
+    mag = ((exp + 127).astype(np.uint64) << np.uint64(23)) + kept + up.astype(np.uint64)
+    return ((sign << np.uint64(31)) | mag).astype(np.uint32)
+
+
+def test_round_to_f32_hand_values_and_bit_rounding():
+    """Ties go to the even significand (fp32 has 24 significant bits); subnormals are spaced by
+    2^-149; values past the largest fp32 overflow to inf; normal values agree with a bit-level
+    rounding of the float64 pattern."""
+    v = np.array([1.0 + 2.0**-24, 1.0 + 3 * 2.0**-24, -(1.0 + 2.0**-24 + 2.0**-50), 3.0, 0.0,
+                  2.0**-149 * 0.5, 2.0**-149 * 1.5, 2.0**-149 * 2.5, 3.5e38,
+                  3.4028234663852886e38])
+    want = [1.0, 1.0 + 2.0**-22, -(1.0 + 2.0**-23), 3.0, 0.0, 0.0, 2.0**-148, 2.0**-148,
+            np.inf, 3.4028234663852886e38]
+    assert O.round_to_f32(v).tolist() == want
+    rng = np.random.default_rng(49)
+    a = rng.normal(size=20000) * np.exp(rng.uniform(-60, 60, 20000))
+    ref = _f64_to_f32_bits_rne(a).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(O.round_to_f32(a), ref)
+    # hand-made ties in the random set's binades: exactly half a step above an fp32 value
+    t = np.float32(rng.normal(size=2000)).astype(np.float64)
+    ties = t + np.spacing(t.astype(np.float32)).astype(np.float64) / 2
+    np.testing.assert_array_equal(O.round_to_f32(ties),
+                                  _f64_to_f32_bits_rne(ties).view(np.float32).astype(np.float64))
+
+
 def test_chain_of_one_is_the_layer_and_rounds_its_output():
     rng = np.random.default_rng(51)
     H, E, k, I = 16, 8, 2, 6
