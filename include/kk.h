@@ -142,19 +142,35 @@ kk_status kk_router_topk(kk_ctx* ctx, int32_t B, const float* h32, int32_t* topk
 /* Routed experts (each selected expert's weights read once), the shared expert, and the
  * combine out = h32 + sum g y + y_shared (RNE to the config dtype), all on `stream`; the
  * experts read u = h32, or h32 normalised when the context has a norm weight.
- * Routing tables as written by kk_router_topk for the same B; tables that are not a valid
- * routing leave the routed part out (no out-of-bounds access) -- undefined output.
- * "Recovering time between operators": selected experts; shared expert on another stream. */
+ * Routing tables as written by kk_router_topk for the same B.  A device-side check runs before
+ * any weight is read: expert_offsets non-decreasing from 0 to B*k with at most B slots per
+ * expert, perm a permutation of the B*k slots, each expert's slots in ascending token order,
+ * and topk_idx of every slot naming the expert whose perm range holds it.  Tables that fail
+ * leave the routed part out (out = h32 + y_shared, no out-of-bounds access) and record why in
+ * ws: kk_routing_status reports it.  (The call itself returns as soon as the work is enqueued.)
+ * "Recovering time between operators": selected experts; shared expert on another stream.
+ * "Faster code needs targeted validation": a path that silently falls back gives no evidence,
+ * so the caller can always tell a dropped MoE part from a computed one. */
 kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t* topk_idx,
                         const float* topk_gate, const int32_t* expert_offsets, const int32_t* perm,
                         void* out, void* ws, kk_stream stream);
+
+/* Result of the table check of the last kk_moe_decode that used workspace ws: waits for
+ * `stream` (a host synchronisation; enqueue nothing that changes ws in between), then returns
+ * KK_OK when the tables were a valid routing, else KK_ERR_INVALID_ARG with kk_last_error()
+ * naming each rule they broke (that call's routed part was left out of its output).  Other ops
+ * do not update the record.  "Faster code needs targeted validation": no silent fallback. */
+kk_status kk_routing_status(kk_ctx* ctx, const void* ws, kk_stream stream);
 
 /* The whole step: o-proj + residual (+ norm), router logits, top-k || shared expert gate/up,
  * routed gate/up, down-projection with the combine (batch 1-2: four launches on `stream`, the
  * norm recomputed inside the launches that read u; the split-K MFMA path for larger batches,
  * the norm fused into the o-proj's reduce: see kk_query_plan).  topk_idx / topk_gate are optional
  * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
- * first use for these (B, pointers, stream, flags) and replayed afterwards. */
+ * first use for these (B, pointers, stream, flags, planned path) and replayed afterwards.
+ * "Recovering time between operators": the o-proj fused with the residual processing, router
+ * scores in the MoE preparation, the selected experts and the shared expert, with the kernel
+ * choice depending on the batch (small-matrix kernels at batch 1-2, split-K above). */
 kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* resid, void* out,
                           int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
                           uint32_t flags);
@@ -172,6 +188,15 @@ kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* res
 kk_status kk_chain_decode(kk_ctx* const* ctx, int32_t L, int32_t B, const void* const* x,
                           const void* resid, void* const* out, void* ws, kk_stream stream,
                           uint32_t flags);
+/* Test hook for stream hazards: a one-wave kernel that waits `microseconds` (0..10000; 0
+ * removes it) of the device's constant-rate clock is enqueued before every later step's work on
+ * the caller's stream (which = 0, ahead of the o-proj) or on the auxiliary stream right after it
+ * waits for the fork (which = 1: the KK_TWO_STREAM shared expert, the KK_PREFETCH reads).  A
+ * missing cross-stream wait then shows as changed output bits.  Every delay kernel ends after
+ * its time (or after about a second of sleeps at most).  "Faster code needs targeted
+ * validation": reads moved before a synchronisation wait escape ordinary functional tests. */
+kk_status kk_set_stream_delay(kk_ctx* ctx, int32_t which, float microseconds);
+
 /* Per-kernel timing of eager (non-graph) launches: when enabled, every kernel the context
  * launches is bracketed by HIP events on its own stream.  kk_read_kernel_timing waits for
  * the recorded events and returns up to `cap` (name, milliseconds) records of the launches

@@ -40,15 +40,15 @@ kk_status hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxBatch = 64;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 512;
-constexpr int kMaxOprojSplits = 16;
-constexpr int kMaxRouterSplits = 32;
+constexpr int kMaxOprojSplits = 8;   // o-proj K chunks (7 on the split-K path)
+constexpr int kMaxRouterSplits = 8;  // router logit K chunks (7, or 1 for the fp32 layer)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace carve-up (offsets in bytes from ws, each 256-byte aligned).
 struct Layout {
   size_t h32, u32, logit_part, topk_idx, topk_gate, offsets, perm, inv_perm, act, n_act, vg, n_vg,
-      A, As, Y, ys, oproj_part, total;
+      status, A, As, Y, ys, oproj_part, total;
 };
 
 kk::Shape to_shape(const kk_config& c) {
@@ -67,7 +67,7 @@ Layout make_layout(const kk_config& c, int Bm) {
   const size_t slots = (size_t)Bm * c.top_k;
   L.h32 = take((size_t)Bm * c.hidden * 4);
   L.u32 = take((size_t)Bm * c.hidden * 4);  // normalised h (split-K path with a norm)
-  L.logit_part = take((size_t)kMaxRouterSplits * Bm * c.n_experts * 4);
+  L.logit_part = take((size_t)kMaxRouterSplits * Bm * c.n_experts * 4);  // [splits][Bm][E]
   L.topk_idx = take(slots * 4);
   L.topk_gate = take(slots * 4);
   L.offsets = take((size_t)(c.n_experts + 1) * 4);
@@ -77,6 +77,7 @@ Layout make_layout(const kk_config& c, int Bm) {
   L.n_act = take(16);
   L.vg = take((size_t)(c.n_experts + 64) * 4);  // pieces of <= 16 positions (<= E + B*k/16)
   L.n_vg = take(16);
+  L.status = take(16);  // check of caller-supplied routing tables (kk_moe_decode)
   L.A = take(slots * c.inter * 4);
   L.As = take((size_t)Bm * c.shared_inter * 4);
   L.Y = take(slots * c.hidden * 4);
@@ -149,6 +150,7 @@ struct TimingRec {
 struct GraphEntry {
   int B;
   uint32_t flags;
+  int path;  // the plan the step was captured with (KK_FORCE_PLAN may change it)
   const void *x, *r, *out, *idx, *gate, *ws;
   hipStream_t stream;
   hipGraphExec_t exec;
@@ -157,7 +159,7 @@ struct GraphEntry {
 
 // A captured chain of layers (kept by its first context).
 struct ChainGraph {
-  std::vector<uintptr_t> key;  // context serials, x[], out[], resid, ws, stream
+  std::vector<uintptr_t> key;  // context serials, x[], out[], plan paths, resid, ws, stream
   int B;
   uint32_t flags;
   hipGraphExec_t exec;
@@ -182,6 +184,8 @@ struct kk_ctx {
   std::vector<ChainGraph> chains;
   unsigned long long clock = 0;
   bool timing = false;
+  long long wall_khz = 0;        // constant-rate device clock, for the delay test hook
+  long long delay_ticks[2] = {0, 0};  // main stream / auxiliary stream delays (test hook)
   std::vector<TimingRec> trecs;
   std::vector<hipEvent_t> tpool;
 };
@@ -272,6 +276,7 @@ struct WsPtrs {
   int32_t* n_act;
   int32_t* vg;
   int32_t* n_vg;
+  int32_t* status;
   float* A;
   float* As;
   float* Y;
@@ -279,13 +284,12 @@ struct WsPtrs {
   float* oproj_part;
 };
 
-WsPtrs carve(const kk_ctx* c, void* ws) {
+WsPtrs carve(const Layout& L, void* ws) {
   char* b = (char*)ws;
-  const Layout& L = c->L;
   return WsPtrs{(float*)(b + L.h32),     (float*)(b + L.u32),        (float*)(b + L.logit_part), (int32_t*)(b + L.topk_idx),
                 (float*)(b + L.topk_gate), (int32_t*)(b + L.offsets),  (int32_t*)(b + L.perm),
                 (int32_t*)(b + L.inv_perm), (int32_t*)(b + L.act),    (int32_t*)(b + L.n_act),
-                (int32_t*)(b + L.vg),       (int32_t*)(b + L.n_vg),
+                (int32_t*)(b + L.vg),       (int32_t*)(b + L.n_vg),  (int32_t*)(b + L.status),
                 (float*)(b + L.A),         (float*)(b + L.As),         (float*)(b + L.Y),
                 (float*)(b + L.ys),         (float*)(b + L.oproj_part)};
 }
@@ -479,6 +483,7 @@ kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
   const size_t eb = sh.dtype == 1 ? 2 : 4;
   KK_HIP(hipEventRecord(o->ev_fork, s), "prefetch fork event");
   KK_HIP(hipStreamWaitEvent(o->aux, o->ev_fork, 0), "prefetch fork wait");
+  KK_HIP(kk::launch_delay(o->delay_ticks[1], o->aux), "delay launch");
   const struct {
     const void* p;
     size_t bytes;
@@ -496,9 +501,10 @@ kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
                         float* gate, void* ws, hipStream_t s, bool two_stream, int path,
                         const PrefetchNext* pf = nullptr) {
-  WsPtrs p = carve(c, ws);
+  WsPtrs p = carve(c->L, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
+  KK_HIP(kk::launch_delay(c->delay_ticks[0], s), "delay launch");
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
   if (pf && (st = enqueue_prefetch(*pf, s)) != KK_OK) return st;
@@ -518,6 +524,7 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
   // shared expert's gate/up on the auxiliary stream, joined before the routed gate/up
   KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
   KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
+  KK_HIP(kk::launch_delay(c->delay_ticks[1], c->aux), "delay launch");
   st = enqueue_shared_gateup(c, B, p.h32, rt, p.As, c->aux);
   if (st != KK_OK) return st;
   KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
@@ -619,6 +626,9 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device);
     if (e != hipSuccess) return bail(e, "LDS size");
     c->dev = kk::Device{ncu, lds};
+    int wall = 0;
+    if (hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, c->device) == hipSuccess)
+      c->wall_khz = wall;
     e = hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking);
     if (e != hipSuccess) return bail(e, "aux stream");
     e = hipEventCreateWithFlags(&c->ev_fork, hipEventDisableTiming);
@@ -667,7 +677,7 @@ kk_status kk_oproj_residual(kk_ctx* c, int32_t B, const void* x, const void* res
     if (h_out && misaligned(h_out)) return fail(KK_ERR_INVALID_ARG, "h_out is not 16-byte aligned");
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
-    WsPtrs p = carve(c, ws);
+    WsPtrs p = carve(c->L, ws);
     return enqueue_oproj(c, B, x, resid, h32, h_out, p.oproj_part, nullptr, plan.path,
                          (hipStream_t)stream);
   } catch (...) {
@@ -688,7 +698,7 @@ kk_status kk_router_topk(kk_ctx* c, int32_t B, const float* h32, int32_t* topk_i
     KK_PTR(perm, "perm");
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
-    WsPtrs p = carve(c, ws);
+    WsPtrs p = carve(c->L, ws);
     kk::Routing rt{topk_idx, topk_gate, expert_offsets, perm, p.inv_perm, p.act, p.n_act, p.vg,
                    p.n_vg};
     if (plan.path == KK_PATH_SPLITK_MFMA) {
@@ -721,9 +731,9 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    WsPtrs p = carve(c, ws);
+    WsPtrs p = carve(c->L, ws);
     kk::Routing rt{(int32_t*)topk_idx, (float*)topk_gate, (int32_t*)expert_offsets,
-                   (int32_t*)perm, p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
+                   (int32_t*)perm, p.inv_perm, p.act, p.n_act, p.vg, p.n_vg, p.status};
     KK_HIP(timed(c, K_PREP, s, [&] { return kk::launch_moe_prep(c->shape, B, rt, s); }),
            "moe prep launch");
     if (plan.path == KK_PATH_SPLITK_MFMA) {
@@ -736,6 +746,43 @@ kk_status kk_moe_decode(kk_ctx* c, int32_t B, const float* h32, const int32_t* t
     return enqueue_routed_and_combine(c, B, h32, rt, p, nullptr, out, s);
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_moe_decode");
+  }
+}
+
+kk_status kk_routing_status(kk_ctx* c, const void* ws, kk_stream stream) {
+  try {
+    if (!c) return fail(KK_ERR_INVALID_ARG, "context is NULL");
+    if (!ws) return fail(KK_ERR_WORKSPACE, "workspace is NULL");
+    if (misaligned(ws, 256)) return fail(KK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != c->device)
+      return fail(KK_ERR_INVALID_ARG, "current device %d is not the context's device %d", dev,
+                  c->device);
+    hipStream_t s = (hipStream_t)stream;
+    int32_t bits = 0;
+    KK_HIP(hipMemcpyAsync(&bits, (const char*)ws + c->L.status, sizeof bits, hipMemcpyDeviceToHost,
+                          s),
+           "status read");
+    KK_HIP(hipStreamSynchronize(s), "status sync");
+    if (bits == 0) return KK_OK;
+    std::string why;
+    const struct {
+      int bit;
+      const char* text;
+    } reasons[] = {
+        {kk::kRoutingOffsets, "expert_offsets not non-decreasing from 0 to B*k, or an expert with "
+                              "more than B slots"},
+        {kk::kRoutingPermRange, "a perm entry outside 0..B*k-1"},
+        {kk::kRoutingPermDup, "perm lists a slot twice (not a permutation)"},
+        {kk::kRoutingOrder, "an expert's slots are not in ascending token order"},
+        {kk::kRoutingIdx, "topk_idx of a slot names another expert than the perm range it is in"}};
+    for (const auto& r : reasons)
+      if (bits & r.bit) why += std::string(why.empty() ? "" : "; ") + r.text;
+    return fail(KK_ERR_INVALID_ARG,
+                "kk_moe_decode was given invalid routing tables (%s); its routed part was left out",
+                why.c_str());
+  } catch (...) {
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_routing_status");
   }
 }
 
@@ -763,8 +810,8 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
     ++c->clock;
     for (auto& g : c->graphs) {
-      if (g.B == B && g.flags == flags && g.x == x && g.r == resid && g.out == out && g.idx == topk_idx &&
-          g.gate == topk_gate && g.ws == ws && g.stream == s) {
+      if (g.B == B && g.flags == flags && g.path == plan0.path && g.x == x && g.r == resid &&
+          g.out == out && g.idx == topk_idx && g.gate == topk_gate && g.ws == ws && g.stream == s) {
         g.uses = c->clock;
         KK_HIP(hipGraphLaunch(g.exec, s), "graph launch");
         return KK_OK;
@@ -791,7 +838,7 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     (void)hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "graph instantiate");
     c->graphs.push_back(
-        GraphEntry{B, flags, x, resid, out, topk_idx, topk_gate, ws, s, exec, c->clock});
+        GraphEntry{B, flags, plan0.path, x, resid, out, topk_idx, topk_gate, ws, s, exec, c->clock});
     KK_HIP(hipGraphLaunch(exec, s), "graph launch");
     return KK_OK;
   } catch (...) {
@@ -824,10 +871,16 @@ kk_status kk_chain_decode(kk_ctx* const* ctx, int32_t L, int32_t B, const void* 
     if (!s) return fail(KK_ERR_INVALID_ARG, "KK_GRAPH needs a non-null stream");
     kk_ctx* c0 = ctx[0];
     std::vector<uintptr_t> key;
-    key.reserve(3 * L + 3);
+    key.reserve(4 * L + 3);
     for (int l = 0; l < L; ++l) key.push_back((uintptr_t)ctx[l]->serial);
     for (int l = 0; l < L; ++l) key.push_back((uintptr_t)x[l]);
     for (int l = 0; l < L; ++l) key.push_back((uintptr_t)out[l]);
+    for (int l = 0; l < L; ++l) {  // the plans the chain is captured with
+      kk_plan plan;
+      kk_status st = plan_for(ctx[l], B, &plan);
+      if (st != KK_OK) return st;
+      key.push_back((uintptr_t)plan.path);
+    }
     key.push_back((uintptr_t)resid);
     key.push_back((uintptr_t)ws);
     key.push_back((uintptr_t)s);
@@ -865,6 +918,17 @@ kk_status kk_chain_decode(kk_ctx* const* ctx, int32_t L, int32_t B, const void* 
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_chain_decode");
   }
+}
+
+kk_status kk_set_stream_delay(kk_ctx* c, int32_t which, float microseconds) {
+  if (!c) return fail(KK_ERR_INVALID_ARG, "context is NULL");
+  if (which != 0 && which != 1) return fail(KK_ERR_INVALID_ARG, "which must be 0 (main) or 1 (auxiliary)");
+  if (!(microseconds >= 0.f && microseconds <= 10000.f))
+    return fail(KK_ERR_INVALID_ARG, "delay must be 0..10000 microseconds");
+  if (microseconds > 0.f && c->wall_khz <= 0)
+    return fail(KK_ERR_UNSUPPORTED, "the device reports no constant-rate clock");
+  c->delay_ticks[which] = (long long)((double)microseconds * (double)c->wall_khz / 1000.0);
+  return KK_OK;
 }
 
 kk_status kk_set_kernel_timing(kk_ctx* c, int32_t enable) {

@@ -1,12 +1,11 @@
 // GEMV path of the decode-layer step (batch 1-2): every weight row is streamed from HBM
 // once with 128-bit non-temporal loads, each row's dot product finished with a wavefront
-// shuffle reduction.  One stream, six launches per step:
+// (DPP) reduction.  One stream, four launches per step:
 //   1. o-proj + residual                     (activations held in registers)
-//   2. router logits (split-K partials)         ||  shared expert gate/up, first half
-//   3. top-k / gates / routing tables (block 0)  ||  shared expert gate/up, second half
-//   4. routed gate/up over the active experts
-//   5. routed + shared down-projection, one contiguous run of one expert's rows per unit
-//   6. weighted combine into the residual
+//   2. router logits (K-slice partials)      ||  shared expert gate/up
+//   3. top-k, gates and routing tables (every block, from the partials)  ||  shared expert
+//      down-projection; then the routed gate/up over the active experts
+//   4. routed down-projection with the weighted combine into the residual
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
 // time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
@@ -290,6 +289,15 @@ __global__ __launch_bounds__(256) void prefetch_kernel(const u32x4* __restrict__
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   asm volatile("" ::"v"(acc));  // the loads stay; nothing is stored
+}
+
+// ------------------------------------------------------------------------------ delay
+// Waits `ticks` of the constant-rate device clock, sleeping between reads, then returns; the
+// loop also stops after 2^22 sleeps (about a second), so the wave ends even if the clock
+// stalls.  A test hook: placed first on one stream, it lets the other run ahead.
+__global__ __launch_bounds__(64) void delay_kernel(long long ticks) {
+  const long long t0 = wall_clock64();
+  for (int i = 0; i < (1 << 22) && wall_clock64() - t0 < ticks; ++i) __builtin_amdgcn_s_sleep(8);
 }
 
 // ------------------------------------------------------------------------------ top-k, large batch
@@ -781,28 +789,59 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
 
 // ------------------------------------------------------------------------------ prep
 // act / n_act / inv_perm (and the pieces of at most 16 positions) from expert_offsets + perm
-// supplied by the caller.  Tables that are not a valid routing of nslots slots of B tokens
-// (offsets not non-decreasing from 0 to nslots, more than B positions for one expert, perm
-// entries out of range) set n_act = 0 and no pieces, so no kernel indexes through them.
-__global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, int B, Routing rt) {
+// supplied by the caller, after checking that they are a routing of nslots = B * k slots as
+// kk_router_topk writes one: offsets non-decreasing from 0 to nslots with at most B positions
+// per expert; perm a permutation of the slots; within each expert the slots in ascending
+// token order (so no token twice); and topk_idx of every slot naming the expert whose range
+// holds it.  Invalid tables set n_act = 0 and no pieces, so no kernel indexes through them,
+// and write the reasons (kRouting* bits) to rt.status; valid ones write status 0.
+// One wave (64 threads).
+__global__ __launch_bounds__(64) void moe_prep_kernel(int E, int k, int nslots, int B, Routing rt) {
+  __shared__ uint32_t seen[kMaxSlots / 32];
   const int lane = threadIdx.x;
   const int per = (E + 63) / 64;
-  bool ok = true;
+  for (int i = lane; i < kMaxSlots / 32; i += 64) seen[i] = 0u;
+  __syncthreads();
+  int bad = 0;
   int lf = 0;
   for (int q = 0; q < per; ++q) {
     const int e = lane * per + q;
     if (e < E) {
       const int a = rt.offsets[e], b = rt.offsets[e + 1];
-      ok = ok && a >= 0 && b >= a && b <= nslots && b - a <= B;  // <= B tokens per expert
+      if (!(a >= 0 && b >= a && b <= nslots && b - a <= B)) bad |= kRoutingOffsets;
       if (b > a) ++lf;
     }
   }
-  if (lane == 0) ok = ok && rt.offsets[0] == 0 && rt.offsets[E] == nslots;
+  if (lane == 0 && (rt.offsets[0] != 0 || rt.offsets[E] != nslots)) bad |= kRoutingOffsets;
   for (int p = lane; p < nslots; p += 64) {
     const int v = rt.perm[p];
-    ok = ok && v >= 0 && v < nslots;
+    if (v < 0 || v >= nslots) {
+      bad |= kRoutingPermRange;
+    } else {
+      const uint32_t bit = 1u << (v & 31);
+      if (atomicOr(&seen[v >> 5], bit) & bit) bad |= kRoutingPermDup;
+    }
   }
-  const bool all_ok = __all(ok);
+  // each expert's slots: ascending tokens, topk_idx naming that expert (only over ranges the
+  // offsets check has passed, so every position read is in 0..nslots-1)
+  if (!(bad & kRoutingOffsets)) {
+    for (int q = 0; q < per; ++q) {
+      const int e = lane * per + q;
+      if (e < E) {
+        int prev = -1;
+        for (int p = rt.offsets[e]; p < rt.offsets[e + 1]; ++p) {
+          const int v = rt.perm[p];
+          if (v < 0 || v >= nslots) continue;  // reported above
+          const int t = v / k;
+          if (t <= prev) bad |= kRoutingOrder;
+          prev = t;
+          if (rt.topk_idx[v] != e) bad |= kRoutingIdx;
+        }
+      }
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) bad |= __shfl_xor(bad, off, 64);
+  const bool all_ok = bad == 0;
   int inc = lf;
   for (int off = 1; off < 64; off <<= 1) {
     const int v = __shfl_up(inc, off, 64);
@@ -817,6 +856,7 @@ __global__ __launch_bounds__(64) void moe_prep_kernel(int E, int nslots, int B, 
     for (int p = lane; p < nslots; p += 64) rt.inv_perm[rt.perm[p]] = p;
   }
   if (lane == 63) *rt.n_act = all_ok ? inc : 0;
+  if (lane == 0 && rt.status) *rt.status = bad;
   if (rt.vg) {
     // pieces of at most 16 positions per active expert, in expert order (none if invalid)
     int vt = 0;
@@ -1076,8 +1116,15 @@ hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_delay(long long ticks, hipStream_t st) {
+  if (ticks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(delay_kernel, dim3(1), dim3(64), 0, st, ticks);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st) {
-  hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(64), 0, st, s.E, B * s.k, B, rt);
+  if (B * s.k > kMaxSlots) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_prep_kernel, dim3(1), dim3(64), 0, st, s.E, s.k, B * s.k, B, rt);
   return hipGetLastError();
 }
 

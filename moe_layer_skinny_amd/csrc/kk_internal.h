@@ -1,4 +1,5 @@
-// Internal interface between the host API (kk_api.cpp) and the kernels (kk_kernels.hip).
+// Internal interface between the host API (kk_api.cpp) and the kernels (kk_gemv.hip,
+// kk_mfma.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,7 +37,19 @@ struct Routing {
   // entry = (index into act) << 2 | piece (positions offsets[e] + 16 piece ..)
   int32_t* vg = nullptr;    // [E + 64]
   int32_t* n_vg = nullptr;  // [1]
+  // check of caller-supplied tables (kk_moe_decode): 0 valid, else kRouting* bits
+  int32_t* status = nullptr;  // [1]
 };
+
+// Bits of Routing::status: what made caller-supplied tables invalid.
+constexpr int kRoutingOffsets = 1;    // offsets not non-decreasing from 0 to B*k, or an
+                                      // expert with more than B positions
+constexpr int kRoutingPermRange = 2;  // a perm entry outside 0..B*k-1
+constexpr int kRoutingPermDup = 4;    // a slot listed twice in perm (not a permutation)
+constexpr int kRoutingOrder = 8;      // an expert's slots not in ascending token order
+                                      // (or one token twice)
+constexpr int kRoutingIdx = 16;       // topk_idx of a slot names another expert than the
+                                      // range of perm it sits in
 
 // RMSNorm between the residual add and the router / experts:
 // u = h * gamma / sqrt(mean(h^2) + eps); gamma == nullptr: none, u = h.
@@ -106,10 +119,15 @@ hipError_t launch_tables(const Shape& s, int B, const Routing& rt, hipStream_t s
 hipError_t launch_topk_tables(const Shape& s, int B, const float* part, int splits,
                               const float* bias, const Routing& rt, hipStream_t st);
 
+// One wave that waits `ticks` of the constant-rate device clock (bounded; nothing if <= 0).
+hipError_t launch_delay(long long ticks, hipStream_t st);
+
 // Reads `bytes` (a multiple of 16) at p once with cache-allocating loads and discards them.
 hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStream_t st);
 
-// act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode).
+// act / n_act / inv_perm from caller-provided offsets + perm (standalone kk_moe_decode), after
+// checking the tables; invalid tables give n_act = 0 (routed part left out) and the reason in
+// rt.status.
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
 
 // ---- split-K MFMA path (batch 3..64) ---------------------------------------------------

@@ -10,12 +10,18 @@
 // NTERM bf16 terms hi + lo (+ lo2) whose sum reproduces them (to 2^-17 relative with two
 // terms, exactly with three), so the products keep fp32-level accuracy; x is already bf16.
 //
-// Launches of one step:
-//   1. o-proj partials over 7 K chunks (32 rows x one chunk per block unit)
-//   2. reduce: h32 = resid + sum of chunks (fixed order), optional h_out
-//   3. router logit partials (three-term h32), then the top-k launch
+// Launches of one step (7 to 10, by batch and intermediate size; kk_query_plan counts them):
+//   1. o-proj partials over 7 K chunks (32 rows x one chunk per block unit; one chunk for a
+//      448-wide input slice)
+//   2. reduce: h32 = resid + sum of chunks (fixed order), optional h_out (with an RMSNorm the
+//      reduce also writes u32 = norm(h32))
+//   3. router logit partials (three-term h32), then the top-k: one launch with the routing
+//      tables up to 16 tokens, else a top-k launch and a tables launch
 //   4. grouped gate/up over the active experts + the shared expert, one (expert, 16 gate
-//      rows, 16 up rows) unit per block over the whole K; SwiGLU epilogue -> A (fp32)
+//      rows, 16 up rows) unit per block over the whole K; SwiGLU epilogue -> A (fp32).  Small
+//      intermediates split every group over K chunks and add a SwiGLU launch that sums them;
+//      over 32 tokens the shared expert's gate/up is a split-K launch of its own plus that
+//      SwiGLU launch
 //   5. grouped down-projection the same way -> Y (per position) and ys (shared)
 //   6. the combine launch shared with the GEMV path
 //

@@ -69,9 +69,11 @@ def lib():
             "kk_oproj_residual": (i32, [vp, i32, vp, vp, vp, vp, vp, vp]),
             "kk_router_topk": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "kk_moe_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+            "kk_routing_status": (i32, [vp, vp, vp]),
             "kk_layer_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, u32]),
             "kk_chain_decode": (i32, [ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp), vp,
                                       ctypes.POINTER(vp), vp, vp, u32]),
+            "kk_set_stream_delay": (i32, [vp, i32, ctypes.c_float]),
             "kk_set_kernel_timing": (i32, [vp, i32]),
             "kk_read_kernel_timing": (i32, [vp, ctypes.POINTER(ctypes.c_char_p),
                                             ctypes.POINTER(ctypes.c_float), i32,
@@ -184,11 +186,20 @@ class Layer:
                                    _ptr(expert_offsets), _ptr(perm), _ptr(out), _ptr(ws),
                                    _stream(stream)))
 
+    def routing_status(self, ws, stream=None):
+        """Raises KKError(KK_ERR_INVALID_ARG) if the last moe_decode on ws was given invalid
+        routing tables (waits for the stream)."""
+        _check(lib().kk_routing_status(self._h, _ptr(ws), _stream(stream)))
+
     def layer_decode(self, B, x, resid, out, ws, topk_idx=None, topk_gate=None, stream=None,
                      graph=False, two_stream=False):
         flags = (KK_GRAPH if graph else 0) | (KK_TWO_STREAM if two_stream else 0)
         _check(lib().kk_layer_decode(self._h, B, _ptr(x), _ptr(resid), _ptr(out), _ptr(topk_idx),
                                      _ptr(topk_gate), _ptr(ws), _stream(stream), flags))
+
+    def set_stream_delay(self, which: int, microseconds: float):
+        """Test hook: a bounded wait first on the main (0) or auxiliary (1) stream of each step."""
+        _check(lib().kk_set_stream_delay(self._h, which, float(microseconds)))
 
     def set_kernel_timing(self, enable: bool):
         _check(lib().kk_set_kernel_timing(self._h, 1 if enable else 0))

@@ -201,33 +201,76 @@ def test_device_side_argument_errors():
     assert e.value.status == kk.KK_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("B", [2, 8])
-def test_invalid_tables_leave_routed_part_out(B):
-    """kk_moe_decode validates caller-supplied tables on the device: offsets that do not end at
-    B*k mark the routing invalid, no routed expert is read, and out = h + shared expert(h)."""
-    log(f"[invalid-tables] tp_rank B={B}")
+def _break_tables(kind, idx, offsets, perm, B, k):
+    """Turn valid routing tables (host copies) into tables that break one rule."""
+    idx, offsets, perm = idx.copy(), offsets.copy(), perm.copy()
+    if kind == "offsets":  # the last offset past B*k
+        offsets[-1] = B * k + 5
+    elif kind == "range":  # a perm entry out of range
+        perm[3] = -7
+    elif kind == "dup":  # one slot listed twice (another one missing)
+        perm[1] = perm[0]
+    elif kind == "order":  # two tokens of one expert in descending order
+        counts = np.diff(offsets)
+        e = int(np.nonzero(counts >= 2)[0][0])
+        p0 = offsets[e]
+        perm[p0], perm[p0 + 1] = perm[p0 + 1], perm[p0]
+    elif kind == "idx":  # a slot's topk_idx names an expert its token did not pick
+        row = set(idx[0].tolist())
+        idx[0, 0] = next(e for e in range(len(offsets) - 1) if e not in row)
+    else:
+        raise ValueError(kind)
+    return idx, offsets, perm
+
+
+INVALID = [(2, "offsets"), (2, "range"), (2, "dup"), (2, "idx"), (8, "offsets"), (8, "dup"),
+           (8, "order"), (8, "idx")]
+
+
+@pytest.mark.parametrize("B,kind", INVALID)
+def test_invalid_tables_are_reported(B, kind):
+    """kk_moe_decode checks caller-supplied tables on the device before reading any routed
+    weight.  Tables that break a rule leave the routed part out (out = h + shared expert(h), no
+    out-of-range access) and kk_routing_status reports KK_ERR_INVALID_ARG naming the rule;
+    valid tables report KK_OK and give the full step."""
+    log(f"[invalid-tables] tp_rank B={B} {kind}")
     torch = _torch()
     import synth.device as sd
     import oracle as O
+    from moe_layer_skinny_amd import kk
     from tests.gpu_common import host_layer_weights
     cfg, _, L = gpu_layer("tp_rank")
+    k = cfg.top_k
     ref = oracle_step("tp_rank", B)
     x, r, _, _ = sd.device_tokens(cfg, B)
     b = _bufs(cfg, B)
     ws = L.new_workspace()
     L.oproj_residual(B, x, r, b["h32"], ws)
-    b["offsets"].zero_()
-    b["offsets"][-1] = B * cfg.top_k + 5
-    b["perm"].fill_(-7)
-    b["idx"].zero_()
-    b["gate"].fill_(0.5)
+    L.router_topk(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], ws)
     L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws)
-    torch.cuda.synchronize()
+    L.routing_status(ws)  # valid tables: no error
+    assert_close(as_f64_out(b["out"]), ref["out"], "out with valid tables")
+    idx, offsets, perm = _break_tables(kind, b["idx"].cpu().numpy(), b["offsets"].cpu().numpy(),
+                                       b["perm"].cpu().numpy(), B, k)
+    b["idx"].copy_(torch.from_numpy(idx))
+    b["offsets"].copy_(torch.from_numpy(offsets))
+    b["perm"].copy_(torch.from_numpy(perm))
+    L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws)
+    with pytest.raises(kk.KKError) as e:
+        L.routing_status(ws)
+    assert e.value.status == kk.KK_ERR_INVALID_ARG
+    words = {"offsets": "expert_offsets", "range": "outside", "dup": "twice", "order": "ascending",
+             "idx": "topk_idx"}
+    assert words[kind] in str(e.value), str(e.value)
     w = host_layer_weights("tp_rank")
     ws13, ws2 = w.shared()
     expect = ref["h"] + O.swiglu_expert(ref["h"], ws13, ws2)
     rep = assert_close(as_f64_out(b["out"]), expect, "out without routed experts")
-    log(f"[invalid-tables] B={B}: {rep}")
+    log(f"[invalid-tables] B={B} {kind}: {e.value}; {rep}")
+    # the next valid call clears the record
+    L.router_topk(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], ws)
+    L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws)
+    L.routing_status(ws)
 
 
 @pytest.mark.parametrize("B", [1, 8, 64])
