@@ -1,0 +1,114 @@
+"""GPU parity of the full-size layer (hidden 7168, 384 experts top-8, intermediate 2048) at the
+batches where its kernel instances change, against the fp64 oracle, and the batch invariance
+of each token's routing.
+
+The layer is the uniform-bias workload's, created for up to 64 tokens; a batch of B tokens is
+token seeds 0..B-1.  The oracle's routing and h are computed in the test; its outputs come
+from the file tests/golden/make_expected.py wrote for all 64 tokens (a token's output does not
+depend on the rest of its batch, which the oracle's own pins check).  Instances covered:
+batch 2 on the GEMV path (two-token o-proj staged through LDS, two-token gate/up and
+down-projection with the combine), batches 17-32 on the split-K path (two-tile o-proj over the
+full K, one-tile gate/up over the routed and shared pieces, mixed one/two-tile down-projection).
+("Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Faster code needs
+targeted validation": operator-level checks over shapes and inputs; sweeps that cover batches.)
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_common import (as_f64_out, assert_close, assert_routing_equal, golden_out,
+                              gpu_layer, log, oracle_step)
+
+pytestmark = pytest.mark.gpu
+
+NAME = "full_b64"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bufs(cfg, B):
+    torch = _torch()
+    return {
+        "h32": torch.empty(B, cfg.hidden, dtype=torch.float32, device="cuda"),
+        "out": torch.empty(B, cfg.hidden, dtype=torch.bfloat16, device="cuda"),
+        "idx": torch.full((B, cfg.top_k), -1, dtype=torch.int32, device="cuda"),
+        "gate": torch.zeros(B, cfg.top_k, dtype=torch.float32, device="cuda"),
+        "offsets": torch.full((cfg.n_experts + 1,), -1, dtype=torch.int32, device="cuda"),
+        "perm": torch.full((B * cfg.top_k,), -1, dtype=torch.int32, device="cuda"),
+    }
+
+
+@pytest.mark.parametrize("B", [2, 17, 24, 32])
+def test_full_size_batch(B):
+    log(f"[full-batch] {NAME} B={B}")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(NAME)
+    assert L.query_plan(B)["path_name"] == ("gemv" if B <= 2 else "splitk_mfma")
+    ref = oracle_step(NAME, B, ())
+    want = golden_out(NAME, B)
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
+    ws = L.new_workspace()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s)
+    s.synchronize()
+    eager = b["out"].clone()
+    rep = assert_close(as_f64_out(eager), want, "layer out")
+    assert_routing_equal({"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy()},
+                         ref, B, cfg.top_k, "layer routing")
+    log(f"[full-batch] B={B} layer: {rep}")
+    for _ in range(2):
+        b["out"].zero_()
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s, graph=True)
+        s.synchronize()
+        assert torch.equal(b["out"], eager), "graph replay differs from eager"
+    # the three ops on their own
+    with torch.cuda.stream(s):
+        L.oproj_residual(B, x, r, b["h32"], ws, stream=s)
+        L.router_topk(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], ws, stream=s)
+        L.moe_decode(B, b["h32"], b["idx"], b["gate"], b["offsets"], b["perm"], b["out"], ws,
+                     stream=s)
+    s.synchronize()
+    L.routing_status(ws, stream=s)
+    assert_close(b["h32"].cpu().numpy().astype(np.float64), ref["h"], "h32")
+    assert_routing_equal({"topk_idx": b["idx"].cpu().numpy(), "topk_gate": b["gate"].cpu().numpy(),
+                          "offsets": b["offsets"].cpu().numpy(), "perm": b["perm"].cpu().numpy()},
+                         ref, B, cfg.top_k, "router tables")
+    assert_close(as_f64_out(b["out"]), want, "moe out")
+
+
+def test_routing_of_a_token_does_not_depend_on_its_batch():
+    """Each of the 64 tokens alone (GEMV path), in batches of 8 and in the batch of 64 (split-K
+    path): the same experts as the oracle every time, gates within 1e-5 of it, outputs within
+    the tolerance of its output."""
+    log(f"[batch-invariance] {NAME} 1 / 8 / 64")
+    torch = _torch()
+    import synth.device as sd
+    cfg, _, L = gpu_layer(NAME)
+    k = cfg.top_k
+    ref = oracle_step(NAME, 64, ())
+    want = golden_out(NAME, 64)
+    x, r, _, _ = sd.device_tokens(cfg, 64)
+    ws = L.new_workspace()
+    got = {}
+    for B in (1, 8, 64):
+        idx = torch.full((64, k), -1, dtype=torch.int32, device="cuda")
+        gate = torch.zeros(64, k, dtype=torch.float32, device="cuda")
+        out = torch.empty(64, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+        for t0 in range(0, 64, B):
+            L.layer_decode(B, x[t0:t0 + B], r[t0:t0 + B], out[t0:t0 + B], ws, idx[t0:t0 + B],
+                           gate[t0:t0 + B])
+        torch.cuda.synchronize()
+        got[B] = (idx.cpu().numpy(), gate.cpu().numpy(), as_f64_out(out))
+        np.testing.assert_array_equal(got[B][0], ref["topk_idx"], err_msg=f"batch {B}: experts")
+        np.testing.assert_allclose(got[B][1], ref["topk_gate"], rtol=0, atol=1e-5,
+                                   err_msg=f"batch {B}: gates")
+        rep = assert_close(got[B][2], want, f"batch {B}: out")
+        log(f"[batch-invariance] B={B}: {rep}")
+    for B in (8, 64):
+        np.testing.assert_array_equal(got[B][0], got[1][0])
