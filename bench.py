@@ -124,6 +124,44 @@ def time_steps(layer, B, x, r, out, idx, gate, ws, s, flush, steps, warmup):
     return statistics.median(a.elapsed_time(b) * 1e3 for a, b in evs)
 
 
+def kernel_times(layer, B, x, r, out, idx, gate, ws, s, flush, steps) -> dict:
+    """Mean us per kernel record over `steps` flushed eager steps, from the library's HIP events
+    recorded around each launch on the stream it is launched on."""
+    import torch
+    layer.set_kernel_timing(True)
+    layer.read_kernel_timing()
+    with torch.cuda.stream(s):
+        for _ in range(steps):
+            flush.add_(1.0)
+            layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s)
+    s.synchronize()
+    recs = layer.read_kernel_timing()
+    layer.set_kernel_timing(False)
+    kernels = {}
+    for name, ms in recs:
+        kernels.setdefault(name, []).append(ms * 1e3)
+    return {k: statistics.mean(v) for k, v in kernels.items()}
+
+
+def roofline_for(path_name, by, kernels, workload, B):
+    """The dominant kernel's achieved HBM rate: its algorithmic bytes per launch over its
+    event-timed average duration.  GEMV path: the routed gate/up launch, which also runs the
+    top-k and streams the shared expert's down rows; split-K path: the gate/up record (routed
+    and shared rows, and on small intermediates the SwiGLU launch that sums its K chunks)."""
+    if path_name == "gemv":
+        name, nbytes = "topk_gateup_gemv_routed", by["routed_gateup"] + by["shared_down"]
+    else:
+        name, nbytes = "gateup_mfma", by["routed_gateup"] + by["shared_gateup"]
+    if name not in kernels:
+        return None
+    ach = nbytes / (kernels[name] * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": name, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(path_name, workload, B),
+            "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(kernels[name], 3)}
+
+
 def sweep(main_cfg, main_w, args, s, flush) -> dict:
     """The other workloads: batch 8 / 64 of the full-size layer, an 8-token speculative-verify
     batch (correlated tokens of one sequence) and the layer with an RMSNorm before the router
@@ -159,12 +197,19 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
         ws = layer.new_workspace()
         us = time_steps(layer, B, x, r, o, idx, gate, ws, s, flush, args.steps, max(2, args.warmup))
         n_act = int(torch.unique(idx).numel())
-        by = unique_bytes(cfg, n_act)["total"]
+        parts = unique_bytes(cfg, n_act)
+        by = parts["total"]
         gbs = by / (us * 1e-6) / 1e9
+        plan = layer.query_plan(B)
+        kern = {} if args.no_timing_pass else kernel_times(layer, B, x, r, o, idx, gate, ws, s,
+                                                            flush, max(5, args.steps // 2))
         out[f"{name}@{B}"] = {"us_per_step": round(us, 3), "tokens_per_s": round(B / (us * 1e-6), 1),
                               "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                               "n_act": n_act, "unique_bytes": by,
-                              "path": layer.query_plan(B)["path_name"]}
+                              "path": plan["path_name"],
+                              "kernels_per_step": plan["kernels_per_step"],
+                              "kernel_us_eager": {k: round(v, 3) for k, v in kern.items()},
+                              "roofline": roofline_for(plan["path_name"], parts, kern, name, B)}
         log(f"[bench] {name}@{B}: {out[f'{name}@{B}']}")
         layer.close()
     return out
@@ -230,7 +275,7 @@ def main():
     ap.add_argument("--config", default="full_b1")
     ap.add_argument("--batch", type=int, default=0, help="default: the workload's first batch")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=1)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--no-timing-pass", action="store_true")
     ap.add_argument("--mode", choices=["eager", "graph"], default="eager",
                     help="how each timed step is submitted (eager: one launch per kernel on one stream)")
@@ -329,36 +374,21 @@ def main():
     # ---- per-kernel durations (eager launches, library HIP events on each kernel's stream)
     kernels = {}
     if not args.no_timing_pass:
-        layer.set_kernel_timing(True)
-        layer.read_kernel_timing()
-        with torch.cuda.stream(s):
-            for _ in range(args.steps):
-                flush.add_(1.0)
-                layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, graph=False,
-                                   two_stream=args.two_stream)
-        s.synchronize()
-        recs = layer.read_kernel_timing()
-        layer.set_kernel_timing(False)
-        for name, ms in recs:
-            kernels.setdefault(name, []).append(ms * 1e3)
-        kernels = {k: statistics.mean(v) for k, v in kernels.items()}
-
-    # dominant kernel and the weight bytes one launch of it must read: on the GEMV path the
-    # routed gate/up launch also runs the top-k and streams the shared expert's down rows; on
-    # the split-K path the gate/up record covers the routed and the shared expert's rows
-    if plan["path_name"] == "gemv":
-        dom_name, dom_bytes = "topk_gateup_gemv_routed", by["routed_gateup"] + by["shared_down"]
-    else:
-        dom_name, dom_bytes = "gateup_mfma", by["routed_gateup"] + by["shared_gateup"]
-    roofline = None
-    if dom_name in kernels:
-        ach = dom_bytes / (kernels[dom_name] * 1e-6) / 1e9
-        roofline = {"bound": "hbm", "kernel": dom_name, "achieved": round(ach, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(plan["path_name"], cfg.name, B),
-                    "traffic_unit": "HBM bytes per launch (scaled FETCH_SIZE + WRITE_SIZE)",
-                    "bytes_per_launch": dom_bytes,
-                    "avg_launch_us": round(kernels[dom_name], 3)}
+        if args.two_stream:
+            layer.set_kernel_timing(True)
+            layer.read_kernel_timing()
+            with torch.cuda.stream(s):
+                for _ in range(args.steps):
+                    flush.add_(1.0)
+                    layer.layer_decode(B, x, r, out, ws, idx, gate, stream=s, two_stream=True)
+            s.synchronize()
+            for name, ms in layer.read_kernel_timing():
+                kernels.setdefault(name, []).append(ms * 1e3)
+            layer.set_kernel_timing(False)
+            kernels = {k: statistics.mean(v) for k, v in kernels.items()}
+        else:
+            kernels = kernel_times(layer, B, x, r, out, idx, gate, ws, s, flush, args.steps)
+    roofline = roofline_for(plan["path_name"], by, kernels, cfg.name, B)
 
     gbs = by["total"] / (med * 1e-6) / 1e9
     res = {
@@ -366,7 +396,7 @@ def main():
         "value": round(med, 3), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(med / 1e3, 6), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "accum_dtype": "f32",
-        "data": "synthetic (seeded Philox weights N(0,0.02)-like, tokens N(0,1)-like, random init)",
+        "data": "synthetic (seeded Philox + Box-Muller: weights N(0,0.02), tokens N(0,1); random init)",
         "config": {"workload": cfg.name, "description": cfg.description, "batch": B,
                    "hidden": cfg.hidden, "oproj_in": cfg.oproj_in, "n_experts": cfg.n_experts,
                    "top_k": cfg.top_k, "inter": cfg.inter, "shared_inter": cfg.shared_inter,
@@ -397,6 +427,10 @@ def main():
     if not args.no_cpu:
         log("[bench] timing the oracle on the host cores")
         res["cpu_baseline"] = cpu_baseline(cfg, B, args.cpu_reps)
+        if not args.no_sweep:
+            # the batch-8 metric point: one step (about 37 experts) per repetition
+            c8 = synth.CONFIGS["full_b8"]
+            res["cpu_baseline_sweep"] = {"full_b8@8": cpu_baseline(c8, 8, 1)}
     print(json.dumps(res), flush=True)
 
 
