@@ -175,6 +175,20 @@ kk_status kk_layer_decode(kk_ctx* ctx, int32_t B, const void* x, const void* res
                           int32_t* topk_idx, float* topk_gate, void* ws, kk_stream stream,
                           uint32_t flags);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): kk_layer_decode without a workspace argument.  The
+ * step's intermediates live in a static device array of the library (64 MiB per GPU, held from
+ * the library's first use on that GPU until the process ends; its address is looked up once per
+ * device by kk_create); the call itself allocates nothing.  A batch whose intermediates exceed
+ * the array returns KK_ERR_WORKSPACE (every supported shape fits up to 64 tokens).  flags: 0 or
+ * KK_TWO_STREAM (no KK_GRAPH).  Output bits equal kk_layer_decode's for the same inputs.  All
+ * calls on one GPU share its array and keep no state in it between calls (every region a step
+ * reads is written earlier in that step), so calls that overlap in time on one GPU, from any
+ * context or stream, race and give undefined output: serialise them. */
+kk_status kk_layer_decode_static(kk_ctx* ctx, int32_t B, const void* x, const void* resid,
+                                 void* out, int32_t* topk_idx, float* topk_gate,
+                                 kk_stream stream, uint32_t flags);
+
 /* Consecutive layers, each with its own context and weights: layer l reads x[l] [B][Ko] and the
  * residual stream r_l (resid for l = 0, out[l-1] after it) and writes out[l] [B][H]; every
  * layer's output is kept.  All L contexts must have the same kk_config, max_batch >= B and

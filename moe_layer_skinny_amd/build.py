@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkk.so")
 
-SOURCES = ["kk_gemv.hip", "kk_mfma.hip", "kk_api.cpp"]
+SOURCES = ["kk_gemv.hip", "kk_mfma.hip", "kk_scratch.hip", "kk_api.cpp"]
 ARCH = "gfx950"
 # Packed fp32 instructions are kept out of every kernel.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -188,6 +188,9 @@ struct kk_ctx {
   long long delay_ticks[2] = {0, 0};  // main stream / auxiliary stream delays (test hook)
   std::vector<TimingRec> trecs;
   std::vector<hipEvent_t> tpool;
+  void* scratch = nullptr;            // this device's static scratch (kk_layer_decode_static)
+  hipError_t scratch_err = hipSuccess;
+  bool no_alloc = false;              // inside kk_layer_decode_static: no timing events
 };
 
 namespace {
@@ -254,7 +257,7 @@ bool capturing(hipStream_t s) {
 // Runs one launch, bracketed by timing events when enabled (never inside a capture).
 template <typename F>
 hipError_t timed(kk_ctx* c, int name, hipStream_t s, F&& launch) {
-  if (!c->timing || capturing(s)) return launch();
+  if (!c->timing || c->no_alloc || capturing(s)) return launch();
   TimingRec r{name, pool_event(c), pool_event(c)};
   if (r.a) (void)hipEventRecord(r.a, s);
   hipError_t e = launch();
@@ -500,8 +503,8 @@ kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
 
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
                         float* gate, void* ws, hipStream_t s, bool two_stream, int path,
-                        const PrefetchNext* pf = nullptr) {
-  WsPtrs p = carve(c->L, ws);
+                        const PrefetchNext* pf = nullptr, const Layout* lay = nullptr) {
+  WsPtrs p = carve(lay ? *lay : c->L, ws);
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
   KK_HIP(kk::launch_delay(c->delay_ticks[0], s), "delay launch");
@@ -635,6 +638,10 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     if (e != hipSuccess) return bail(e, "fork event");
     e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "join event");
+    // the static scratch of kk_layer_decode_static: its address on this device, looked up once
+    // per device (a failure only disables that entry point)
+    c->scratch_err = kk::scratch_init(c->device);
+    if (c->scratch_err == hipSuccess) c->scratch = kk::scratch_ptr(c->device);
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return bail(e, "create sync");
     *out = c;
@@ -843,6 +850,48 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     return KK_OK;
   } catch (...) {
     return fail(KK_ERR_INVALID_ARG, "internal error in kk_layer_decode");
+  }
+}
+
+kk_status kk_layer_decode_static(kk_ctx* c, int32_t B, const void* x, const void* resid, void* out,
+                                 int32_t* topk_idx, float* topk_gate, kk_stream stream,
+                                 uint32_t flags) {
+  try {
+    if (!c) return fail(KK_ERR_INVALID_ARG, "context is NULL");
+    if (flags & ~KK_TWO_STREAM)
+      return fail(KK_ERR_INVALID_ARG, "kk_layer_decode_static takes only KK_TWO_STREAM (flags 0x%x)",
+                  flags);
+    if (B < 1 || B > c->max_batch)
+      return fail(KK_ERR_INVALID_ARG, "batch %d outside 1..%d (max_batch of this context)", B,
+                  c->max_batch);
+    if (!c->scratch)
+      return hip_fail(c->scratch_err != hipSuccess ? c->scratch_err : hipErrorInvalidValue,
+                      "static scratch unavailable on this device");
+    // the regions this batch needs, in the same order as a workspace of max_batch B
+    const Layout Ls = make_layout(c->cfg, B);
+    if (Ls.total > kk::kScratchBytes)
+      return fail(KK_ERR_WORKSPACE, "batch %d of this shape needs %zu bytes of scratch; the static "
+                  "scratch holds %zu", B, Ls.total, kk::kScratchBytes);
+    kk_status st = check_common(c, B, c->scratch);
+    if (st != KK_OK) return st;
+    KK_PTR(x, "x");
+    KK_PTR(resid, "resid");
+    KK_PTR(out, "out");
+    if (topk_idx && misaligned(topk_idx)) return fail(KK_ERR_INVALID_ARG, "topk_idx misaligned");
+    if (topk_gate && misaligned(topk_gate)) return fail(KK_ERR_INVALID_ARG, "topk_gate misaligned");
+    const bool two = (flags & KK_TWO_STREAM) != 0;
+    kk_plan plan;
+    if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
+    if (two && plan.path != KK_PATH_GEMV)
+      return fail(KK_ERR_UNSUPPORTED, "KK_TWO_STREAM applies to the GEMV path (batch 1-2)");
+    c->no_alloc = true;
+    st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, c->scratch, (hipStream_t)stream,
+                       two, plan.path, nullptr, &Ls);
+    c->no_alloc = false;
+    return st;
+  } catch (...) {
+    c->no_alloc = false;
+    return fail(KK_ERR_INVALID_ARG, "internal error in kk_layer_decode_static");
   }
 }
 

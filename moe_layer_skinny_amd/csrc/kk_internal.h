@@ -130,6 +130,14 @@ hipError_t launch_prefetch(const Device& d, const void* p, size_t bytes, hipStre
 // rt.status.
 hipError_t launch_moe_prep(const Shape& s, int B, const Routing& rt, hipStream_t st);
 
+// ---- static scratch (kk_scratch.hip) ----------------------------------------------------
+// Size of the per-device static scratch array of the entry point that allocates nothing.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+// Looks up the array's device address on `device` (which must be current) once, and keeps it.
+hipError_t scratch_init(int device);
+// The address scratch_init found for `device`, or nullptr.
+void* scratch_ptr(int device);
+
 // ---- split-K MFMA path (batch 3..64) ---------------------------------------------------
 bool mfma_supported(const Shape& s, int B);
 int mfma_oproj_splits(const Shape& s);

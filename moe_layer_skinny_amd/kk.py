@@ -71,6 +71,7 @@ def lib():
             "kk_moe_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
             "kk_routing_status": (i32, [vp, vp, vp]),
             "kk_layer_decode": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, u32]),
+            "kk_layer_decode_static": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, u32]),
             "kk_chain_decode": (i32, [ctypes.POINTER(vp), i32, i32, ctypes.POINTER(vp), vp,
                                       ctypes.POINTER(vp), vp, vp, u32]),
             "kk_set_stream_delay": (i32, [vp, i32, ctypes.c_float]),
@@ -196,6 +197,13 @@ class Layer:
         flags = (KK_GRAPH if graph else 0) | (KK_TWO_STREAM if two_stream else 0)
         _check(lib().kk_layer_decode(self._h, B, _ptr(x), _ptr(resid), _ptr(out), _ptr(topk_idx),
                                      _ptr(topk_gate), _ptr(ws), _stream(stream), flags))
+
+    def layer_decode_static(self, B, x, resid, out, topk_idx=None, topk_gate=None, stream=None,
+                            two_stream=False):
+        """kk_layer_decode_static: the step with the library's static scratch (no workspace)."""
+        flags = KK_TWO_STREAM if two_stream else 0
+        _check(lib().kk_layer_decode_static(self._h, B, _ptr(x), _ptr(resid), _ptr(out),
+                                            _ptr(topk_idx), _ptr(topk_gate), _stream(stream), flags))
 
     def set_stream_delay(self, which: int, microseconds: float):
         """Test hook: a bounded wait first on the main (0) or auxiliary (1) stream of each step."""
