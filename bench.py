@@ -146,9 +146,13 @@ def kernel_times(layer, B, x, r, out, idx, gate, ws, s, flush, steps) -> dict:
 def roofline_for(path_name, by, kernels, workload, B):
     """The dominant kernel's achieved HBM rate: its algorithmic bytes per launch over its
     event-timed average duration.  GEMV path: the routed gate/up launch, which also runs the
-    top-k and streams the shared expert's down rows; split-K path: the gate/up record (routed
+    top-k and streams the shared expert's gate/up rows (layers with a norm: its down rows);
+    split-K path: the gate/up record (routed
     and shared rows, and on small intermediates the SwiGLU launch that sums its K chunks)."""
-    if path_name == "gemv":
+    if path_name == "gemv" and "topk_shared_gateup_gemv" in kernels:
+        # the routed gate/up launch whose prologue streams the shared expert's gate/up rows
+        name, nbytes = "topk_shared_gateup_gemv", by["routed_gateup"] + by["shared_gateup"]
+    elif path_name == "gemv":
         name, nbytes = "topk_gateup_gemv_routed", by["routed_gateup"] + by["shared_down"]
     else:
         name, nbytes = "gateup_mfma", by["routed_gateup"] + by["shared_gateup"]

@@ -41,7 +41,7 @@ constexpr int kMaxBatch = 64;
 constexpr int kMaxTopK = 16;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxOprojSplits = 8;   // o-proj K chunks (7 on the split-K path)
-constexpr int kMaxRouterSplits = 8;  // router logit K chunks (7, or 1 for the fp32 layer)
+constexpr int kMaxRouterSplits = 10;  // router logit partial slots (up to 10)
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -135,11 +135,13 @@ const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_log
                               "down_combine_gemv", "moe_prep",    "combine",    "oproj_mfma",
                               "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
                               "topk_rows",   "tables", "topk_tables", "oproj_reduce_norm",
-                              "norm_rows", "prefetch"};
+                              "norm_rows", "prefetch", "oproj_router_gemv",
+                              "topk_shared_gateup_gemv", "oproj_router_mfma"};
 enum KName {
   K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
   K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
-  K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS, K_PREFETCH
+  K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS, K_PREFETCH, K_OPROJ_ROUTER,
+  K_TOPK_SHARED_GU, K_OPROJ_ROUTER_MFMA
 };
 
 struct TimingRec {
@@ -174,6 +176,7 @@ struct kk_ctx {
   kk::Shape shape;
   kk::Weights w;
   kk::Norm norm;  // gamma == nullptr: no norm
+  void* mr = nullptr;  // router-o-proj product W_r W_o (GEMV path without a norm), owned
   int max_batch;
   int device;
   kk::Device dev;
@@ -203,6 +206,10 @@ int forced_path() {
   return -2;
 }
 
+// Whether batch B on the split-K path runs the o-proj and the router as one launch (a layer with
+// the router-o-proj product, up to 16 tokens).
+bool mfma_fused(const kk_ctx* c, int B) { return c->mr != nullptr && B <= 16; }
+
 kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   std::memset(p, 0, sizeof *p);
   const int f = forced_path();
@@ -213,15 +220,22 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   if (p->path == KK_PATH_GEMV) {
     if (!kk::gemv_supported(c->shape, B))
       return fail(KK_ERR_UNSUPPORTED, "GEMV path has no kernels for batch %d of this shape", B);
-    const size_t lds_down = kk::down_combine_gemv_lds(c->shape, c->dev, B);
+    const size_t lds_down = kk::down_combine_gemv_lds(c->shape, c->dev, B, true);
     if ((long)lds_down > c->dev.max_lds)
       return fail(KK_ERR_UNSUPPORTED, "GEMV down-projection needs %zu B of LDS (device: %d)",
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
-    p->router_splitk = kk::router_gemv_splits(c->shape);
-    // oproj, router logits + shared gate/up, top-k + shared down + routed gate/up,
-    // routed down + combine
-    p->kernels_per_step = 4;
+    if (c->mr) {
+      // o-proj + router logits (from x and r), top-k + shared gate/up + routed gate/up,
+      // routed + shared down + combine
+      p->router_splitk = kk::router_fused_splits(c->shape);
+      p->kernels_per_step = 3;
+    } else {
+      // oproj, router logits + shared gate/up, top-k + shared down + routed gate/up,
+      // routed down + combine
+      p->router_splitk = kk::router_gemv_splits(c->shape);
+      p->kernels_per_step = 4;
+    }
     return KK_OK;
   }
   if (!kk::mfma_supported(c->shape, B))
@@ -234,6 +248,12 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   // tokens an unsplit gate/up adds the shared expert's split-K launch and its SwiGLU
   const bool split = kk::mfma_gateup_split(c->shape, B);
   p->kernels_per_step = (B > 16 ? 8 : 7) + (split ? 1 : 0) + (B > 32 && !split ? 2 : 0);
+  if (mfma_fused(c, B)) {
+    // o-proj (with the residual) + router logits from x and r in one launch: no reduce and
+    // no router launch
+    p->router_splitk = kk::mfma_fused_splits(c->shape);
+    p->kernels_per_step -= 2;
+  }
   return KK_OK;
 }
 
@@ -467,7 +487,7 @@ kk_status enqueue_routed_and_combine(kk_ctx* c, int B, const float* h32, const k
   KK_HIP(timed(c, K_DOWN, s,
                [&] {
                  return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.ys, c->w.w2, h32,
-                                                     rt, out, s);
+                                                     rt, out, nullptr, nullptr, s);
                }),
          "down + combine launch");
   return KK_OK;
@@ -501,6 +521,54 @@ kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
   return KK_OK;
 }
 
+// GEMV path of a layer without a norm (the router-o-proj product mr exists): three launches.
+// o-proj + router logits from x and r; the top-k in every block of the routed gate/up launch,
+// covered by the shared expert's gate/up (or, two_stream, that gate/up on the auxiliary stream,
+// joined before the last launch); routed and shared down-projection with the combine.
+kk_status enqueue_layer_gemv3(kk_ctx* c, int B, const void* x, const void* r, void* out,
+                              const kk::Routing& rt, const WsPtrs& p, hipStream_t s,
+                              bool two_stream, const PrefetchNext* pf) {
+  KK_HIP(timed(c, K_OPROJ_ROUTER, s,
+               [&] {
+                 return kk::launch_oproj_router_gemv(c->shape, c->dev, B, x, r, c->w.w_o, c->w.w_r,
+                                                     c->mr, p.h32, nullptr, p.logit_part, s);
+               }),
+         "o-proj + router launch");
+  if (pf) {
+    kk_status st = enqueue_prefetch(*pf, s);
+    if (st != KK_OK) return st;
+  }
+  kk::GateupExtras gx;
+  gx.part = p.logit_part;
+  gx.splits = kk::router_fused_splits(c->shape);
+  gx.bias = c->w.bias;
+  if (two_stream) {
+    KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
+    KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
+    KK_HIP(kk::launch_delay(c->delay_ticks[1], c->aux), "delay launch");
+    kk_status st = enqueue_shared_gateup(c, B, p.h32, rt, p.As, c->aux);
+    if (st != KK_OK) return st;
+    KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
+  } else {
+    gx.ws13 = c->w.ws13;
+    gx.As_out = p.As;
+  }
+  KK_HIP(timed(c, two_stream ? K_TOPK_GU : K_TOPK_SHARED_GU, s,
+               [&] {
+                 return kk::launch_gateup_gemv(c->shape, c->dev, B, p.h32, c->w.w13, false, rt, p.A,
+                                               gx, s);
+               }),
+         "routed gate/up launch");
+  if (two_stream) KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
+  KK_HIP(timed(c, K_DOWN, s,
+               [&] {
+                 return kk::launch_down_combine_gemv(c->shape, c->dev, B, p.A, p.ys, c->w.w2, p.h32,
+                                                     rt, out, c->w.ws2, p.As, s);
+               }),
+         "down + combine launch");
+  return KK_OK;
+}
+
 kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* out, int32_t* idx,
                         float* gate, void* ws, hipStream_t s, bool two_stream, int path,
                         const PrefetchNext* pf = nullptr, const Layout* lay = nullptr) {
@@ -508,6 +576,22 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
   KK_HIP(kk::launch_delay(c->delay_ticks[0], s), "delay launch");
+  if (path == KK_PATH_GEMV && c->mr) return enqueue_layer_gemv3(c, B, x, r, out, rt, p, s, two_stream, pf);
+  if (path == KK_PATH_SPLITK_MFMA && mfma_fused(c, B)) {
+    KK_HIP(timed(c, K_OPROJ_ROUTER_MFMA, s,
+                 [&] {
+                   return kk::launch_oproj_router_mfma(c->shape, c->dev, B, x, r, c->w.w_o, c->w.w_r,
+                                                       c->mr, p.h32, p.oproj_part, p.logit_part, s);
+                 }),
+           "o-proj + router launch");
+    if (pf) {
+      kk_status st = enqueue_prefetch(*pf, s);
+      if (st != KK_OK) return st;
+    }
+    kk_status st = enqueue_topk(c, B, p.logit_part, kk::mfma_fused_splits(c->shape), rt, s);
+    if (st != KK_OK) return st;
+    return enqueue_experts_mfma(c, B, p.h32, p.h32, rt, p, out, s);
+  }
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
   if (pf && (st = enqueue_prefetch(*pf, s)) != KK_OK) return st;
@@ -638,6 +722,16 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     if (e != hipSuccess) return bail(e, "fork event");
     e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "join event");
+    // the router-o-proj product for the GEMV path's fused o-proj + router launch: a layer
+    // without a norm (the router reads h itself) whose o-proj input is a slice (Ko < H), so
+    // that the product (E x Ko per plane) is small beside the router matrix (E x H); for a
+    // full-width input it costs more bandwidth than the launch it saves
+    if (kk::router_fused_applies(c->shape) && !c->norm.gamma) {
+      e = hipMalloc(&c->mr, kk::router_oproj_product_bytes(c->shape));
+      if (e != hipSuccess) return bail(e, "router-o-proj product allocation");
+      e = kk::launch_router_oproj_product(c->shape, c->w.w_r, c->w.w_o, c->mr, nullptr);
+      if (e != hipSuccess) return bail(e, "router-o-proj product launch");
+    }
     // the static scratch of kk_layer_decode_static: its address on this device, looked up once
     // per device (a failure only disables that entry point)
     c->scratch_err = kk::scratch_init(c->device);
@@ -655,6 +749,7 @@ kk_status kk_destroy(kk_ctx* c) {
   if (!c) return KK_OK;
   if (c->aux) (void)hipStreamSynchronize(c->aux);
   destroy_graphs(c);
+  if (c->mr) (void)hipFree(c->mr);
   for (auto& r : c->trecs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);

@@ -94,6 +94,177 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WP
   }
 }
 
+// Rows of T (16-byte chunks) -> fp32 in LDS, n elements (n a multiple of a chunk's elements).
+template <typename T>
+__device__ __forceinline__ void stage_to_f32(const T* __restrict__ src, int n, float* dst) {
+  constexpr int EPC = Elem<T>::EPC;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  for (int c = threadIdx.x; c < n / EPC; c += blockDim.x) {
+    float f[EPC];
+    Elem<T>::unpack(s[c], f);
+    float4* d = reinterpret_cast<float4*>(dst + (size_t)c * EPC);
+#pragma unroll
+    for (int h = 0; h < EPC / 4; ++h) d[h] = make_float4(f[4 * h], f[4 * h + 1], f[4 * h + 2], f[4 * h + 3]);
+  }
+}
+
+// ------------------------------------------------------------------------------ o-proj + router
+// The o-proj and the router logits in one launch, the router not waiting for h: the logit
+// W_r[e] . h_t = W_r[e] . r_t + (W_r W_o)[e] . x_t, with mr = W_r W_o computed once per layer
+// (router_oproj_product_kernel) and kept as npl planes of T whose sum is its fp32 value,
+// laid out [npl][E][Ko].  The unit space has H + npl E rows of Ko elements:
+//  * rows 0..H-1 are W_o's: h32[t][n] = r[t][n] + W_o[n] . x_t (and h_out = RNE(h32));
+//  * row H + p E + e is plane p of mr[e]: part[RS + p][t][e] = mr_p[e] . x_t.
+// Besides its rows, the wave with global id g < E RS (ids across the blocks first) takes slice
+// sl = g % RS of router row e = g / RS against r, staged in LDS as fp32:
+// part[sl][t][e] = W_r[e][slice sl] . r_t.  The top-k sums the RS + npl partials of (t, e) in
+// slot order.  x sits in registers as in oproj_gemv_kernel when it fits, else in LDS.
+template <typename T, int CPR, int CPS, int NT, int R, int WPE = 2>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void oproj_router_gemv_kernel(
+    const T* __restrict__ x, const T* __restrict__ r, const T* __restrict__ w_o,
+    const T* __restrict__ w_r, const T* __restrict__ mr, int npl, float* __restrict__ h32,
+    T* __restrict__ h_out, float* __restrict__ part, int H, int E, int RS) {
+  using G = Geo<T, CPR>;
+  using GS = Geo<T, CPS>;
+  static_assert(GS::SEG == 64, "router slices span the wave");
+  constexpr bool kRegs = NT * G::CPL <= 14;
+  extern __shared__ float lds[];  // r as fp32 [NT][H], then x as fp32 [NT][Ko] if not in registers
+  float* lr = lds;
+  float* lx = lds + (size_t)NT * H;
+  const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane % G::SEG, seg = lane / G::SEG;
+  const int rows = H + npl * E;
+  const int rows_per_unit = G::RPW * R;
+  const int units = (rows + rows_per_unit - 1) / rows_per_unit;
+  const int stride = gridDim.x * wpb;
+  int unit = blockIdx.x * wpb + wave;
+
+  // this wave's router slice, requested first
+  const int gs = wave * gridDim.x + blockIdx.x;
+  const bool has_slice = gs < E * RS;
+  const int se = has_slice ? gs / RS : 0, ssl = has_slice ? gs - se * RS : 0;
+  u32x4 wr[GS::CPL];
+  if (has_slice) load_row<T, CPS>(w_r + (size_t)se * H + (size_t)ssl * GS::K, lane, wr);
+
+  u32x4 w[R][G::CPL];
+  auto issue = [&](int u) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int n = u * rows_per_unit + seg + G::RPW * q;
+      if (n < rows)
+        load_row<T, CPR>(n < H ? w_o + (size_t)n * G::K : mr + (size_t)(n - H) * G::K, sub, w[q]);
+      else
+#pragma unroll
+        for (int i = 0; i < G::CPL; ++i) w[q][i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  if (unit < units) issue(unit);
+  u32x4 xa[kRegs ? NT : 1][G::CPL];
+  if constexpr (kRegs) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) load_act_chunks<T, CPR>(x + (size_t)t * G::K, sub, xa[t]);
+  }
+  stage_to_f32<T>(r, NT * H, lr);
+  if constexpr (!kRegs) stage_to_f32<T>(x, NT * G::K, lx);
+  __syncthreads();
+  if (has_slice) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v = seg_sum_dpp<64>(dot_lane<T, CPS>(wr, lr + (size_t)t * H + (size_t)ssl * GS::K, lane));
+      if (lane == 63) part[((size_t)ssl * NT + t) * E + se] = v;
+    }
+  }
+  if (unit >= units) return;
+
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int n = unit * rows_per_unit + seg + G::RPW * q;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float d;
+        if constexpr (kRegs)
+          d = dot_rr<T, CPR>(w[q], xa[t], sub);
+        else
+          d = dot_lane<T, CPR>(w[q], lx + t * G::K, sub);
+        const float acc = seg_sum<G::SEG>(d);
+        if (sub == 0 && n < rows) {
+          if (n < H) {
+            const size_t o = (size_t)t * H + n;
+            const float hv = Elem<T>::load(r, o) + acc;
+            h32[o] = hv;
+            if (h_out) Elem<T>::store(h_out, o, hv);
+          } else {
+            const int pl = (n - H) / E, e = (n - H) - pl * E;
+            part[((size_t)(RS + pl) * NT + t) * E + e] = acc;
+          }
+        }
+      }
+    }
+    unit += stride;
+    if (unit >= units) break;
+    __builtin_amdgcn_sched_barrier(0);
+    issue(unit);
+  }
+}
+
+// The router-o-proj product of a layer, once: M[e][j] = sum_n W_r[e][n] W_o[n][j], accumulated
+// in fp64, rounded to fp32 and stored as npl planes of T ([npl][E][Ko]): bf16 hi = RNE(m),
+// lo = RNE(m - hi) (their sum reproduces m to 2^-17 relative); fp32 one plane, m itself.
+// (A logit's error from the two planes: about 2^-17 of |M| |x| per term, ~1e-6 over 448
+// terms, far below the 1e-3 gap the selection keeps.)
+// Block tile 32 experts x 64 columns, 32-wide steps along n staged in LDS; each thread owns
+// 2 x 4 outputs.
+template <typename T>
+__global__ __launch_bounds__(256) void router_oproj_product_kernel(const T* __restrict__ w_r,
+                                                                   const T* __restrict__ w_o, int E,
+                                                                   int H, int Ko, T* __restrict__ mr,
+                                                                   int npl) {
+  __shared__ double sr[32][33];  // W_r tile [e][n]
+  __shared__ double so[32][65];  // W_o tile [n][j]
+  const int e0 = blockIdx.y * 32, j0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // columns j0 + 4 tx .., experts e0 + 2 ty ..
+  double acc[2][4] = {};
+  for (int n0 = 0; n0 < H; n0 += 32) {
+    for (int i = threadIdx.x; i < 32 * 32; i += 256) {
+      const int ee = i >> 5, nn = i & 31;
+      sr[ee][nn] = e0 + ee < E && n0 + nn < H ? (double)Elem<T>::load(w_r, (size_t)(e0 + ee) * H + n0 + nn) : 0.0;
+    }
+    for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+      const int nn = i >> 6, jj = i & 63;
+      so[nn][jj] = n0 + nn < H && j0 + jj < Ko ? (double)Elem<T>::load(w_o, (size_t)(n0 + nn) * Ko + j0 + jj) : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int nn = 0; nn < 32; ++nn) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(sr[2 * ty + a][nn], so[nn][4 * tx + b], acc[a][b]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int e = e0 + 2 * ty + a, j = j0 + 4 * tx + b;
+      if (e < E && j < Ko) {
+        const float m = (float)acc[a][b];
+        T* dst = mr + (size_t)e * Ko + j;
+        if (npl == 1) {
+          Elem<T>::store(dst, 0, m);
+        } else {
+          const uint16_t hi = f32_to_bf16(m);
+          const float lo = m - __uint_as_float((uint32_t)hi << 16);
+          Elem<T>::store(dst, 0, __uint_as_float((uint32_t)hi << 16));
+          Elem<T>::store(dst, (size_t)E * Ko, lo);
+        }
+      }
+    }
+}
+
 // ------------------------------------------------------------------------------ gate / up helpers
 // One gate/up row pair of one expert for the positions [p0, p1) of that expert:
 // A[p][i] = silu(W1[i] . u_t) * (W3[i] . u_t), u_t an fp32 row in LDS.
@@ -415,19 +586,20 @@ struct LdsTables {
 // no load is branched around).  Tables come from the wave's own lanes: lane j holds act[j],
 // the first position of that expert and its position count, lane p the token of position p.
 //
-// Before the routed rows, the launch can do two things that only need the previous launch:
-//  * TOPK: every block runs the top-k from the logit partials (wave 0) and builds the
+// Before the routed rows, the launch can do work that only needs the previous launch:
+//  * TOPK: every block runs the top-k from the logit partials (wave t: token t) and builds the
 //    routing tables in its own LDS -- the same bits in every block; block 0 also writes
 //    them out (topk_idx / topk_gate / offsets / perm / inv_perm / act / n_act);
-//  * ws2 != nullptr: waves 1.. compute the shared expert's down-projection into ys, so its
-//    weight stream covers the top-k's latency.
-template <typename T, int CPR, int CPRS, int NT, bool TOPK>
+//  * ws13 != nullptr: the other waves compute the shared expert's gate/up into As_out, so its
+//    weight stream covers the top-k's latency; or
+//  * ws2 != nullptr: waves 1.. compute the shared expert's down-projection into ys from As.
+template <typename T, int CPR, int CPRS, int NT, bool TOPK, bool SGU>
 __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     const float* __restrict__ u, const T* __restrict__ w13, int I, int k, int B, int shared,
     Routing rt, float* __restrict__ A, const float* __restrict__ part, int splits,
     const float* __restrict__ bias, int E, float routed_scale, const T* __restrict__ ws2,
     const float* __restrict__ As, float* __restrict__ ys, int H, const T* __restrict__ gamma,
-    float eps) {
+    float eps, const T* __restrict__ ws13, int Is, float* __restrict__ As_out) {
   using G = Geo<T, CPR>;
   static_assert(G::SEG == 64 && G::EXACT, "gate/up rows must span the wave exactly");
   constexpr int HA = (G::CPL + 1) / 2, HB = G::CPL - HA;
@@ -436,31 +608,63 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   __shared__ TopkScratch sm;
   __shared__ LdsTables tb;
   __shared__ float lg[TOPK ? 2 * kMaxExperts : 1];
+  __shared__ float lb[SGU ? kMaxExperts : 1];  // the bias, when the selection runs after the staging
   const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nslot = B * k;
   // the logits first, by the whole block, before any weight stream competes with their loads;
   // the waves that run a token's selection (wave t: token t) request their bias values with
-  // them
+  // them.  With the shared gate/up (SGU), the waves past the selecting ones request their
+  // first shared row pair before that (one token; with two, the pair waits for the staging, as
+  // the registers would not hold it beside the staged rows).
+  const int sw = (wave - B) * gridDim.x + blockIdx.x, nsw = gridDim.x * (wpb - B);
+  u32x4 sg[SGU ? G::CPL : 1], su[SGU ? G::CPL : 1];
+  if constexpr (SGU && NT == 1)
+    if (wave >= B && sw < Is) load_pair<T, CPR>(ws13, 0, sw, Is, sg, su, lane);
   float bv[kMaxM];
-  if (TOPK && wave < B) load_bias(bias, E, bv);
+  if (TOPK && !SGU && wave < B) load_bias(bias, E, bv);
+  if constexpr (SGU)
+    for (int i = threadIdx.x; i < E; i += blockDim.x) lb[i] = bias[i];
   if (TOPK) {
     logits_to_lds<false>(part, splits, B, E, lg);
     __syncthreads();
   }
   Stage<stage_q(NT, G::K)> st;
   st.load(u, B * G::K);
-  if (TOPK && wave < B) {
-    Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
-    topk_row_lds(lg, bv, E, k, routed_scale, wave, rl, sm.sel);
+  if constexpr (SGU) {
+    // the shared expert's gate/up rows read u, so it goes to LDS first; then the selecting
+    // waves run the top-k while the others stream the shared rows into As_out
+    if (gamma)
+      st.template store_rmsnorm<T, NT>(lds, gamma, eps, G::K, nred);
+    else
+      st.store(lds);
+    __syncthreads();
+    if (TOPK && wave < B) {
+      Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
+#pragma unroll
+      for (int m = 0; m < kMaxM; ++m) bv[m] = lb[min(lane + 64 * m, E - 1)];
+      topk_row_lds(lg, bv, E, k, routed_scale, wave, rl, sm.sel);
+    }
+    if (wave >= B) {
+      if constexpr (NT > 1)
+        if (sw < Is) load_pair<T, CPR>(ws13, 0, sw, Is, sg, su, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      shared_rows<T, CPR, NT>(ws13, Is, 0, Is, sw, nsw, sg, su, lds, k, B, rt, As_out, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    if (TOPK && wave < B) {
+      Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
+      topk_row_lds(lg, bv, E, k, routed_scale, wave, rl, sm.sel);
+    }
+    if (ws2 && wave > 0)
+      shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, (wave - 1) * gridDim.x + blockIdx.x,
+                                       gridDim.x * (wpb - 1), lane);
+    if (gamma)
+      st.template store_rmsnorm<T, NT>(lds, gamma, eps, G::K, nred);
+    else
+      st.store(lds);
   }
-  if (ws2 && wave > 0)
-    shared_down_rows<T, CPRS, NT, 4>(ws2, As, ys, H, B, (wave - 1) * gridDim.x + blockIdx.x,
-                                     gridDim.x * (wpb - 1), lane);
-  if (gamma)
-    st.template store_rmsnorm<T, NT>(lds, gamma, eps, G::K, nred);
-  else
-    st.store(lds);
   __syncthreads();
   if (TOPK) {
     Routing rl{tb.idx, tb.gate, tb.offsets, tb.perm, tb.inv, tb.act, &tb.n_act};
@@ -630,53 +834,61 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Row ownership: block b owns RG row groups (RPW consecutive rows each) of the output, groups
 // b, b + nb, b + 2 nb, ... (interleaved, so the blocks that work in step read neighbouring
 // rows and every HBM channel stays busy).  Its work items are (a, row group) for every active
-// expert a; an item's dot products W2_a[n] . A[p] for each position p of expert a land in
-// LDS, and once all items are done the block writes out[t][n] = RNE(h32[t][n] + sum_j
-// g[t][j] * part[pos(t,j)][n] + ys[t][n]) (j in ascending expert order, then the shared
-// expert's output ys), so the routed expert outputs never leave the chip.
+// expert a and, with ws2, the shared expert as one more group after them (its positions are
+// the B tokens, its activations the rows of As).  An item's dot products W2_a[n] . A[p] for
+// each position p of expert a land in LDS, and once all items are done the block writes
+// out[t][n] = RNE(h32[t][n] + sum_j g[t][j] * part[pos(t,j)][n] + y_s[t][n]) (j in ascending
+// expert order, then the shared expert's output y_s: its group's dots, or ys when the shared
+// expert's down-projection ran elsewhere), so no expert output leaves the chip.
 // Items are split into contiguous runs over the waves.  A wave alternates two register
 // buffers of U items (the loads of one in flight while the other is consumed), keeps the
-// activation values of the expert it is on in registers, and reads the active-expert tables
-// from its own lanes (lane i: expert act[i], its first position and its position count).
+// activation values of the group it is on in registers, and reads the group tables from its
+// own lanes (lane i: expert act[i], its first position and its position count; lane n_act:
+// the shared expert).
 template <typename T, int CPR, int NT, int U, int WPB, int MINB>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB * WPB / 4))) void down_combine_kernel(
     const float* __restrict__ A, const float* __restrict__ ys, const T* __restrict__ w2,
     const float* __restrict__ h32, int H, int k, int B, int RG, Routing rt,
-    T* __restrict__ out) {
+    T* __restrict__ out, const T* __restrict__ ws2, const float* __restrict__ As) {
   using G = Geo<T, CPR>;
   extern __shared__ float lds[];
-  const int nslot = B * k, RB = RG * G::RPW;
-  float* sA = lds;                               // [nslot][K]: A rows
-  float* part = sA + (size_t)nslot * G::K;       // [nslot][RB]
-  float* sG = part + (size_t)nslot * RB;         // [nslot] gates
+  const bool sh = ws2 != nullptr;
+  const int nslot = B * k, npos = nslot + (sh ? B : 0), RB = RG * G::RPW;
+  float* sA = lds;                               // [npos][K]: A rows, then As rows
+  float* part = sA + (size_t)npos * G::K;        // [npos][RB]
+  float* sG = part + (size_t)npos * RB;          // [nslot] gates
   int* sQ = (int*)(sG + nslot);                  // [nslot] slot -> position
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % G::SEG, seg = lane / G::SEG;
   const int t_a = rt.act[lane];                  // act has E >= 64 entries (read before n_act)
-  const int n_act = min(*rt.n_act, 64);          // at most B * k <= 32 on this path
+  const int n_act = min(*rt.n_act, 63);          // at most B * k <= 32 on this path
+  const int ng = n_act + (sh ? 1 : 0);           // groups, the shared expert last
   const int nb = gridDim.x;
   auto row_of = [&](int rg, int sg) { return ((int)blockIdx.x + nb * rg) * G::RPW + sg; };
-  const int items = n_act * RG;
+  const int items = ng * RG;
   const int i0 = wave * items / WPB, i1 = (wave + 1) * items / WPB;
 
   // activation rows (up to 8 slots per token in registers; more are copied by a loop)
   Stage<stage_q(8 * NT, G::K)> sta;
   sta.load(A, nslot * G::K);
-  // the residual and shared-expert values of this thread's combine item, requested now (every
-  // block has at most one item per thread at these shapes; otherwise the tail loads them)
+  Stage<stage_q(NT, G::K)> stb;
+  if (sh) stb.load(As, B * G::K);
+  // the residual (and shared-expert) values of this thread's combine item, requested now
+  // (every block has at most one item per thread at these shapes; otherwise the tail loads
+  // them)
   const bool pre = B * RB <= (int)blockDim.x;
-  float pre_h, pre_y;
+  float pre_h, pre_y = 0.f;
   {
     const int i = min((int)threadIdx.x, B * RB - 1);
     const int t = i / RB, nl = i - t * RB;
     const size_t o = (size_t)t * H + min(row_of(nl / G::RPW, nl % G::RPW), H - 1);
     pre_h = h32[o];
-    pre_y = ys[o];
+    if (!sh) pre_y = ys[o];
   }
   const int t_e = lane < n_act ? t_a : 0;  // entries past n_act are not expert ids
-  const int t_lo = rt.offsets[t_e];
-  const int t_cnt = rt.offsets[t_e + 1] - t_lo;
+  const int t_lo = lane < n_act ? rt.offsets[t_e] : (lane == n_act ? nslot : 0);
+  const int t_cnt = lane < n_act ? rt.offsets[t_e + 1] - t_lo : (lane == n_act ? B : 0);
 
   // Two register buffers of U items.  Loads are never branched around: an item past the
   // run's end reads the first row of A instead (L2-resident), so the waits stay exact.
@@ -693,12 +905,13 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
     for (int q = 0; q < U; ++q) {
       const int e = __builtin_amdgcn_readlane(t_e, min(ci.a, 63));
       const int n = min(row_of(ci.rg, seg), H - 1);
-      load_row<T, CPR>(ci.it < i1 ? w2 + ((size_t)e * H + n) * G::K : dummy, sub, w[q]);
+      const T* row = (sh && ci.a == n_act) ? ws2 + (size_t)n * G::K : w2 + ((size_t)e * H + n) * G::K;
+      load_row<T, CPR>(ci.it < i1 ? row : dummy, sub, w[q]);
       advance(ci);
     }
   };
-  // The lane's activation values for the positions of the expert being consumed, held in
-  // registers while the run stays on that expert (reloaded from LDS when it moves on).
+  // The lane's activation values for the positions of the group being consumed, held in
+  // registers while the run stays on that group (reloaded from LDS when it moves on).
   float xa[NT][G::CPL][G::EPC];
   int a_cur = -1;
   auto consume = [&](const u32x4 (&w)[U][G::CPL]) {
@@ -758,6 +971,7 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
   issue(w0);
   issue(w1);
   sta.store(sA);
+  if (sh) stb.store(sA + (size_t)nslot * G::K);
   // (n_act == 0 marks tables that failed validation: the routed terms are then left out, and
   // positions are clamped so that no index leaves the block's arrays)
   for (int i = threadIdx.x; i < nslot; i += blockDim.x) {
@@ -782,7 +996,8 @@ __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(MINB *
       float acc = pre ? pre_h : h32[(size_t)t * H + n];
       if (n_act > 0)
         for (int j = 0; j < k; ++j) acc = fmaf(sG[t * k + j], part[sQ[t * k + j] * RB + nl], acc);
-      Elem<T>::store(out, (size_t)t * H + n, acc + (pre ? pre_y : ys[(size_t)t * H + n]));
+      const float y = sh ? part[(nslot + t) * RB + nl] : (pre ? pre_y : ys[(size_t)t * H + n]);
+      Elem<T>::store(out, (size_t)t * H + n, acc + y);
     }
   }
 }
@@ -926,6 +1141,30 @@ hipError_t oproj_t(const Shape& s, const Device& d, int B, const void* x, const 
   return hipGetLastError();
 }
 
+template <typename T, int CPR, int CPS, int R>
+hipError_t oproj_router_t(const Shape& s, const Device& d, int B, const void* x, const void* r,
+                          const void* w_o, const void* w_r, const void* mr, float* h32,
+                          void* h_out, float* part, hipStream_t st) {
+  using G = Geo<T, CPR>;
+  constexpr int R2 = (R > 1 && G::CPL > 4) ? R / 2 : R;
+  const int npl = router_oproj_planes(s);
+  const int RS = s.H / Geo<T, CPS>::K;
+  if (RS * Geo<T, CPS>::K != s.H || RS + npl > kMaxTopkSplits) return hipErrorInvalidValue;
+  const int rows_per_unit = G::RPW * (B == 1 ? R : R2);
+  const int units = (s.H + npl * s.E + rows_per_unit - 1) / rows_per_unit;
+  const LaunchShape ls = balanced(d, units);
+  if ((long)ls.blocks * (ls.threads / 64) < (long)s.E * RS) return hipErrorInvalidValue;
+  auto kern = B == 1 ? oproj_router_gemv_kernel<T, CPR, CPS, 1, R>
+                     : oproj_router_gemv_kernel<T, CPR, CPS, 2, R2>;
+  const bool regs = (B == 1 ? 1 : 2) * G::CPL <= 14;
+  const size_t lds = ((size_t)B * s.H + (regs ? 0 : (size_t)B * G::K)) * sizeof(float);
+  allow_lds(kern, lds);
+  hipLaunchKernelGGL(kern, dim3(ls.blocks), dim3(ls.threads), lds, st, (const T*)x, (const T*)r,
+                     (const T*)w_o, (const T*)w_r, (const T*)mr, npl, h32, (T*)h_out, part, s.H,
+                     s.E, RS);
+  return hipGetLastError();
+}
+
 template <typename T, int CPS, int CPRH>
 hipError_t router_logits_t(const Shape& s, const Device& d, int B, const float* h32,
                            const void* w_r, float* part, const void* ws13, const Routing& rt,
@@ -947,34 +1186,42 @@ hipError_t gateup_t(const Shape& s, const Device& d, int B, const float* u, cons
                     bool shared, const Routing& rt, float* A, const GateupExtras& x,
                     hipStream_t st) {
   if (x.part && (x.splits > kMaxTopkSplits || shared)) return hipErrorInvalidValue;
+  if (x.ws13 && (shared || x.ws2 || s.Is != s.I || !x.As_out)) return hipErrorInvalidValue;
   const size_t lds = (size_t)B * Geo<T, CPR>::K * sizeof(float);
   auto pick = [&](auto k1, auto k2) { return B == 1 ? k1 : k2; };
-  auto kern = x.part ? pick(gateup_gemv_kernel<T, CPR, CPRS, 1, true>,
-                            gateup_gemv_kernel<T, CPR, CPRS, 2, true>)
-                     : pick(gateup_gemv_kernel<T, CPR, CPRS, 1, false>,
-                            gateup_gemv_kernel<T, CPR, CPRS, 2, false>);
+  if (x.ws13 && !x.part) return hipErrorInvalidValue;  // the shared gate/up covers a top-k
+  // (the shared gate/up prologue serves the fused-router plan, bf16 layers only)
+  constexpr bool kSgu = std::is_same<T, uint16_t>::value;
+  if (x.ws13 && !kSgu) return hipErrorInvalidValue;
+  auto kern = x.ws13 ? pick(gateup_gemv_kernel<T, CPR, CPRS, 1, true, kSgu>,
+                            gateup_gemv_kernel<T, CPR, CPRS, 2, true, kSgu>)
+              : x.part ? pick(gateup_gemv_kernel<T, CPR, CPRS, 1, true, false>,
+                              gateup_gemv_kernel<T, CPR, CPRS, 2, true, false>)
+                       : pick(gateup_gemv_kernel<T, CPR, CPRS, 1, false, false>,
+                              gateup_gemv_kernel<T, CPR, CPRS, 2, false, false>);
   allow_lds(kern, lds);
   const int inter = shared ? s.Is : s.I;
   hipLaunchKernelGGL(kern, dim3(d.num_cu), dim3(kGemvThreads), lds, st, u, (const T*)w13, inter,
                      s.k, B, shared ? 1 : 0, rt, A, x.part, x.splits, x.bias, s.E, s.routed_scale,
-                     (const T*)x.ws2, x.As, x.ys, s.H, (const T*)x.norm.gamma, x.norm.eps);
+                     (const T*)x.ws2, x.As, x.ys, s.H, (const T*)x.norm.gamma, x.norm.eps,
+                     (const T*)x.ws13, s.Is, x.As_out);
   return hipGetLastError();
 }
 
 template <typename T, int CPR>
-size_t down_combine_lds(const Shape& s, int B, int RG) {
+size_t down_combine_lds(const Shape& s, int B, int RG, bool sh) {
   using G = Geo<T, CPR>;
-  const int nslot = B * s.k;
-  return ((size_t)nslot * G::K + (size_t)nslot * RG * G::RPW + 2 * (size_t)nslot) * 4;
+  const int nslot = B * s.k, npos = nslot + (sh ? B : 0);
+  return ((size_t)npos * G::K + (size_t)npos * RG * G::RPW + 2 * (size_t)nslot) * 4;
 }
 
 // Row groups per block: two blocks of 8 waves per CU when their LDS fits and the kernel
 // fits in 128 VGPRs (not so for two tokens' activations over 4 KB rows), else one.
 template <typename T, int CPR>
-int down_groups_per_block(const Shape& s, const Device& d, int B, int* per_cu) {
+int down_groups_per_block(const Shape& s, const Device& d, int B, bool sh, int* per_cu) {
   const int groups = (s.H + Geo<T, CPR>::RPW - 1) / Geo<T, CPR>::RPW;
   const int rg2 = (groups + 2 * d.num_cu - 1) / (2 * d.num_cu);
-  const bool two = 2 * down_combine_lds<T, CPR>(s, B, rg2) <= (size_t)d.max_lds &&
+  const bool two = 2 * down_combine_lds<T, CPR>(s, B, rg2, sh) <= (size_t)d.max_lds &&
                    !(B == 2 && Geo<T, CPR>::CPL >= 4);
   if (per_cu) *per_cu = two ? 2 : 1;
   return two ? rg2 : (groups + d.num_cu - 1) / d.num_cu;
@@ -983,12 +1230,14 @@ int down_groups_per_block(const Shape& s, const Device& d, int B, int* per_cu) {
 template <typename T, int CPR, int U>
 hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A, const float* ys,
                           const void* w2, const float* h32, const Routing& rt, void* out,
-                          hipStream_t st) {
+                          const void* ws2, const float* As, hipStream_t st) {
   using G = Geo<T, CPR>;
+  const bool sh = ws2 != nullptr;
+  if (sh && (!As || s.Is != s.I)) return hipErrorInvalidValue;
   int per_cu = 1;
-  const int RG = down_groups_per_block<T, CPR>(s, d, B, &per_cu);
+  const int RG = down_groups_per_block<T, CPR>(s, d, B, sh, &per_cu);
   const int groups = (s.H + G::RPW - 1) / G::RPW;
-  const size_t lds = down_combine_lds<T, CPR>(s, B, RG);
+  const size_t lds = down_combine_lds<T, CPR>(s, B, RG, sh);
   constexpr int NT2_PER_CU = Geo<T, CPR>::CPL >= 4 ? 1 : 2;
   auto kern = per_cu == 2 ? (B == 1 ? down_combine_kernel<T, CPR, 1, U, 8, 2>
                                     : down_combine_kernel<T, CPR, 2, U, 8, NT2_PER_CU>)
@@ -996,7 +1245,7 @@ hipError_t down_combine_t(const Shape& s, const Device& d, int B, const float* A
                                     : down_combine_kernel<T, CPR, 2, U, 8, 1>);
   allow_lds(kern, lds);
   hipLaunchKernelGGL(kern, dim3((groups + RG - 1) / RG), dim3(kGemvThreads), lds, st, A, ys,
-                     (const T*)w2, h32, s.H, s.k, B, RG, rt, (T*)out);
+                     (const T*)w2, h32, s.H, s.k, B, RG, rt, (T*)out, (const T*)ws2, As);
   return hipGetLastError();
 }
 
@@ -1037,6 +1286,37 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
   return hipErrorInvalidValue;
 }
 
+bool router_fused_applies(const Shape& s) {
+  return s.dtype == 1 && s.Ko < s.H && s.H == 7168 && gemv_supported(s, 1);
+}
+
+int router_oproj_planes(const Shape& s) { return s.dtype == 1 ? 2 : 1; }
+
+int router_fused_splits(const Shape& s) { return 2 + router_oproj_planes(s); }
+
+size_t router_oproj_product_bytes(const Shape& s) {
+  return (size_t)s.E * router_oproj_planes(s) * s.Ko * (s.dtype == 1 ? 2 : 4);
+}
+
+hipError_t launch_router_oproj_product(const Shape& s, const void* w_r, const void* w_o, void* mr,
+                                       hipStream_t st) {
+  if (!router_fused_applies(s)) return hipErrorInvalidValue;
+  const dim3 grid((s.Ko + 63) / 64, (s.E + 31) / 32);
+  hipLaunchKernelGGL(router_oproj_product_kernel<uint16_t>, grid, dim3(256), 0, st,
+                     (const uint16_t*)w_r, (const uint16_t*)w_o, s.E, s.H, s.Ko, (uint16_t*)mr,
+                     router_oproj_planes(s));
+  return hipGetLastError();
+}
+
+hipError_t launch_oproj_router_gemv(const Shape& s, const Device& d, int B, const void* x,
+                                    const void* r, const void* w_o, const void* w_r, const void* mr,
+                                    float* h32, void* h_out, float* part, hipStream_t st) {
+  const int c = cpr_of(s.Ko, s.dtype);
+  if (router_fused_applies(s) && c == 56)  // 448-wide input slice; router slices of 3584
+    return oproj_router_t<uint16_t, 56, 448, 4>(s, d, B, x, r, w_o, w_r, mr, h32, h_out, part, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_router_logits(const Shape& s, const Device& d, int B, const float* h32,
                                 const void* w_r, float* part, const void* ws13, const Routing& rt,
                                 float* As, const Norm& nm, hipStream_t st) {
@@ -1060,24 +1340,26 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
   return hipErrorInvalidValue;
 }
 
-size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B) {
+size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B, bool shared_down) {
   const int c = cpr_of(s.I, s.dtype);
+  const bool sh = shared_down;
   if (s.dtype == 1 && c == 256)
-    return down_combine_lds<uint16_t, 256>(s, B, down_groups_per_block<uint16_t, 256>(s, d, B, nullptr));
+    return down_combine_lds<uint16_t, 256>(s, B, down_groups_per_block<uint16_t, 256>(s, d, B, sh, nullptr), sh);
   if (s.dtype == 1 && c == 16)
-    return down_combine_lds<uint16_t, 16>(s, B, down_groups_per_block<uint16_t, 16>(s, d, B, nullptr));
-  return down_combine_lds<float, 32>(s, B, down_groups_per_block<float, 32>(s, d, B, nullptr));
+    return down_combine_lds<uint16_t, 16>(s, B, down_groups_per_block<uint16_t, 16>(s, d, B, sh, nullptr), sh);
+  return down_combine_lds<float, 32>(s, B, down_groups_per_block<float, 32>(s, d, B, sh, nullptr), sh);
 }
 
 hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
                                     const float* ys, const void* w2, const float* h32,
-                                    const Routing& rt, void* out, hipStream_t st) {
+                                    const Routing& rt, void* out, const void* ws2,
+                                    const float* As, hipStream_t st) {
   const int c = cpr_of(s.I, s.dtype);
   if (s.dtype == 1) {
-    if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, ys, w2, h32, rt, out, st);
-    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, ys, w2, h32, rt, out, st);
+    if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
+    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
   } else if (c == 32) {
-    return down_combine_t<float, 32, 2>(s, d, B, A, ys, w2, h32, rt, out, st);
+    return down_combine_t<float, 32, 2>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
   }
   return hipErrorInvalidValue;
 }

@@ -72,6 +72,20 @@ bool gemv_supported(const Shape& s, int B);
 hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void* x, const void* r,
                              const void* w_o, float* h32, void* h_out, hipStream_t st);
 
+// The router-o-proj product mr = W_r W_o of a layer ([planes][E][Ko] in the weight dtype:
+// bf16 as hi + lo planes, fp32 as one), computed once (fp64 accumulation).
+bool router_fused_applies(const Shape& s);  // bf16 GEMV shapes with Ko < H
+int router_oproj_planes(const Shape& s);
+size_t router_oproj_product_bytes(const Shape& s);
+hipError_t launch_router_oproj_product(const Shape& s, const void* w_r, const void* w_o, void* mr,
+                                       hipStream_t st);
+// o-proj + residual and the router logit partials in one launch, the router reading x and r
+// (logit = W_r . r + mr . x): part[router_fused_splits(s)][B][E].
+int router_fused_splits(const Shape& s);
+hipError_t launch_oproj_router_gemv(const Shape& s, const Device& d, int B, const void* x,
+                                    const void* r, const void* w_o, const void* w_r, const void* mr,
+                                    float* h32, void* h_out, float* part, hipStream_t st);
+
 // Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s]; with ws13 !=
 // nullptr the same launch computes the shared expert's gate/up,
 // As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  The top-k runs in the routed gate/up
@@ -90,6 +104,8 @@ struct GateupExtras {
   const void* ws2 = nullptr;    // shared expert's down-projection ys = Ws2 . As in the launch
   const float* As = nullptr;
   float* ys = nullptr;
+  const void* ws13 = nullptr;   // or its gate/up As_out = SwiGLU(Ws13 . u) in the launch
+  float* As_out = nullptr;
   Norm norm;                    // stage u = norm(u) (every block from the rows it reads)
 };
 
@@ -101,11 +117,13 @@ hipError_t launch_gateup_gemv(const Shape& s, const Device& d, int B, const floa
 
 // Down projection of the active experts fused with the weighted combine (GEMV path):
 // out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] Y[inv_perm[t*k+j]][n] + ys[t][n]) with
-// Y[p][n] = W2_e[n] . A[p] kept on chip and ys the shared expert's output.
-size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B);
+// Y[p][n] = W2_e[n] . A[p] kept on chip and ys the shared expert's output: with ws2 != nullptr
+// computed in the same launch from As (ys unused), else read from ys.
+size_t down_combine_gemv_lds(const Shape& s, const Device& d, int B, bool shared_down);
 hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, const float* A,
                                     const float* ys, const void* w2, const float* h32,
-                                    const Routing& rt, void* out, hipStream_t st);
+                                    const Routing& rt, void* out, const void* ws2,
+                                    const float* As, hipStream_t st);
 // Weighted combine of Y / ys written by the grouped MFMA down-projection.
 hipError_t launch_combine(const Shape& s, int B, const float* h32, const float* Y, const float* ys,
                           const Routing& rt, void* out, hipStream_t st);
@@ -145,6 +163,14 @@ int mfma_router_splits(const Shape& s);
 // o-proj partials part[sp][t][n] over the K slices, then h32 = r + sum (and h_out).
 hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x, float* part,
                              const void* w_o, hipStream_t st);
+// Split-K path, up to 16 tokens, layers with the router-o-proj product (bf16, Ko = 448): the
+// o-proj (h32 = r + W_o x directly) and the router logit partials from r and x in one launch,
+// part[mfma_fused_splits(s)][B][E].
+int mfma_fused_splits(const Shape& s);
+hipError_t launch_oproj_router_mfma(const Shape& s, const Device& d, int B, const void* x,
+                                    const void* r, const void* w_o, const void* w_r,
+                                    const void* mr, float* h32, float* oproj_part,
+                                    float* logit_part, hipStream_t st);
 hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const void* r,
                                float* h32, void* h_out, hipStream_t st);
 // One block per token: u32 = norm(h) with h = r + sum of the o-proj partials (also written to

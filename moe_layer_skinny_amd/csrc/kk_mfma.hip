@@ -205,6 +205,10 @@ struct UnitArgs {
   // positions gu_P - B ..) instead of the SwiGLU into A / As
   float* gu_part;
   int gu_P;
+  // MODE 2 with one K chunk and resid != nullptr: h32[t][n] = resid[t][n] + the product
+  // (the o-proj with its residual add) instead of the partial
+  const uint16_t* resid;
+  float* h32;
 };
 
 // ------------------------------------------------------------------------------ LDS-staged
@@ -388,7 +392,13 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
         o = outp + ((size_t)chunk * x.B + p0 + j) * out_rows + row0 + 4 * gg;
       else
         o = outp + (size_t)(p0 + j) * out_rows + row0 + 4 * gg;
-      if (MODE == 0 && x.gu_part) {
+      if (MODE == 2 && x.resid) {
+        const size_t ho = (size_t)(p0 + j) * out_rows + row0 + 4 * gg;
+        const float4 r0 = Elem<uint16_t>::load4(x.resid, ho);
+        const float4 r1 = Elem<uint16_t>::load4(x.resid, ho + 16);
+        *reinterpret_cast<float4*>(x.h32 + ho) = float4{r0.x + s0[0], r0.y + s0[1], r0.z + s0[2], r0.w + s0[3]};
+        *reinterpret_cast<float4*>(x.h32 + ho + 16) = float4{r1.x + s1[0], r1.y + s1[1], r1.z + s1[2], r1.w + s1[3]};
+      } else if (MODE == 0 && x.gu_part) {
         const int pos = shared ? x.gu_P - x.B + p0 + j : p0 + j;
         float* q = x.gu_part + ((size_t)chunk * x.gu_P + pos) * 2 * x.I + row0 + 4 * gg;
         *reinterpret_cast<float4*>(q) = float4{s0[0], s0[1], s0[2], s0[3]};
@@ -600,6 +610,36 @@ __global__ __launch_bounds__(256) void mfma_token_split_kernel(UnitArgs x) {
   }
 }
 
+// The o-proj and the router in one launch, for up to 16 tokens (one token tile), the router not
+// waiting for h: logit = W_r . r + (W_r W_o) . x, with the router-o-proj product kept as two
+// bf16 planes ([2][E][Ko]).  Four split-K products of bf16 activations: the router rows against
+// r over eight K chunks of two stages (logit partial slots 0-7), the o-proj (one K chunk:
+// h32 = r + W_o x in its epilogue), and the two product planes against x (slots 8 and 9).  The
+// router's units, the longest, come first.
+struct MultiArgs {
+  UnitArgs p[4];
+  int units[4];
+};
+template <int KS>
+__global__ __launch_bounds__(256) void mfma_oproj_router_kernel(MultiArgs m) {
+  extern __shared__ u32x4 lds[];
+  const int c1 = m.units[0], c2 = c1 + m.units[1], c3 = c2 + m.units[2], total = c3 + m.units[3];
+  auto run = [&](const UnitArgs& x, int u) {
+    const int tile = u / x.chunks, chunk = u - tile * x.chunks;
+    staged_unit<2, 1, KS, 1, true>(x, lds, tile, chunk, 0, x.B, x.w_routed, false);
+  };
+  for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
+    if (unit < c1)
+      run(m.p[0], unit);
+    else if (unit < c2)
+      run(m.p[1], unit - c1);
+    else if (unit < c3)
+      run(m.p[2], unit - c2);
+    else
+      run(m.p[3], unit - c3);
+  }
+}
+
 // Grouped launch (gate/up or down) for batches over 16 tokens: groups of more than 16 tokens
 // (the shared expert, and any routed expert that hot) use TTB-wide token tiles, the rest one
 // tile, in the same launch; the groups are walked from the last (the shared expert) down, so
@@ -744,6 +784,45 @@ hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void*
     return staged_t<2, 4, 64, 1, true>(d, a, units, st);  // 448 = 7 x 64
   }
   return hipErrorInvalidValue;
+}
+
+constexpr int kFusedRouterChunks = 8;
+int mfma_fused_splits(const Shape& s) { return kFusedRouterChunks + 2; }
+
+hipError_t launch_oproj_router_mfma(const Shape& s, const Device& d, int B, const void* x,
+                                    const void* r, const void* w_o, const void* w_r,
+                                    const void* mr, float* h32, float* oproj_part,
+                                    float* logit_part, hipStream_t st) {
+  constexpr int KS = 448;  // the 448-wide input slice in one stage; router chunks of 4 stages
+  if (B > 16 || s.dtype != 1 || s.Ko != KS || s.H % (kFusedRouterChunks * KS) || s.E % 32)
+    return hipErrorInvalidValue;
+  MultiArgs m{};
+  auto product = [&](int q, const void* w, const void* act, float* out, int N, int K, int chunks) {
+    UnitArgs& a = m.p[q];
+    a.w_routed = (const uint16_t*)w;
+    a.act_routed = act;
+    a.out_routed = out;
+    a.B = B;
+    a.N = N;
+    a.K = K;
+    a.chunks = chunks;
+    m.units[q] = (N / 32) * chunks;
+  };
+  const size_t slot = (size_t)B * s.E;
+  const int rc = kFusedRouterChunks;
+  product(0, w_r, r, logit_part, s.E, s.H, rc);
+  product(1, w_o, x, oproj_part, s.H, s.Ko, 1);
+  m.p[1].resid = (const uint16_t*)r;
+  m.p[1].h32 = h32;
+  product(2, mr, x, logit_part + rc * slot, s.E, s.Ko, 1);
+  product(3, (const uint16_t*)mr + (size_t)s.E * s.Ko, x, logit_part + (rc + 1) * slot, s.E, s.Ko, 1);
+  auto kern = mfma_oproj_router_kernel<KS>;
+  constexpr size_t lds = staged_lds(1, KS, 1);
+  if (lds > 64 * 1024) allow_lds_mfma(kern);
+  static thread_local int bpc = 0;
+  const int units = m.units[0] + m.units[1] + m.units[2] + m.units[3];
+  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, m);
+  return hipGetLastError();
 }
 
 hipError_t launch_oproj_reduce(const Shape& s, int B, const float* part, const void* r,

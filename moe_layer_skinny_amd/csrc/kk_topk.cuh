@@ -126,7 +126,7 @@ __device__ __forceinline__ void load_bias(const float* __restrict__ bias, int E,
 // kMaxTopkSplits), summed in slice order.  All global loads (partials and bias) are issued
 // before any is used (addresses clamped instead of branched around, so nothing waits on a
 // join).
-constexpr int kMaxTopkSplits = 8;
+constexpr int kMaxTopkSplits = 10;
 __device__ __forceinline__ void topk_row(const float* part, int splits, const float* __restrict__ bias,
                                 int B, int E, int k, float routed_scale, int t, const Routing& rt,
                                 int* sel) {
