@@ -36,7 +36,7 @@ namespace kk {
 namespace {
 
 // K chunks of the shared expert's split-K gate/up over more than 32 tokens.
-constexpr int kSharedSplits = 7;
+constexpr int kSharedSplits = 14;
 // Gate/up K chunks for experts with a small intermediate: their groups have only I/16 row tiles
 // (8 at I = 128), too few units to fill the chip, so each unit also takes one K chunk.
 constexpr int kGateupSplits = 4;
@@ -586,6 +586,145 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
   }
 }
 
+// Split-K product for many tokens with tall units: a unit is 128 weight rows x one K chunk for
+// all the group's tokens (16 TT slots).  Each stage the block stages the 128 rows' KS columns of
+// weights and the tokens' KS activations (NTERM bf16 terms) in LDS once, and wave w multiplies
+// its own 32-row tile pair against every token tile over the stage's whole depth, so a stage's
+// activations are staged once per 128 weight rows (not once per 32) and no cross-wave reduction
+// is needed.  Out: part[chunk][t][n] for t < B (MODE 2 of UnitArgs).  The next stage's loads
+// are in flight while the current one is multiplied; a stage past the end re-reads the
+// activation buffer.
+template <int TT, int KS, int NTERM, bool BF16SRC, int RTW = 2>
+__global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
+  constexpr int ROWS = 64 * RTW, K8 = KS / 8, WP = K8 + 1, NTOK = 16 * TT;
+  constexpr int WLD = ROWS * K8 / 256;          // weight chunks per thread per stage
+  constexpr int ALD = (NTOK * K8 + 255) / 256;  // activation chunks (8 values) per thread
+  constexpr int AW = BF16SRC ? 1 : 2;           // 16-byte words per activation chunk
+  constexpr int KSTEPS = KS / 32;
+  static_assert(ROWS * K8 % 256 == 0, "whole weight chunks per thread");
+  extern __shared__ u32x4 lds[];
+  u32x4* lw = lds;                  // [ROWS][WP]
+  u32x4* la = lds + ROWS * WP;      // [NTERM][K8][NTOK]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
+  const int K = x.K, N = x.N, B = x.B, chunks = x.chunks;
+  const int kchunk = K / chunks, nst = kchunk / KS;
+  const int units = (N / ROWS) * chunks;
+  const int ntt = (B + 15) / 16;
+  // slots past the batch stay zero in LDS for the whole launch
+  for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
+    if (q % NTOK >= B) la[q] = u32x4{0u, 0u, 0u, 0u};
+  const void* dummy = x.act_routed;
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int rb = unit / chunks, chunk = unit - rb * chunks;
+    const int row0 = rb * ROWS, kbase = chunk * kchunk;
+    const uint16_t* wsrc[WLD];
+#pragma unroll
+    for (int i = 0; i < WLD; ++i) {
+      const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+      wsrc[i] = x.w_routed + (size_t)(row0 + rr) * K + kbase + ch * 8;
+    }
+    const void* asrc[ALD];
+    bool aok[ALD];
+#pragma unroll
+    for (int i = 0; i < ALD; ++i) {
+      const int q = min(tid + 256 * i, NTOK * K8 - 1), j = q / K8, ch = q - j * K8;
+      aok[i] = tid + 256 * i < NTOK * K8 && j < B;
+      const size_t off = (size_t)(aok[i] ? j : 0) * K + kbase + ch * 8;
+      asrc[i] = BF16SRC ? (const void*)((const uint16_t*)x.act_routed + off)
+                        : (const void*)((const float*)x.act_routed + off);
+    }
+    u32x4 wreg[WLD], areg[ALD][AW];
+    auto load_stage = [&](int st) {
+      const bool live = st < nst;
+#pragma unroll
+      for (int i = 0; i < WLD; ++i)
+        wreg[i] = __builtin_nontemporal_load(live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
+                                                  : reinterpret_cast<const u32x4*>(dummy));
+#pragma unroll
+      for (int i = 0; i < ALD; ++i) {
+        const u32x4* p = !live ? reinterpret_cast<const u32x4*>(dummy)
+                         : BF16SRC ? reinterpret_cast<const u32x4*>((const uint16_t*)asrc[i] + st * KS)
+                                   : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
+#pragma unroll
+        for (int w = 0; w < AW; ++w) areg[i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+      for (int i = 0; i < WLD; ++i) {
+        const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
+        lw[rr * WP + ch] = wreg[i];
+      }
+#pragma unroll
+      for (int i = 0; i < ALD; ++i) {
+        const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
+        if (q < NTOK * K8 && aok[i]) {
+          if constexpr (BF16SRC) {
+            la[ch * NTOK + j] = areg[i][0];
+          } else {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = __uint_as_float(areg[i][0][e]);
+              v[4 + e] = __uint_as_float(areg[i][1][e]);
+            }
+            u32x4 terms[NTERM];
+            split_terms<NTERM>(v, terms);
+#pragma unroll
+            for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
+          }
+        }
+      }
+    };
+    f32x4 acc[RTW][TT];
+#pragma unroll
+    for (int r = 0; r < RTW; ++r)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_stage(0);
+    for (int st = 0; st < nst; ++st) {
+      store_stage();
+      __syncthreads();
+      if (st + 1 < nst) load_stage(st + 1);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        u32x4 a[RTW];
+#pragma unroll
+        for (int r = 0; r < RTW; ++r) a[r] = lw[(wave * 16 * RTW + 16 * r + c) * WP + ks * 4 + g];
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+          if (tt < ntt) {
+#pragma unroll
+            for (int q2 = 0; q2 < NTERM; ++q2) {
+              const u32x4 bq = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
+#pragma unroll
+              for (int r = 0; r < RTW; ++r) acc[r][tt] = mfma(a[r], bq, acc[r][tt]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // lane (g, c) of each accumulator holds rows 4 g .. 4 g + 3 of its 16-row tile, token c
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int j = tt * 16 + c;
+      if (tt < ntt && j < B) {
+        float* o = x.out_routed + ((size_t)chunk * B + j) * N + row0 + wave * 16 * RTW + 4 * g;
+#pragma unroll
+        for (int r = 0; r < RTW; ++r)
+          *reinterpret_cast<float4*>(o + 16 * r) =
+              float4{acc[r][tt][0], acc[r][tt][1], acc[r][tt][2], acc[r][tt][3]};
+      }
+    }
+  }
+}
+
+// LDS bytes of one block of mfma_tall_kernel<TT, KS, NTERM, .., RTW>.
+constexpr size_t tall_lds(int TT, int KS, int NTERM, int RTW = 2) {
+  return (size_t)(64 * RTW * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
+}
+
 // Split-K product with the tokens split as well: units (row tile, K chunk, 16-token quarter),
 // so that a launch over many tokens but few row tiles (the router: 12 row tiles x 7 chunks)
 // still fills the chip.  Each quarter reads the unit's weights; the quarters of one (tile,
@@ -708,6 +847,19 @@ hipError_t token_split_t(const Device& d, const UnitArgs& x, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int TT, int KS, int NTERM, bool BF16SRC, int RTW = 2>
+hipError_t tall_t(const Device& d, const UnitArgs& x, hipStream_t st) {
+  constexpr int ROWS = 64 * RTW;
+  if (x.N % ROWS || x.K % x.chunks || (x.K / x.chunks) % KS || x.B > 16 * TT) return hipErrorInvalidValue;
+  auto kern = mfma_tall_kernel<TT, KS, NTERM, BF16SRC, RTW>;
+  constexpr size_t lds = tall_lds(TT, KS, NTERM, RTW);
+  if (lds > 64 * 1024) allow_lds_mfma(kern);
+  static thread_local int bpc = 0;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, (x.N / ROWS) * x.chunks, &bpc)), dim3(256),
+                     lds, st, x);
+  return hipGetLastError();
+}
+
 template <int MODE, int TTB, int KSB, int KS1>
 hipError_t grouped_t(const Device& d, const UnitArgs& x, int max_units, hipStream_t st) {
   auto kern = mfma_grouped_kernel<MODE, TTB, KSB, KS1>;
@@ -777,7 +929,13 @@ hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void*
   a.K = s.Ko;
   a.chunks = mfma_oproj_splits(s);
   const int units = (s.H / 32) * a.chunks;
-  if (s.Ko == 7168) return staged_dispatch<2, 1, true>(d, a, units, st);  // 7 x 1024 k
+  if (s.Ko == 7168) {  // 7 x 1024 k
+    // over 16 tokens 128-row units, so that the tokens' activations are staged once per 128
+    // weight rows
+    if (B > 32) return tall_t<4, 128, 1, true>(d, a, st);
+    if (B > 16) return tall_t<2, 128, 1, true>(d, a, st);
+    return staged_dispatch<2, 1, true>(d, a, units, st);
+  }
   if (s.Ko == 448) {  // up to 32 tokens the whole 448 k in one stage (one weight round trip)
     if (B <= 16) return staged_t<2, 1, 448, 1, true>(d, a, units, st);
     if (B <= 32) return staged_t<2, 2, 448, 1, true>(d, a, units, st);
@@ -886,8 +1044,12 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   const int nslot = B * s.k;
   auto reduce = [&](const SwigluRegion& r0, const SwigluRegion& r1) {
     const int n = (r0.rows + r1.rows) * s.I;
-    hipLaunchKernelGGL((swiglu_reduce_kernel<8>), dim3((n + 255) / 256), dim3(256), 0, st, r0, r1,
-                       s.I);
+    if (r0.chunks > 8 || r1.chunks > 8)
+      hipLaunchKernelGGL((swiglu_reduce_kernel<16>), dim3((n + 255) / 256), dim3(256), 0, st, r0,
+                         r1, s.I);
+    else
+      hipLaunchKernelGGL((swiglu_reduce_kernel<8>), dim3((n + 255) / 256), dim3(256), 0, st, r0,
+                         r1, s.I);
     return hipGetLastError();
   };
   if (split) {
@@ -913,9 +1075,9 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   }
   if (B <= 16) return grouped_dispatch<0>(d, a, max_units, st);
   // over 32 tokens (not split) the shared expert's gate/up is a split-K product of its own
-  // (its group alone has too few row tiles to fill the chip), its units split by 16-token
-  // quarter as well; then every routed expert, hot ones cut into pieces of 16 positions, in
-  // one one-tile launch, and one launch applies the SwiGLU to the shared partials
+  // (its group alone has too few row tiles to fill the chip) with 128-row units; then every
+  // routed expert, hot ones cut into pieces of 16 positions, in one one-tile launch, and one
+  // launch applies the SwiGLU to the shared partials
   UnitArgs sh{};
   sh.w_routed = (const uint16_t*)ws13;
   sh.act_routed = h32;
@@ -924,7 +1086,7 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   sh.N = 2 * s.Is;
   sh.K = s.H;
   sh.chunks = kSharedSplits;
-  hipError_t e = token_split_t<256, 2, false>(d, sh, st);
+  hipError_t e = tall_t<4, 128, 2, false>(d, sh, st);
   if (e != hipSuccess) return e;
   const int units = (s.E + nslot / 16 + 1) * (s.I / 16);
   e = staged_t<0, 1, 256, 2, false, 4>(d, a, units, st);
