@@ -207,8 +207,8 @@ int forced_path() {
 }
 
 // Whether batch B on the split-K path runs the o-proj and the router as one launch (a layer with
-// the router-o-proj product, up to 16 tokens).
-bool mfma_fused(const kk_ctx* c, int B) { return c->mr != nullptr && B <= 16; }
+// the router-o-proj product).
+bool mfma_fused(const kk_ctx* c, int B) { return c->mr != nullptr; }
 
 kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   std::memset(p, 0, sizeof *p);

@@ -163,8 +163,8 @@ int mfma_router_splits(const Shape& s);
 // o-proj partials part[sp][t][n] over the K slices, then h32 = r + sum (and h_out).
 hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void* x, float* part,
                              const void* w_o, hipStream_t st);
-// Split-K path, up to 16 tokens, layers with the router-o-proj product (bf16, Ko = 448): the
-// o-proj (h32 = r + W_o x directly) and the router logit partials from r and x in one launch,
+// Split-K path, layers with the router-o-proj product (bf16, Ko = 448): the o-proj
+// (h32 = r + W_o x directly) and the router logit partials from r and x in one launch,
 // part[mfma_fused_splits(s)][B][E].
 int mfma_fused_splits(const Shape& s);
 hipError_t launch_oproj_router_mfma(const Shape& s, const Device& d, int B, const void* x,

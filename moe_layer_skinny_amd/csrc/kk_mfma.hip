@@ -749,33 +749,46 @@ __global__ __launch_bounds__(256) void mfma_token_split_kernel(UnitArgs x) {
   }
 }
 
-// The o-proj and the router in one launch, for up to 16 tokens (one token tile), the router not
-// waiting for h: logit = W_r . r + (W_r W_o) . x, with the router-o-proj product kept as two
-// bf16 planes ([2][E][Ko]).  Four split-K products of bf16 activations: the router rows against
-// r over eight K chunks of two stages (logit partial slots 0-7), the o-proj (one K chunk:
-// h32 = r + W_o x in its epilogue), and the two product planes against x (slots 8 and 9).  The
-// router's units, the longest, come first.
+// The o-proj and the router in one launch, the router not waiting for h: logit = W_r . r +
+// (W_r W_o) . x, with the router-o-proj product kept as two bf16 planes ([2][E][Ko]).  Four
+// split-K products of bf16 activations: the router rows against r over eight K chunks of two
+// stages (logit partial slots 0-7), the o-proj (one K chunk: h32 = r + W_o x in its epilogue),
+// and the two product planes against x (slots 8 and 9).  Units are (product, row tile pair, K
+// chunk), the router's first (the longest); over 16 tokens (QUARTERS) each unit also takes one
+// 16-token quarter, the quarters of one (product, tile, chunk) 8 units apart so that they run on
+// blocks of one XCD and read its weights through that XCD's L2 (plain loads).
 struct MultiArgs {
   UnitArgs p[4];
   int units[4];
 };
-template <int KS>
+template <int KS, bool QUARTERS>
 __global__ __launch_bounds__(256) void mfma_oproj_router_kernel(MultiArgs m) {
   extern __shared__ u32x4 lds[];
-  const int c1 = m.units[0], c2 = c1 + m.units[1], c3 = c2 + m.units[2], total = c3 + m.units[3];
-  auto run = [&](const UnitArgs& x, int u) {
+  const int c1 = m.units[0], c2 = c1 + m.units[1], c3 = c2 + m.units[2], pairs = c3 + m.units[3];
+  const int B = m.p[0].B, nq = QUARTERS ? (B + 15) / 16 : 1;
+  const int total = QUARTERS ? (pairs + 7) / 8 * 8 * nq : pairs;
+  auto run = [&](const UnitArgs& x, int u, int q) {
     const int tile = u / x.chunks, chunk = u - tile * x.chunks;
-    staged_unit<2, 1, KS, 1, true>(x, lds, tile, chunk, 0, x.B, x.w_routed, false);
+    const int p0 = 16 * q;
+    staged_unit<2, 1, KS, 1, true, !QUARTERS>(x, lds, tile, chunk, p0, min(16, B - p0), x.w_routed,
+                                               false);
   };
   for (int unit = blockIdx.x; unit < total; unit += gridDim.x) {
-    if (unit < c1)
-      run(m.p[0], unit);
-    else if (unit < c2)
-      run(m.p[1], unit - c1);
-    else if (unit < c3)
-      run(m.p[2], unit - c2);
+    int tc = unit, q = 0;
+    if (QUARTERS) {
+      const int grp = unit / (8 * nq), r = unit - grp * 8 * nq;
+      q = r / 8;
+      tc = grp * 8 + (r & 7);
+      if (tc >= pairs) continue;
+    }
+    if (tc < c1)
+      run(m.p[0], tc, q);
+    else if (tc < c2)
+      run(m.p[1], tc - c1, q);
+    else if (tc < c3)
+      run(m.p[2], tc - c2, q);
     else
-      run(m.p[3], unit - c3);
+      run(m.p[3], tc - c3, q);
   }
 }
 
@@ -952,7 +965,7 @@ hipError_t launch_oproj_router_mfma(const Shape& s, const Device& d, int B, cons
                                     const void* mr, float* h32, float* oproj_part,
                                     float* logit_part, hipStream_t st) {
   constexpr int KS = 448;  // the 448-wide input slice in one stage; router chunks of 4 stages
-  if (B > 16 || s.dtype != 1 || s.Ko != KS || s.H % (kFusedRouterChunks * KS) || s.E % 32)
+  if (B > 64 || s.dtype != 1 || s.Ko != KS || s.H % (kFusedRouterChunks * KS) || s.E % 32)
     return hipErrorInvalidValue;
   MultiArgs m{};
   auto product = [&](int q, const void* w, const void* act, float* out, int N, int K, int chunks) {
@@ -974,12 +987,20 @@ hipError_t launch_oproj_router_mfma(const Shape& s, const Device& d, int B, cons
   m.p[1].h32 = h32;
   product(2, mr, x, logit_part + rc * slot, s.E, s.Ko, 1);
   product(3, (const uint16_t*)mr + (size_t)s.E * s.Ko, x, logit_part + (rc + 1) * slot, s.E, s.Ko, 1);
-  auto kern = mfma_oproj_router_kernel<KS>;
+  const int pairs = m.units[0] + m.units[1] + m.units[2] + m.units[3];
   constexpr size_t lds = staged_lds(1, KS, 1);
-  if (lds > 64 * 1024) allow_lds_mfma(kern);
-  static thread_local int bpc = 0;
-  const int units = m.units[0] + m.units[1] + m.units[2] + m.units[3];
-  hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, m);
+  if (B <= 16) {
+    auto kern = mfma_oproj_router_kernel<KS, false>;
+    if (lds > 64 * 1024) allow_lds_mfma(kern);
+    static thread_local int bpc = 0;
+    hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, pairs, &bpc)), dim3(256), lds, st, m);
+  } else {
+    auto kern = mfma_oproj_router_kernel<KS, true>;
+    if (lds > 64 * 1024) allow_lds_mfma(kern);
+    static thread_local int bpc = 0;
+    const int units = (pairs + 7) / 8 * 8 * ((B + 15) / 16);
+    hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, m);
+  }
   return hipGetLastError();
 }
 

@@ -60,9 +60,9 @@ def test_plan_is_mfma(name, B):
     cfg = synth.CONFIGS[name]
     split = (B <= 16 or B > 32) and cfg.inter <= 256
     want = (8 if B > 16 else 7) + split + (2 if B > 32 and not split else 0)
-    # a 448-wide o-proj slice without a norm: up to 16 tokens the o-proj (with its residual)
-    # and the router run as one launch (no reduce, no router launch), ten logit partials
-    fused = cfg.oproj_in < cfg.hidden and not cfg.norm and B <= 16
+    # a 448-wide o-proj slice without a norm: the o-proj (with its residual) and the router
+    # run as one launch (no reduce, no router launch), ten logit partials
+    fused = cfg.oproj_in < cfg.hidden and not cfg.norm
     assert p["kernels_per_step"] == want - (2 if fused else 0)
     assert p["oproj_splitk"] == (7 if cfg.oproj_in == 7168 else 1)
     assert p["router_splitk"] == (10 if fused else 7)
