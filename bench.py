@@ -32,7 +32,13 @@ FLUSH_BYTES = 1 << 30
 COPY_BYTES = 256 << 20
 # rocprofv3 HBM byte counters per dominant kernel and workload: committed summaries, valid only
 # while the kernel's sources hash to what they were when the counters were taken
-TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/topk_gateup_gemv_full_b1.json"}
+TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/topk_gateup_gemv_full_b1.json",
+                   ("gemv", "tp_rank", 1): "profiles/gemv_tp_rank_b1.json",
+                   ("splitk_mfma", "tp_rank", 8): "profiles/mfma_tp_rank_b8.json",
+                   ("splitk_mfma", "tp_rank", 64): "profiles/mfma_tp_rank_b64.json",
+                   ("splitk_mfma", "full_b8", 8): "profiles/grouped_mfma_full_b8.json",
+                   ("splitk_mfma", "verify_b8", 8): "profiles/grouped_mfma_verify_b8.json",
+                   ("splitk_mfma", "full_b64", 64): "profiles/grouped_mfma_full_b64.json"}
 
 
 def measured_traffic(path_name: str, workload: str, B: int):
