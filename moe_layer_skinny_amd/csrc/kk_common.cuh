@@ -290,4 +290,48 @@ __device__ __forceinline__ void dot2_lane(const u32x4 (&wa)[Geo<T, CPR>::CPL],
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// ---- MFMA operands (v_mfma_f32_16x16x32_bf16) ----------------------------------------
+// A: 16 rows x 32 k, B: 32 k x 16 columns, D: 16 x 16 fp32.  Lane l holds row (column)
+// l % 16 and k = 8 * (l / 16) + e of each operand; of D it holds rows 4 * (l / 16) + i,
+// column l % 16.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> packed bf16 (a in the low half), round to nearest even: gfx950's
+// v_cvt_pk_bf16_f32, the same bits as f32_to_bf16 for every non-NaN input.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// 8 fp32 values -> NTERM bf16 vectors (RNE), each term the rounding of what the previous
+// ones left over; the differences are exact in fp32.
+template <int NTERM>
+__device__ __forceinline__ void split_terms(const float (&x)[8], u32x4 (&out)[NTERM]) {
+  float r[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e];
+#pragma unroll
+  for (int q = 0; q < NTERM; ++q) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[e] = pack_bf16x2(r[2 * e], r[2 * e + 1]);
+      if (q + 1 < NTERM) {
+        r[2 * e] -= __uint_as_float(w[e] << 16);
+        r[2 * e + 1] -= __uint_as_float(w[e] & 0xffff0000u);
+      }
+    }
+    out[q] = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
 }  // namespace kk

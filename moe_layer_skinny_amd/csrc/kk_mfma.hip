@@ -41,36 +41,6 @@ constexpr int kSharedSplits = 14;
 // (8 at I = 128), too few units to fill the chip, so each unit also takes one K chunk.
 constexpr int kGateupSplits = 4;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-// 8 fp32 values -> NTERM bf16 vectors (RNE), each term the rounding of what the previous
-// ones left over; the differences are exact in fp32.
-template <int NTERM>
-__device__ __forceinline__ void split_terms(const float (&x)[8], u32x4 (&out)[NTERM]) {
-  float r[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = x[e];
-#pragma unroll
-  for (int q = 0; q < NTERM; ++q) {
-    uint32_t b[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      b[e] = f32_to_bf16(r[e]);
-      r[e] -= bf16_bits_to_f32(b[e]);
-    }
-    out[q] = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                   b[6] | (b[7] << 16)};
-  }
-}
-
 // h32[t][n] = r[t][n] + sum_sp part[sp][t][n] (slice order); h_out = RNE(h32) if given.
 template <typename T, int MAXS>
 __global__ __launch_bounds__(256) void oproj_reduce_kernel(const float* __restrict__ part,
