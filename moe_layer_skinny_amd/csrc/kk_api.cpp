@@ -248,6 +248,8 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   // tokens an unsplit gate/up adds the shared expert's split-K launch and its SwiGLU
   const bool split = kk::mfma_gateup_split(c->shape, B);
   p->kernels_per_step = (B > 16 ? 8 : 7) + (split ? 1 : 0) + (B > 32 && !split ? 2 : 0);
+  // (a small intermediate up to 16 tokens: the down-projection sums the K chunks itself)
+  if (kk::mfma_swiglu_in_down(c->shape, B)) p->kernels_per_step -= 1;
   if (mfma_fused(c, B)) {
     // o-proj (with the residual) + router logits from x and r in one launch: no reduce and
     // no router launch
@@ -428,7 +430,7 @@ kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* u, const float* h3
   KK_HIP(timed(c, K_DOWN_MFMA, s,
                [&] {
                  return kk::launch_down_mfma(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
-                                             p.Y, p.ys, s);
+                                             p.Y, p.ys, p.oproj_part, s);
                }),
          "down launch");
   KK_HIP(timed(c, K_COMBINE, s,

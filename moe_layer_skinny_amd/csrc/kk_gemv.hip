@@ -798,31 +798,34 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
 }
 
 // ------------------------------------------------------------------------------ combine (MFMA path)
-// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] * Y[inv_perm[t*k+j]][n] + ys[t][n]), j in
-// ascending expert order.  KMAX >= k; every load is issued before the sum (clamped indices,
-// zero gates past k) so the launch costs one memory latency.
+// out[t][n] = RNE(h32[t][n] + sum_j gate[t][j] * Y[row(t*k+j)][n] + ys[t][n]), j in ascending
+// expert order, row(slot) = slot when the down-projection wrote Y by slot (by_slot), else
+// inv_perm[slot].  KMAX >= k; every load is issued before the sum (clamped indices, zero gates
+// past k), so with Y by slot the launch costs one memory latency.
 template <typename T, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ h32,
                                                       const float* __restrict__ Y,
                                                       const float* __restrict__ ys, Routing rt,
-                                                      int H, int k, int B, T* __restrict__ out) {
+                                                      int H, int k, int B, bool by_slot,
+                                                      T* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= B * H) return;
   const int t = i / H, n = i - t * H;
-  float g[KMAX];
-  int q[KMAX];
+  float g[KMAX], y[KMAX];
   const bool routed = *rt.n_act > 0;  // 0: tables failed validation, routed terms left out
+  int q[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int slot = t * k + min(j, k - 1);
-    g[j] = (j < k && routed) ? rt.topk_gate[slot] : 0.f;
-    q[j] = min(max(rt.inv_perm[slot], 0), B * k - 1);
+    q[j] = by_slot ? slot : min(max(rt.inv_perm[slot], 0), B * k - 1);
+    g[j] = rt.topk_gate[slot];
   }
-  float y[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) y[j] = Y[(size_t)q[j] * H + n];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    y[j] = Y[(size_t)q[j] * H + n];
-    y[j] = routed ? y[j] : 0.f;  // unwritten rows of Y are never used
+    g[j] = (j < k && routed) ? g[j] : 0.f;
+    y[j] = (j < k && routed) ? y[j] : 0.f;  // unwritten rows of Y are never used
   }
   float acc = h32[i];
 #pragma unroll
@@ -1255,7 +1258,7 @@ hipError_t combine_t(const Shape& s, int B, const float* h32, const float* Y, co
   const int n = B * s.H;
   auto kern = s.k <= 8 ? combine_kernel<T, 8> : combine_kernel<T, 16>;
   hipLaunchKernelGGL(kern, dim3((n + 255) / 256), dim3(256), 0, st, h32, Y, ys, rt, s.H, s.k, B,
-                     (T*)out);
+                     mfma_y_by_slot(B), (T*)out);
   return hipGetLastError();
 }
 

@@ -185,14 +185,21 @@ hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const floa
 // (mfma_scratch_floats floats).
 size_t mfma_scratch_floats(const Shape& s, int B);
 // Whether batch B's gate/up also splits every group over K chunks (small intermediates), with
-// a SwiGLU launch of its own after it.
+// a SwiGLU launch of its own after it (or, with mfma_swiglu_in_down, inside the down-projection).
 bool mfma_gateup_split(const Shape& s, int B);
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
                               float* As, float* scratch, hipStream_t st);
-// Grouped down-projection -> Y (per position), ys (shared).
+// Whether the down-projection forms its activations itself, as the SwiGLU of the gate/up K-chunk
+// partials (small intermediate up to 16 tokens): the gate/up launch then leaves A / As unwritten.
+bool mfma_swiglu_in_down(const Shape& s, int B);
+// Whether the grouped down-projection writes the rows of Y by slot t*k + j (up to 16 tokens;
+// the combine then reads them without the inverse permutation) rather than by position.
+bool mfma_y_by_slot(int B);
+// Grouped down-projection -> Y (rows by slot or by position), ys (shared); its activations are A / As, or
+// with mfma_swiglu_in_down the SwiGLU of the gate/up partials in gu_part (the gate/up's scratch).
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, hipStream_t st);
+                            float* Y, float* ys, const float* gu_part, hipStream_t st);
 
 }  // namespace kk

@@ -179,6 +179,8 @@ struct UnitArgs {
   // (the o-proj with its residual add) instead of the partial
   const uint16_t* resid;
   float* h32;
+  // MODE 1: rows of Y by slot t*k + j (up to 16 tokens) instead of by position
+  bool y_by_slot;
 };
 
 // ------------------------------------------------------------------------------ LDS-staged
@@ -204,7 +206,7 @@ struct UnitArgs {
 // resident), so no load is branched around.  Weights are read with non-temporal loads, or
 // with plain (cached) loads when NTW is false, for units whose weights other blocks of the
 // same XCD read again.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true, bool SLOT = false>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
                                             int p0, int cnt, const uint16_t* wbase,
                                             bool shared) {
@@ -309,6 +311,14 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
   if (cnt < NTOK)
     for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
       if (q % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
+  // SLOT (one-tile down-projection units) with Y by slot, a routed group: the slot of the
+  // epilogue's position (thread tid writes position tid % 16 of the unit), requested now so it
+  // is there at the end
+  int out_slot = 0;
+  if constexpr (SLOT) {
+    static_assert(MODE == 1 && TT == 1, "slots of one-tile down-projection units");
+    if (!shared && x.y_by_slot && tid < 64) out_slot = x.rt.perm[p0 + min(tid & 15, cnt - 1)];
+  }
   auto compute_stage = [&]() {
     for (int pr = wave; pr < KSTEPS * ntt; pr += 4) {
       const int ks = pr % KSTEPS, tt = pr / KSTEPS;
@@ -360,6 +370,8 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       float* o;
       if (MODE == 2)
         o = outp + ((size_t)chunk * x.B + p0 + j) * out_rows + row0 + 4 * gg;
+      else if (SLOT && !shared && x.y_by_slot)
+        o = outp + (size_t)out_slot * out_rows + row0 + 4 * gg;
       else
         o = outp + (size_t)(p0 + j) * out_rows + row0 + 4 * gg;
       if (MODE == 2 && x.resid) {
@@ -458,7 +470,8 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
     const int rem = unit - a * tiles * chunks;
     const int tile = rem / chunks, chunk = rem - tile * chunks;
     const Group gr = group_of<MODE>(x, a, n_groups);
-    staged_unit<MODE, TT, KS, NTERM, BF16SRC>(x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
+    staged_unit<MODE, TT, KS, NTERM, BF16SRC, true, MODE == 1 && TT == 1>(
+        x, lds, tile, chunk, gr.p0, gr.cnt, gr.wbase,
                                              gr.shared);
   }
 }
@@ -468,7 +481,9 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
 // the whole K for its own tile pair, token tile by token tile, so a unit costs one weight round
 // trip and needs no cross-wave reduction; the next unit's weights are requested as soon as
 // this unit's are in LDS.  (The general unit splits K over the four waves, which for K = 128
-// leaves one 32-wide step per wave and a reduction per 8 KB of weights.)
+// leaves one 32-wide step per wave and a reduction per 8 KB of weights.)  With x.gu_part the
+// activations are formed as they are staged: the SwiGLU of the gate/up K-chunk partials, summed
+// in chunk order (no SwiGLU launch between the gate/up and the down-projection).
 template <int K>
 __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
   constexpr int K8 = K / 8, WP = K8 + 1, ROWS = 128, WLD = ROWS * K8 / 256;
@@ -511,19 +526,50 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
       lw[rr * WP + ch] = wreg[i];
     }
-    if (unit + step < u1) load_w(unit + step);
     const int ntt = (gr.cnt + 15) / 16;
     const float* asrc = gr.shared ? x.act_shared : reinterpret_cast<const float*>(x.act_routed);
     float* outp = gr.shared ? x.out_shared : x.out_routed;
+    // With Y by slot (up to 16 tokens, one token tile): the slot of the lane's output position,
+    // requested before the next unit's weights so that waiting for it does not wait for those.
+    const int oslot = (gr.shared || !x.y_by_slot) ? 0 : x.rt.perm[gr.p0 + min(c, gr.cnt - 1)];
+    if (unit + step < u1) load_w(unit + step);
     for (int tt = 0; tt < ntt; ++tt) {
       if (ntt > 1 || staged != a) {
         staged = ntt > 1 ? -1 : a;
         const int j = tid / K8, ch = tid - j * K8, jt = tt * 16 + j;
         const bool ok = jt < gr.cnt;
-        const int row = ok ? (gr.shared ? jt : gr.p0 + jt) : 0;
-        const float4* src = reinterpret_cast<const float4*>(asrc + (size_t)row * K + ch * 8);
-        const float4 v0 = src[0], v1 = src[1];
-        float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        float v[8];
+        if (x.gu_part) {
+          // the SwiGLU of the gate/up K-chunk partials of this position (the shared expert's
+          // tokens after the routed positions), chunks summed in order
+          const int pos = ok ? (gr.shared ? x.gu_P - x.B + jt : gr.p0 + jt) : 0;
+          float4 pg[kGateupSplits][2], pu[kGateupSplits][2];
+#pragma unroll
+          for (int c2 = 0; c2 < kGateupSplits; ++c2) {
+            const float* src = x.gu_part + ((size_t)c2 * x.gu_P + pos) * 2 * K + ch * 8;
+            pg[c2][0] = reinterpret_cast<const float4*>(src)[0];
+            pg[c2][1] = reinterpret_cast<const float4*>(src)[1];
+            pu[c2][0] = reinterpret_cast<const float4*>(src + K)[0];
+            pu[c2][1] = reinterpret_cast<const float4*>(src + K)[1];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float zg = 0.f, zu = 0.f;
+#pragma unroll
+            for (int c2 = 0; c2 < kGateupSplits; ++c2) {
+              const float4 g4 = pg[c2][e >> 2], u4 = pu[c2][e >> 2];
+              zg += (e & 3) == 0 ? g4.x : (e & 3) == 1 ? g4.y : (e & 3) == 2 ? g4.z : g4.w;
+              zu += (e & 3) == 0 ? u4.x : (e & 3) == 1 ? u4.y : (e & 3) == 2 ? u4.z : u4.w;
+            }
+            v[e] = silu_f32(zg) * zu;
+          }
+        } else {
+          const int row = ok ? (gr.shared ? jt : gr.p0 + jt) : 0;
+          const float4* src = reinterpret_cast<const float4*>(asrc + (size_t)row * K + ch * 8);
+          const float4 v0 = src[0], v1 = src[1];
+          v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+          v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+        }
         if (!ok)
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = 0.f;
@@ -547,7 +593,8 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
       }
       const int j = tt * 16 + c;
       if (j < gr.cnt) {
-        float* o = outp + (size_t)((gr.shared ? 0 : gr.p0) + j) * x.H + tile * ROWS + wave * 32 + 4 * g;
+        const int orow = gr.shared ? j : (x.y_by_slot ? oslot : gr.p0 + j);
+        float* o = outp + (size_t)orow * x.H + tile * ROWS + wave * 32 + 4 * g;
         *reinterpret_cast<float4*>(o) = float4{acc0[0], acc0[1], acc0[2], acc0[3]};
         *reinterpret_cast<float4*>(o + 16) = float4{acc1[0], acc1[1], acc1[2], acc1[3]};
       }
@@ -892,6 +939,12 @@ bool mfma_gateup_split(const Shape& s, int B) {
   return s.I <= 256 && (B <= 16 || B > 32) && s.H % (kGateupSplits * 256) == 0;
 }
 
+bool mfma_y_by_slot(int B) { return B <= 16; }
+
+bool mfma_swiglu_in_down(const Shape& s, int B) {
+  return mfma_gateup_split(s, B) && B <= 16 && s.I == 128 && s.H % 128 == 0;
+}
+
 // Gate/up K-chunk partials of the split launches (routed and shared), or the shared expert's
 // split-K partials over 32 tokens when the gate/up is not split.
 size_t mfma_scratch_floats(const Shape& s, int B) {
@@ -1055,6 +1108,7 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
     hipError_t e = B <= 16 ? staged_t<0, 1, 256, 2, false, 0>(d, a, max_units * kGateupSplits, st)
                            : staged_t<0, 1, 256, 2, false, 5>(d, a, piece_units, st);
     if (e != hipSuccess) return e;
+    if (mfma_swiglu_in_down(s, B)) return hipSuccess;  // the down-projection sums the chunks
     const size_t cs = (size_t)a.gu_P * 2 * s.I;
     return reduce(SwigluRegion{scratch, cs, nslot, kGateupSplits, A},
                   SwigluRegion{scratch + (size_t)nslot * 2 * s.I, cs, B, kGateupSplits, As});
@@ -1088,8 +1142,13 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, hipStream_t st) {
+                            float* Y, float* ys, const float* gu_part, hipStream_t st) {
   UnitArgs a{};
+  if (mfma_swiglu_in_down(s, B)) {
+    a.gu_part = const_cast<float*>(gu_part);
+    a.gu_P = B * s.k + B;
+  }
+  a.y_by_slot = mfma_y_by_slot(B);
   a.w_routed = (const uint16_t*)w2;
   a.w_shared = (const uint16_t*)ws2;
   a.act_routed = A;

@@ -54,12 +54,14 @@ def test_plan_is_mfma(name, B):
     _, _, L = gpu_layer(name)
     p = L.query_plan(B)
     assert p["path_name"] == "splitk_mfma" and p["forced"] == 0
-    # a small intermediate (up to 16 tokens and over 32) adds the SwiGLU launch of the K-split
-    # gate/up; over 32 tokens an unsplit gate/up adds the shared expert's split-K launch and
-    # its SwiGLU
+    # a small intermediate (up to 16 tokens and over 32) splits the gate/up over K chunks, which
+    # over 32 tokens adds the SwiGLU launch that sums them; over 32 tokens an unsplit gate/up
+    # adds the shared expert's split-K launch and its SwiGLU
     cfg = synth.CONFIGS[name]
     split = (B <= 16 or B > 32) and cfg.inter <= 256
-    want = (8 if B > 16 else 7) + split + (2 if B > 32 and not split else 0)
+    # (up to 16 tokens the down-projection sums the K chunks of an intermediate of 128 itself)
+    swiglu_launch = split and not (B <= 16 and cfg.inter == 128)
+    want = (8 if B > 16 else 7) + swiglu_launch + (2 if B > 32 and not split else 0)
     # a 448-wide o-proj slice without a norm: the o-proj (with its residual) and the router
     # run as one launch (no reduce, no router launch), ten logit partials
     fused = cfg.oproj_in < cfg.hidden and not cfg.norm
