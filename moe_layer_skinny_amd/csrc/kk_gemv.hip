@@ -625,12 +625,15 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   if (TOPK && !SGU && wave < B) load_bias(bias, E, bv);
   if constexpr (SGU)
     for (int i = threadIdx.x; i < E; i += blockDim.x) lb[i] = bias[i];
+  Stage<stage_q(NT, G::K)> st;
+  // (with the shared gate/up the activation rows are requested with the logits, so the two
+  // round trips overlap; otherwise after them, so the logits are not queued behind)
+  if constexpr (SGU) st.load(u, B * G::K);
   if (TOPK) {
     logits_to_lds<false>(part, splits, B, E, lg);
     __syncthreads();
   }
-  Stage<stage_q(NT, G::K)> st;
-  st.load(u, B * G::K);
+  if constexpr (!SGU) st.load(u, B * G::K);
   if constexpr (SGU) {
     // the shared expert's gate/up rows read u, so it goes to LDS first; then the selecting
     // waves run the top-k while the others stream the shared rows into As_out

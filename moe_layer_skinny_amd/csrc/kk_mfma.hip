@@ -206,7 +206,8 @@ struct UnitArgs {
 // resident), so no load is branched around.  Weights are read with non-temporal loads, or
 // with plain (cached) loads when NTW is false, for units whose weights other blocks of the
 // same XCD read again.
-template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true, bool SLOT = false>
+template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true, bool SLOT = false,
+          int DEPTH = 1>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
                                             int p0, int cnt, const uint16_t* wbase,
                                             bool shared) {
@@ -255,15 +256,17 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     const size_t off = (size_t)src * K + kbase + ch * 8;
     asrc[i] = BF16SRC ? (const void*)((const uint16_t*)base + off) : (const void*)((const float*)base + off);
   }
-  u32x4 wreg[WLD], areg[ALD][AW];
+  // DEPTH register buffers of stage loads: DEPTH stages in flight while one is multiplied
+  static_assert(DEPTH == 1 || DEPTH == 2, "one or two stages in flight");
+  u32x4 wreg[DEPTH][WLD], areg[DEPTH][ALD][AW];
   const void* dummy = x.act_routed;
-  auto load_stage = [&](int st) {
+  auto load_stage = [&](int st, int b) {
     const bool live = st < nst;
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const u32x4* p = live ? reinterpret_cast<const u32x4*>(wsrc[i] + st * KS)
                             : reinterpret_cast<const u32x4*>(dummy);
-      wreg[i] = NTW ? __builtin_nontemporal_load(p) : *p;
+      wreg[b][i] = NTW ? __builtin_nontemporal_load(p) : *p;
     }
 #pragma unroll
     for (int i = 0; i < ALD; ++i) {
@@ -271,7 +274,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
                                : reinterpret_cast<const u32x4*>((const float*)asrc[i] + st * KS);
       if (!live) p = reinterpret_cast<const u32x4*>(dummy);
 #pragma unroll
-      for (int w = 0; w < AW; ++w) areg[i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
+      for (int w = 0; w < AW; ++w) areg[b][i][w] = aok[i] ? p[w] : u32x4{0u, 0u, 0u, 0u};
     }
   };
   f32x4 acc[2][TT];
@@ -280,11 +283,11 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) acc[r][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto store_stage = [&]() {
+  auto store_stage = [&](int b) {
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
-      if (q < 32 * K8) lw[rr * WP + ch] = wreg[i];
+      if (q < 32 * K8) lw[rr * WP + ch] = wreg[b][i];
     }
     // only the group's own token slots: the others were zeroed at the start of the unit
 #pragma unroll
@@ -292,13 +295,13 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
       if (q < NTOK * K8 && aok[i]) {
         if constexpr (BF16SRC) {
-          la[ch * NTOK + j] = areg[i][0];
+          la[ch * NTOK + j] = areg[b][i][0];
         } else {
           float v[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            v[e] = __uint_as_float(areg[i][0][e]);
-            v[4 + e] = __uint_as_float(areg[i][1][e]);
+            v[e] = __uint_as_float(areg[b][i][0][e]);
+            v[4 + e] = __uint_as_float(areg[b][i][1][e]);
           }
           u32x4 terms[NTERM];
           split_terms<NTERM>(v, terms);
@@ -340,13 +343,33 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
     }
   };
 
-  load_stage(0);
-  for (int st = 0; st < nst; ++st) {
-    store_stage();
-    __syncthreads();
-    if (st + 1 < nst) load_stage(st + 1);
-    compute_stage();
-    __syncthreads();
+  if constexpr (DEPTH == 1) {
+    load_stage(0, 0);
+    for (int st = 0; st < nst; ++st) {
+      store_stage(0);
+      __syncthreads();
+      if (st + 1 < nst) load_stage(st + 1, 0);
+      compute_stage();
+      __syncthreads();
+    }
+  } else {
+    // (a stage past the end loads the activation buffer into the spare registers, never used)
+    load_stage(0, 0);
+    load_stage(1, 1);
+    for (int st = 0; st < nst; st += 2) {
+      store_stage(0);
+      __syncthreads();
+      load_stage(st + 2, 0);
+      compute_stage();
+      __syncthreads();
+      if (st + 1 < nst) {
+        store_stage(1);
+        __syncthreads();
+        load_stage(st + 3, 1);
+        compute_stage();
+        __syncthreads();
+      }
+    }
   }
   // sum the four waves' partial tiles in wave order, then the epilogue
   f32x4* red = reinterpret_cast<f32x4*>(lds);
@@ -460,7 +483,10 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
         p0 = 16 * (v - nv);
         cnt = min(16, x.B - p0);
       }
-      staged_unit<MODE, 1, KS, NTERM, BF16SRC>(x, lds, tile, chunk, p0, cnt, gr.wbase, gr.shared);
+      // (the full-size routed pieces over 32 tokens: two stages in flight measured faster there;
+      // the other launches keep four blocks per CU with one)
+      staged_unit<MODE, 1, KS, NTERM, BF16SRC, true, false, GSEL == 4 ? 2 : 1>(
+          x, lds, tile, chunk, p0, cnt, gr.wbase, gr.shared);
     }
     return;
   }
