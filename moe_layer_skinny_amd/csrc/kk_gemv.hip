@@ -140,7 +140,15 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WP
   const int stride = gridDim.x * wpb;
   int unit = blockIdx.x * wpb + wave;
 
-  // this wave's router slice, requested first
+  // this thread's chunks of r, requested first: staging them then waits for them alone, not for
+  // the weight loads queued behind (loads complete in order)
+  constexpr int EPC = Elem<T>::EPC, RQ = 4;
+  const int nrc = NT * H / EPC;
+  const u32x4* rsrc = reinterpret_cast<const u32x4*>(r);
+  u32x4 rc[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) rc[q] = rsrc[min((int)threadIdx.x + q * (int)blockDim.x, nrc - 1)];
+  // this wave's router slice
   const int gs = wave * gridDim.x + blockIdx.x;
   const bool has_slice = gs < E * RS;
   const int se = has_slice ? gs / RS : 0, ssl = has_slice ? gs - se * RS : 0;
@@ -165,7 +173,24 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WP
 #pragma unroll
     for (int t = 0; t < NT; ++t) load_act_chunks<T, CPR>(x + (size_t)t * G::K, sub, xa[t]);
   }
-  stage_to_f32<T>(r, NT * H, lr);
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int c = threadIdx.x + q * blockDim.x;
+    if (c < nrc) {
+      float f[EPC];
+      Elem<T>::unpack(rc[q], f);
+      float4* d = reinterpret_cast<float4*>(lr + (size_t)c * EPC);
+#pragma unroll
+      for (int h = 0; h < EPC / 4; ++h) d[h] = make_float4(f[4 * h], f[4 * h + 1], f[4 * h + 2], f[4 * h + 3]);
+    }
+  }
+  for (int c = threadIdx.x + RQ * blockDim.x; c < nrc; c += blockDim.x) {
+    float f[EPC];
+    Elem<T>::unpack(rsrc[c], f);
+    float4* d = reinterpret_cast<float4*>(lr + (size_t)c * EPC);
+#pragma unroll
+    for (int h = 0; h < EPC / 4; ++h) d[h] = make_float4(f[4 * h], f[4 * h + 1], f[4 * h + 2], f[4 * h + 3]);
+  }
   if constexpr (!kRegs) stage_to_f32<T>(x, NT * G::K, lx);
   __syncthreads();
   if (has_slice) {
@@ -397,9 +422,10 @@ __device__ __forceinline__ void shared_rows(const T* __restrict__ ws13, int Is, 
 
 // Router logit partials part[s][t][e] = h32[t][slice s] . W_r[e][slice s] (at most two
 // (expert, slice) units per wave) and, with ws13 != nullptr, the shared expert's gate/up
-// rows, As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  Every wave requests its router
-// slices and its first shared row pair at the start, so the launch streams both weight sets
-// at full bandwidth; the top-k runs at the start of the routed gate/up launch.
+// rows, As[t][i] = silu(Ws1[i] . u_t) * (Ws3[i] . u_t).  Every wave requests its share of the
+// activation rows, then its router slices and its first shared row pair, at the start, so the
+// launch streams both weight sets at full bandwidth; the top-k runs at the start of the routed
+// gate/up launch.
 template <typename T, int CPS, int CPRH, int NT>
 __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
     const float* __restrict__ h32, const T* __restrict__ w_r, int H, int E, int B, int splits,
@@ -417,6 +443,11 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   const int gw = wave * gridDim.x + blockIdx.x, nw = gridDim.x * wpb;
   const bool shared = ws13 != nullptr;
   const int units = E * splits;
+  // The activation rows are requested first: staging them then waits for them alone, not for
+  // the weight loads queued behind (loads complete in order), so every wave can multiply as soon
+  // as its own weights arrive instead of after the whole block's.
+  Stage<stage_q(NT, GH::K)> st;
+  st.load(h32, B * H);
   // router slices of this wave's units (a missing second unit re-reads the last one)
   u32x4 wr[MAXU][G::CPL];
 #pragma unroll
@@ -427,8 +458,6 @@ __global__ __launch_bounds__(kGemvThreads) void router_logits_kernel(
   }
   u32x4 wg[GH::CPL], wu[GH::CPL];
   if (shared && gw < Is) load_pair<T, CPRH>(ws13, 0, gw, Is, wg, wu, lane);
-  Stage<stage_q(NT, GH::K)> st;
-  st.load(h32, B * H);
   if (gamma)
     st.template store_rmsnorm<T, NT>(lds, gamma, eps, H, nred);
   else
