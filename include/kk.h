@@ -32,10 +32,10 @@
  *
  * Ownership: the caller owns every buffer (weights, activations, outputs, workspace).
  * Weights passed to kk_create must stay alive and unchanged until kk_destroy.  The
- * context owns an auxiliary HIP stream, events, cached HIP graphs and, for a bf16 layer with a
- * 448-wide o-proj input slice and no norm, one device buffer: the router-o-proj product
- * W_r W_o (two bf16 planes [2][E][Ko], 0.69 MB at E = 384), computed by kk_create from the
- * weights and freed by kk_destroy.  Every device pointer must be 16-byte aligned; ws must be
+ * context owns an auxiliary HIP stream, events, cached HIP graphs and, for a bf16 layer without
+ * a norm, one device buffer: the router-o-proj product W_r W_o (two bf16 planes [2][E][Ko]; at
+ * E = 384 0.69 MB for a 448-wide o-proj input slice, 11 MB for a 7168-wide input), computed by
+ * kk_create from the weights and freed by kk_destroy.  Every device pointer must be 16-byte aligned; ws must be
  * 256-byte aligned.
  *
  * Concurrency: every op is asynchronous on the caller's stream; no host synchronisation.
@@ -125,8 +125,9 @@ kk_status kk_validate(const kk_config* cfg, int32_t max_batch);
 size_t kk_workspace_bytes(const kk_config* cfg, int32_t max_batch);
 
 /* Creates a context on the current HIP device; weights are referenced, not copied.  For a bf16
- * layer with a 448-wide o-proj slice and no norm it also allocates the router-o-proj product
- * (0.69 MB) and computes it with one kernel on the null stream, synchronised before returning;
+ * layer without a norm it also allocates the router-o-proj product (0.69 MB for a 448-wide
+ * o-proj slice, 11 MB for a 7168-wide input) and computes it with one kernel on the null
+ * stream, synchronised before returning;
  * an allocation or launch failure returns KK_ERR_HIP and no context. */
 kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch, kk_ctx** out);
 kk_status kk_destroy(kk_ctx* ctx);
@@ -170,9 +171,10 @@ kk_status kk_moe_decode(kk_ctx* ctx, int32_t B, const float* h32, const int32_t*
 kk_status kk_routing_status(kk_ctx* ctx, const void* ws, kk_stream stream);
 
 /* The whole step: o-proj + residual (+ norm), router logits, top-k || shared expert gate/up,
- * routed gate/up, down-projection with the combine (batch 1-2: four launches on `stream`, three
- * for a layer with the router-o-proj product, the norm recomputed inside the launches that read
- * u; the split-K MFMA path for larger batches, the norm fused into the o-proj's reduce: see
+ * routed gate/up, down-projection with the combine (batch 1-2: four launches on `stream`, the
+ * norm recomputed inside the launches that read u; three with the router-o-proj product, for a
+ * 448-wide o-proj slice and for a full-width input at batch 2; the split-K MFMA path for larger
+ * batches, the norm fused into the o-proj's reduce: see
  * kk_query_plan for the launch count).  topk_idx / topk_gate are optional
  * copies of the routing (nullable).  With KK_GRAPH the step is captured into a HIP graph on
  * first use for these (B, pointers, stream, flags, planned path) and replayed afterwards.

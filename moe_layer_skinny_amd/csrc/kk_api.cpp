@@ -206,9 +206,18 @@ int forced_path() {
   return -2;
 }
 
+// Whether batch B on the GEMV path runs the three-launch step (the router from r and x in the
+// o-proj's launch): with a 448-wide o-proj slice at both batches; at full width only for two
+// tokens, where the removed router launch gains more than the 11 MB product costs (one token:
+// 158.5 against 157.8 us per step, two: 282 against 291).
+bool gemv_fused(const kk_ctx* c, int B) {
+  return c->mr != nullptr && (c->shape.Ko < c->shape.H || B == 2);
+}
+
 // Whether batch B on the split-K path runs the o-proj and the router as one launch (a layer with
-// the router-o-proj product).
-bool mfma_fused(const kk_ctx* c, int B) { return c->mr != nullptr; }
+// the router-o-proj product and a 448-wide o-proj slice: at full width the product's split-K
+// units would cost about what the saved launches gain).
+bool mfma_fused(const kk_ctx* c, int B) { return c->mr != nullptr && c->shape.Ko < c->shape.H; }
 
 kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
   std::memset(p, 0, sizeof *p);
@@ -225,7 +234,7 @@ kk_status plan_for(const kk_ctx* c, int B, kk_plan* p) {
       return fail(KK_ERR_UNSUPPORTED, "GEMV down-projection needs %zu B of LDS (device: %d)",
                   lds_down, c->dev.max_lds);
     p->oproj_splitk = 1;
-    if (c->mr) {
+    if (gemv_fused(c, B)) {
       // o-proj + router logits (from x and r), top-k + shared gate/up + routed gate/up,
       // routed + shared down + combine
       p->router_splitk = kk::router_fused_splits(c->shape);
@@ -578,7 +587,7 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
   kk::Routing rt{idx ? idx : p.topk_idx, gate ? gate : p.topk_gate, p.offsets, p.perm,
                  p.inv_perm, p.act, p.n_act, p.vg, p.n_vg};
   KK_HIP(kk::launch_delay(c->delay_ticks[0], s), "delay launch");
-  if (path == KK_PATH_GEMV && c->mr) return enqueue_layer_gemv3(c, B, x, r, out, rt, p, s, two_stream, pf);
+  if (path == KK_PATH_GEMV && gemv_fused(c, B)) return enqueue_layer_gemv3(c, B, x, r, out, rt, p, s, two_stream, pf);
   if (path == KK_PATH_SPLITK_MFMA && mfma_fused(c, B)) {
     KK_HIP(timed(c, K_OPROJ_ROUTER_MFMA, s,
                  [&] {
@@ -724,10 +733,9 @@ kk_status kk_create(const kk_config* cfg, const kk_weights* w, int32_t max_batch
     if (e != hipSuccess) return bail(e, "fork event");
     e = hipEventCreateWithFlags(&c->ev_join, hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "join event");
-    // the router-o-proj product for the GEMV path's fused o-proj + router launch: a layer
-    // without a norm (the router reads h itself) whose o-proj input is a slice (Ko < H), so
-    // that the product (E x Ko per plane) is small beside the router matrix (E x H); for a
-    // full-width input it costs more bandwidth than the launch it saves
+    // the router-o-proj product for the fused o-proj + router launch of a layer without a norm
+    // (the router reads h itself): E x Ko per plane, 0.69 MB for a 448-wide o-proj slice (used
+    // by both paths), 11 MB for a full-width input (GEMV path, two tokens)
     if (kk::router_fused_applies(c->shape) && !c->norm.gamma) {
       e = hipMalloc(&c->mr, kk::router_oproj_product_bytes(c->shape));
       if (e != hipSuccess) return bail(e, "router-o-proj product allocation");

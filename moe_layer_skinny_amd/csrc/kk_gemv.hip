@@ -6,6 +6,9 @@
 //   3. top-k, gates and routing tables (every block, from the partials)  ||  shared expert
 //      down-projection; then the routed gate/up over the active experts
 //   4. routed down-projection with the weighted combine into the residual
+// A layer without a norm runs three: the router logits come from r and x through the
+// router-o-proj product in the o-proj's launch, the top-k runs in the routed gate/up launch
+// beside the shared expert's gate/up, and the shared down-projection joins the last launch.
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
 // time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
@@ -238,7 +241,8 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(WP
 // in fp64, rounded to fp32 and stored as npl planes of T ([npl][E][Ko]): bf16 hi = RNE(m),
 // lo = RNE(m - hi) (their sum reproduces m to 2^-17 relative); fp32 one plane, m itself.
 // (A logit's error from the two planes: about 2^-17 of |M| |x| per term, ~1e-6 over 448
-// terms, far below the 1e-3 gap the selection keeps.)
+// terms and ~2e-5 over 7168 (|M| ~ 0.034 for weights of scale 0.02), far below the 1e-3 gap
+// the selection keeps.)
 // Block tile 32 experts x 64 columns, 32-wide steps along n staged in LDS; each thread owns
 // 2 x 4 outputs.
 template <typename T>
@@ -1322,7 +1326,7 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 }
 
 bool router_fused_applies(const Shape& s) {
-  return s.dtype == 1 && s.Ko < s.H && s.H == 7168 && gemv_supported(s, 1);
+  return s.dtype == 1 && s.H == 7168 && (s.Ko == 448 || s.Ko == 7168) && gemv_supported(s, 1);
 }
 
 int router_oproj_planes(const Shape& s) { return s.dtype == 1 ? 2 : 1; }
@@ -1347,8 +1351,11 @@ hipError_t launch_oproj_router_gemv(const Shape& s, const Device& d, int B, cons
                                     const void* r, const void* w_o, const void* w_r, const void* mr,
                                     float* h32, void* h_out, float* part, hipStream_t st) {
   const int c = cpr_of(s.Ko, s.dtype);
-  if (router_fused_applies(s) && c == 56)  // 448-wide input slice; router slices of 3584
-    return oproj_router_t<uint16_t, 56, 448, 4>(s, d, B, x, r, w_o, w_r, mr, h32, h_out, part, st);
+  if (!router_fused_applies(s)) return hipErrorInvalidValue;
+  // router slices of 3584 against r; 448-wide input slice: 4 rows of W_o or M per wave, a full
+  // 7168-wide input: one row per wave, x in registers (one token) or LDS (two)
+  if (c == 56) return oproj_router_t<uint16_t, 56, 448, 4>(s, d, B, x, r, w_o, w_r, mr, h32, h_out, part, st);
+  if (c == 896) return oproj_router_t<uint16_t, 896, 448, 1>(s, d, B, x, r, w_o, w_r, mr, h32, h_out, part, st);
   return hipErrorInvalidValue;
 }
 

@@ -74,7 +74,7 @@ hipError_t launch_oproj_gemv(const Shape& s, const Device& d, int B, const void*
 
 // The router-o-proj product mr = W_r W_o of a layer ([planes][E][Ko] in the weight dtype:
 // bf16 as hi + lo planes, fp32 as one), computed once (fp64 accumulation).
-bool router_fused_applies(const Shape& s);  // bf16 GEMV shapes with Ko < H
+bool router_fused_applies(const Shape& s);  // bf16 GEMV shapes with H = 7168, Ko 448 or 7168
 int router_oproj_planes(const Shape& s);
 size_t router_oproj_product_bytes(const Shape& s);
 hipError_t launch_router_oproj_product(const Shape& s, const void* w_r, const void* w_o, void* mr,
