@@ -434,7 +434,19 @@ struct Group {
   int p0, cnt;
   bool shared;
 };
-template <int MODE>
+// A wave-uniform read of a routing table entry, through the scalar data cache when SCALAR.  The
+// tables are written by an earlier launch (the cache starts each dispatch invalidated), so the
+// read sees them; its wait then counts scalar loads only, not the vector loads (weights) in
+// flight.  (Measured per kernel: it shortens the short-K down-projection, whose next unit's
+// group is looked up behind the current unit's output-slot load, and costs the grouped
+// launches a little.)
+template <bool SCALAR>
+__device__ __forceinline__ int table_entry(const int* p, int i) {
+  if constexpr (SCALAR) return ((const __attribute__((address_space(4))) int*)p)[i];
+  return p[i];
+}
+
+template <int MODE, bool SCALAR = false>
 __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups) {
   Group gr{x.w_routed, 0, x.B, false};
   if (MODE == 2) return gr;
@@ -443,9 +455,9 @@ __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups
   if (gr.shared) {
     gr.wbase = x.w_shared;
   } else {
-    const int e = x.rt.act[a];
-    gr.p0 = x.rt.offsets[e];
-    gr.cnt = x.rt.offsets[e + 1] - gr.p0;
+    const int e = table_entry<SCALAR>(x.rt.act, a);
+    gr.p0 = table_entry<SCALAR>(x.rt.offsets, e);
+    gr.cnt = table_entry<SCALAR>(x.rt.offsets, e + 1) - gr.p0;
     gr.wbase = x.w_routed + (size_t)e * wstride;
   }
   return gr;
@@ -525,7 +537,7 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
   auto load_w = [&](int un) {
     const int u = min(un, units - 1);  // past the end: a valid unit's rows, never used
     const int a = u / tiles, tile = u - a * tiles;
-    const Group gr = group_of<1>(x, a, n_groups);
+    const Group gr = group_of<1, true>(x, a, n_groups);
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
@@ -546,7 +558,7 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
   int staged = -1;  // group whose (single) token tile la holds
   for (int unit = u0; unit < u1; unit += step) {
     const int a = unit / tiles, tile = unit - a * tiles;
-    const Group gr = group_of<1>(x, a, n_groups);
+    const Group gr = group_of<1, true>(x, a, n_groups);
 #pragma unroll
     for (int i = 0; i < WLD; ++i) {
       const int q = tid + 256 * i, rr = q / K8, ch = q - rr * K8;
