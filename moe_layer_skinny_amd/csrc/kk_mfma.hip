@@ -199,7 +199,9 @@ struct UnitArgs {
 // loads are in flight.  Each wave's partial tiles are summed through LDS in wave order at
 // the end of the unit.
 //   LDS weights: [32 rows][KS/8 + 1] 16-byte chunks (one chunk of padding per row)
-//   LDS activations: [NTERM][KS/8][16*TT tokens] 16-byte chunks
+//   LDS activations: [NTERM][16*TT tokens][KS/8 + 1] 16-byte chunks (token-major: a thread's
+//   store lands next to its neighbours', and the padding spreads the 16 tokens one operand
+//   read touches over all banks)
 // One unit of the LDS-staged product: the tile pair `tile` of group (wbase, positions p0 ..
 // p0 + cnt - 1, `shared`) over K chunk `chunk`.  The next stage's loads are kept in flight in
 // registers; a stage past the end reads the activation buffer instead (small and cache-
@@ -213,6 +215,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
                                             bool shared) {
   constexpr int K8 = KS / 8;
   constexpr int WP = K8 + 1;
+  constexpr int AP = K8 + 1;
   constexpr int NTOK = 16 * TT;
   constexpr int W_CH = 32 * WP;
   constexpr int WLD = (32 * K8 + 255) / 256;    // weight chunks per thread per stage
@@ -295,7 +298,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
       if (q < NTOK * K8 && aok[i]) {
         if constexpr (BF16SRC) {
-          la[ch * NTOK + j] = areg[b][i][0];
+          la[j * AP + ch] = areg[b][i][0];
         } else {
           float v[8];
 #pragma unroll
@@ -306,14 +309,14 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
           u32x4 terms[NTERM];
           split_terms<NTERM>(v, terms);
 #pragma unroll
-          for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
+          for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * NTOK + j) * AP + ch] = terms[q2];
         }
       }
     }
   };
   if (cnt < NTOK)
-    for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
-      if (q % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
+    for (int q = tid; q < NTERM * NTOK * AP; q += 256)
+      if ((q / AP) % NTOK >= cnt) la[q] = u32x4{0u, 0u, 0u, 0u};
   // SLOT (one-tile down-projection units) with Y by slot, a routed group: the slot of the
   // epilogue's position (thread tid writes position tid % 16 of the unit), requested now so it
   // is there at the end
@@ -329,7 +332,7 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
       const u32x4 a1 = lw[(16 + c) * WP + ks * 4 + g];
       u32x4 bq[NTERM];
 #pragma unroll
-      for (int q2 = 0; q2 < NTERM; ++q2) bq[q2] = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
+      for (int q2 = 0; q2 < NTERM; ++q2) bq[q2] = la[(q2 * NTOK + tt * 16 + c) * AP + ks * 4 + g];
 #pragma unroll
       for (int t2 = 0; t2 < TT; ++t2) {
         if (t2 == tt) {
@@ -423,8 +426,8 @@ __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int t
 
 // LDS bytes of one block of staged_unit<.., TT, KS, NTERM, ..>.
 constexpr size_t staged_lds(int TT, int KS, int NTERM) {
-  return (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16 > (size_t)4 * 2 * TT * 64 * 16
-             ? (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16
+  return (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8 + 1) * 16 * TT) * 16 > (size_t)4 * 2 * TT * 64 * 16
+             ? (size_t)(32 * (KS / 8 + 1) + NTERM * (KS / 8 + 1) * 16 * TT) * 16
              : (size_t)4 * 2 * TT * 64 * 16;
 }
 
@@ -524,11 +527,11 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
 // in chunk order (no SwiGLU launch between the gate/up and the down-projection).
 template <int K>
 __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
-  constexpr int K8 = K / 8, WP = K8 + 1, ROWS = 128, WLD = ROWS * K8 / 256;
+  constexpr int K8 = K / 8, WP = K8 + 1, AP = K8 + 1, ROWS = 128, WLD = ROWS * K8 / 256;
   static_assert(16 * K8 == 256, "one activation chunk per thread and token tile");
   extern __shared__ u32x4 lds[];
   u32x4* lw = lds;              // [ROWS][WP]
-  u32x4* la = lds + ROWS * WP;  // [2 terms][K8][16 tokens]
+  u32x4* la = lds + ROWS * WP;  // [2 terms][16 tokens][AP]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
   const int n_groups = *x.rt.n_act + 1;
   const int tiles = x.H / ROWS;
@@ -613,8 +616,8 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
           for (int e = 0; e < 8; ++e) v[e] = 0.f;
         u32x4 terms[2];
         split_terms<2>(v, terms);
-        la[(0 * K8 + ch) * 16 + j] = terms[0];
-        la[(1 * K8 + ch) * 16 + j] = terms[1];
+        la[(0 * 16 + j) * AP + ch] = terms[0];
+        la[(1 * 16 + j) * AP + ch] = terms[1];
       }
       __syncthreads();
       f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -624,7 +627,7 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
         const u32x4 a1 = lw[(wave * 32 + 16 + c) * WP + ks * 4 + g];
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-          const u32x4 b = la[(q2 * K8 + ks * 4 + g) * 16 + c];
+          const u32x4 b = la[(q2 * 16 + c) * AP + ks * 4 + g];
           acc0 = mfma(a0, b, acc0);
           acc1 = mfma(a1, b, acc1);
         }
@@ -651,7 +654,7 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
 // activation buffer.
 template <int TT, int KS, int NTERM, bool BF16SRC, int RTW = 2>
 __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
-  constexpr int ROWS = 64 * RTW, K8 = KS / 8, WP = K8 + 1, NTOK = 16 * TT;
+  constexpr int ROWS = 64 * RTW, K8 = KS / 8, WP = K8 + 1, AP = K8 + 1, NTOK = 16 * TT;
   constexpr int WLD = ROWS * K8 / 256;          // weight chunks per thread per stage
   constexpr int ALD = (NTOK * K8 + 255) / 256;  // activation chunks (8 values) per thread
   constexpr int AW = BF16SRC ? 1 : 2;           // 16-byte words per activation chunk
@@ -659,15 +662,15 @@ __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
   static_assert(ROWS * K8 % 256 == 0, "whole weight chunks per thread");
   extern __shared__ u32x4 lds[];
   u32x4* lw = lds;                  // [ROWS][WP]
-  u32x4* la = lds + ROWS * WP;      // [NTERM][K8][NTOK]
+  u32x4* la = lds + ROWS * WP;      // [NTERM][NTOK][AP]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
   const int K = x.K, N = x.N, B = x.B, chunks = x.chunks;
   const int kchunk = K / chunks, nst = kchunk / KS;
   const int units = (N / ROWS) * chunks;
   const int ntt = (B + 15) / 16;
   // slots past the batch stay zero in LDS for the whole launch
-  for (int q = tid; q < NTERM * K8 * NTOK; q += 256)
-    if (q % NTOK >= B) la[q] = u32x4{0u, 0u, 0u, 0u};
+  for (int q = tid; q < NTERM * NTOK * AP; q += 256)
+    if ((q / AP) % NTOK >= B) la[q] = u32x4{0u, 0u, 0u, 0u};
   const void* dummy = x.act_routed;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int rb = unit / chunks, chunk = unit - rb * chunks;
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
         const int q = tid + 256 * i, j = q / K8, ch = q - j * K8;
         if (q < NTOK * K8 && aok[i]) {
           if constexpr (BF16SRC) {
-            la[ch * NTOK + j] = areg[i][0];
+            la[j * AP + ch] = areg[i][0];
           } else {
             float v[8];
 #pragma unroll
@@ -726,7 +729,7 @@ __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
             u32x4 terms[NTERM];
             split_terms<NTERM>(v, terms);
 #pragma unroll
-            for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * K8 + ch) * NTOK + j] = terms[q2];
+            for (int q2 = 0; q2 < NTERM; ++q2) la[(q2 * NTOK + j) * AP + ch] = terms[q2];
           }
         }
       }
@@ -751,7 +754,7 @@ __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
           if (tt < ntt) {
 #pragma unroll
             for (int q2 = 0; q2 < NTERM; ++q2) {
-              const u32x4 bq = la[(q2 * K8 + ks * 4 + g) * NTOK + tt * 16 + c];
+              const u32x4 bq = la[(q2 * NTOK + tt * 16 + c) * AP + ks * 4 + g];
 #pragma unroll
               for (int r = 0; r < RTW; ++r) acc[r][tt] = mfma(a[r], bq, acc[r][tt]);
             }
@@ -777,7 +780,7 @@ __global__ __launch_bounds__(256) void mfma_tall_kernel(UnitArgs x) {
 
 // LDS bytes of one block of mfma_tall_kernel<TT, KS, NTERM, .., RTW>.
 constexpr size_t tall_lds(int TT, int KS, int NTERM, int RTW = 2) {
-  return (size_t)(64 * RTW * (KS / 8 + 1) + NTERM * (KS / 8) * 16 * TT) * 16;
+  return (size_t)(64 * RTW * (KS / 8 + 1) + NTERM * (KS / 8 + 1) * 16 * TT) * 16;
 }
 
 // Split-K product with the tokens split as well: units (row tile, K chunk, 16-token quarter),
@@ -1202,7 +1205,7 @@ hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float*
   if (s.I == 2048) return grouped_dispatch<1>(d, a, max_units, st);
   if (s.I == 128 && s.H % 128 == 0) {
     auto kern = mfma_down_shortk_kernel<128>;
-    constexpr size_t lds = (size_t)(128 * (128 / 8 + 1) + 2 * (128 / 8) * 16) * 16;
+    constexpr size_t lds = (size_t)(128 * (128 / 8 + 1) + 2 * 16 * (128 / 8 + 1)) * 16;
     static thread_local int bpc = 0;
     const int units = ((s.E < B * s.k ? s.E : B * s.k) + 1) * (s.H / 128);
     hipLaunchKernelGGL(kern, dim3(resident_grid(d, kern, lds, units, &bpc)), dim3(256), lds, st, a);
