@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   // round trips overlap; otherwise after them, so the logits are not queued behind)
   if constexpr (SGU) st.load(u, B * G::K);
   if (TOPK) {
-    logits_to_lds<false>(part, splits, B, E, lg);
+    logits_to_lds(part, splits, B, E, lg);
     __syncthreads();
   }
   if constexpr (!SGU) st.load(u, B * G::K);

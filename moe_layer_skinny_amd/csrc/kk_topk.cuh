@@ -152,9 +152,7 @@ __device__ __forceinline__ void topk_row(const float* part, int splits, const fl
 }
 
 // Block-wide: logits lg[t * E + e] of all B tokens summed from part[splits][B][E] in slice
-// order (B * E <= 2 * blockDim.x), each thread's loads all in flight together; DEVICE: read
-// at device scope (partials written by other blocks in the same launch).
-template <bool DEVICE>
+// order (B * E <= 2 * blockDim.x), each thread's loads all in flight together.
 __device__ inline void logits_to_lds(const float* part, int splits, int B, int E, float* lg) {
   constexpr int MAXS = kMaxTopkSplits;
   const int n = B * E;
@@ -164,8 +162,7 @@ __device__ inline void logits_to_lds(const float* part, int splits, int B, int E
     const int i = min((int)(threadIdx.x + j * blockDim.x), n - 1);
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
-      const float* src = part + (size_t)min(s, splits - 1) * n + i;
-      pv[j][s] = DEVICE ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : *src;
+      pv[j][s] = part[(size_t)min(s, splits - 1) * n + i];
     }
   }
 #pragma unroll
