@@ -1255,16 +1255,16 @@ size_t down_combine_lds(const Shape& s, int B, int RG, bool sh) {
 }
 
 // Row groups per block: two blocks of 8 waves per CU when their LDS fits and the kernel
-// fits in 128 VGPRs (not so for two tokens' activations over 4 KB rows), else one.  One token
-// over short rows (one chunk per lane: a 128-wide intermediate) also takes one block per CU:
-// its waves' longer runs measured faster (TP share batch 1: 11.9 -> 11.1 us; 4 KB rows the
-// other way, 41.2 -> 43.2).
+// fits in 128 VGPRs (not so for two tokens' activations over 4 KB rows), else one.  Short rows
+// (one chunk per lane: a 128-wide intermediate) also take one block per CU: their waves'
+// longer runs measured faster (TP share down-projection, batch 1: 11.9 -> 11.1 us, batch 2:
+// 16.0 -> 14.5; 4 KB rows at batch 1 the other way, 41.2 -> 43.2).
 template <typename T, int CPR>
 int down_groups_per_block(const Shape& s, const Device& d, int B, bool sh, int* per_cu) {
   const int groups = (s.H + Geo<T, CPR>::RPW - 1) / Geo<T, CPR>::RPW;
   const int rg2 = (groups + 2 * d.num_cu - 1) / (2 * d.num_cu);
   const bool two = 2 * down_combine_lds<T, CPR>(s, B, rg2, sh) <= (size_t)d.max_lds &&
-                   !(B == 2 && Geo<T, CPR>::CPL >= 4) && !(B == 1 && Geo<T, CPR>::CPL == 1);
+                   !(B == 2 && Geo<T, CPR>::CPL >= 4) && !(B <= 2 && Geo<T, CPR>::CPL == 1);
   if (per_cu) *per_cu = two ? 2 : 1;
   return two ? rg2 : (groups + d.num_cu - 1) / d.num_cu;
 }
