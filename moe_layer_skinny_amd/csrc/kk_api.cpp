@@ -532,8 +532,8 @@ kk_status enqueue_prefetch(const PrefetchNext& pf, hipStream_t s) {
   return KK_OK;
 }
 
-// GEMV path of a layer without a norm (the router-o-proj product mr exists): three launches.
-// o-proj + router logits from x and r; the top-k in every block of the routed gate/up launch,
+// GEMV step in three launches, for a layer with the router-o-proj product at the batches
+// gemv_fused picks: o-proj + router logits from x and r; the top-k in every block of the routed gate/up launch,
 // covered by the shared expert's gate/up (or, two_stream, that gate/up on the auxiliary stream,
 // joined before the last launch); routed and shared down-projection with the combine.
 kk_status enqueue_layer_gemv3(kk_ctx* c, int B, const void* x, const void* r, void* out,

@@ -6,9 +6,10 @@
 //   3. top-k, gates and routing tables (every block, from the partials)  ||  shared expert
 //      down-projection; then the routed gate/up over the active experts
 //   4. routed down-projection with the weighted combine into the residual
-// A layer without a norm runs three: the router logits come from r and x through the
-// router-o-proj product in the o-proj's launch, the top-k runs in the routed gate/up launch
-// beside the shared expert's gate/up, and the shared down-projection joins the last launch.
+// A layer without a norm can run three (a 448-wide o-proj slice at batch 1-2, a full-width one
+// at batch 2): the router logits come from r and x through the router-o-proj product in the
+// o-proj's launch, the top-k runs in the routed gate/up launch beside the shared expert's
+// gate/up, and the shared down-projection joins the last launch.
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering
 // time between operators": small-matrix projection kernels at batch 1-2; o-proj fused with
