@@ -24,7 +24,9 @@ def _torch():
     return torch
 
 
-@pytest.mark.parametrize("name,B", [("tp_rank", 1), ("tp_rank", 2), ("full_b1", 1)])
+# (the full-width layer at two tokens takes the 3-launch step, its shared gate/up on the
+# auxiliary stream beside the top-k + routed gate/up launch)
+@pytest.mark.parametrize("name,B", [("tp_rank", 1), ("tp_rank", 2), ("full_b1", 1), ("full_b64", 2)])
 def test_two_stream_step_is_timing_independent(name, B):
     log(f"[hazard-two-stream] {name} B={B}")
     torch = _torch()
