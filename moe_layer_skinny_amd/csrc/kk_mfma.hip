@@ -10,19 +10,23 @@
 // NTERM bf16 terms hi + lo (+ lo2) whose sum reproduces them (to 2^-17 relative with two
 // terms, exactly with three), so the products keep fp32-level accuracy; x is already bf16.
 //
-// Launches of one step (7 to 10, by batch and intermediate size; kk_query_plan counts them):
-//   1. o-proj partials over 7 K chunks (32 rows x one chunk per block unit; one chunk for a
-//      448-wide input slice)
+// Launches of one step (5 to 10, by batch, intermediate size and o-proj width;
+// kk_query_plan counts them):
+//   1. o-proj partials over 7 K chunks (32 rows x one chunk per block unit; over 16 tokens
+//      128-row units with all tokens)
 //   2. reduce: h32 = resid + sum of chunks (fixed order), optional h_out (with an RMSNorm the
 //      reduce also writes u32 = norm(h32))
 //   3. router logit partials (three-term h32), then the top-k: one launch with the routing
 //      tables up to 16 tokens, else a top-k launch and a tables launch
+//      (a 448-wide o-proj slice without a norm: 1-3 are one launch, the o-proj with its
+//      residual and the router from r and x through the router-o-proj product, then the top-k)
 //   4. grouped gate/up over the active experts + the shared expert, one (expert, 16 gate
 //      rows, 16 up rows) unit per block over the whole K; SwiGLU epilogue -> A (fp32).  Small
-//      intermediates split every group over K chunks and add a SwiGLU launch that sums them;
-//      over 32 tokens the shared expert's gate/up is a split-K launch of its own plus that
-//      SwiGLU launch
-//   5. grouped down-projection the same way -> Y (per position) and ys (shared)
+//      intermediates split every group over K chunks and add a SwiGLU launch that sums them
+//      (up to 16 tokens the down-projection sums them instead); over 32 tokens the shared
+//      expert's gate/up is a split-K launch of its own plus that SwiGLU launch
+//   5. grouped down-projection the same way -> Y (by slot up to 16 tokens, else by position)
+//      and ys (shared)
 //   6. the combine launch shared with the GEMV path
 //
 // "Hyper Optimizing Kimi K3 in vLLM: Moving Fast and Responsibly", section "Recovering time
@@ -203,11 +207,11 @@ struct UnitArgs {
 //   store lands next to its neighbours', and the padding spreads the 16 tokens one operand
 //   read touches over all banks)
 // One unit of the LDS-staged product: the tile pair `tile` of group (wbase, positions p0 ..
-// p0 + cnt - 1, `shared`) over K chunk `chunk`.  The next stage's loads are kept in flight in
-// registers; a stage past the end reads the activation buffer instead (small and cache-
-// resident), so no load is branched around.  Weights are read with non-temporal loads, or
-// with plain (cached) loads when NTW is false, for units whose weights other blocks of the
-// same XCD read again.
+// p0 + cnt - 1, `shared`) over K chunk `chunk`.  The next stage's loads (DEPTH stages) are
+// kept in flight in registers; with two, a stage past the end reads the activation buffer
+// instead (small and cache-resident), so every loop pass issues the same loads.  Weights are
+// read with non-temporal loads, or with plain (cached) loads when NTW is false, for units
+// whose weights other blocks of the same XCD read again.
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, bool NTW = true, bool SLOT = false,
           int DEPTH = 1>
 __device__ __forceinline__ void staged_unit(const UnitArgs& x, u32x4* lds, int tile, int chunk,
