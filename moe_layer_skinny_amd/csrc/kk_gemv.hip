@@ -643,9 +643,11 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
   __shared__ LdsTables tb;
   __shared__ float lg[TOPK ? 2 * kMaxExperts : 1];
   __shared__ float lb[SGU ? kMaxExperts : 1];  // the bias, when the selection runs after the staging
+  __shared__ int next_unit;  // two tokens, full-size rows: the block's next unit (unit loop)
   const int lane = threadIdx.x & 63, wpb = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nslot = B * k;
+  if (NT > 1 && CPRS >= 256 && threadIdx.x == 0) next_unit = wpb;  // (read after the barriers below)
   // the logits first, by the whole block, before any weight stream competes with their loads;
   // the waves that run a token's selection (wave t: token t) request their bias values with
   // them.  With the shared gate/up (SGU), the waves past the selecting ones request their
@@ -788,11 +790,30 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
     }
   };
 
-  // units run across the blocks first: with fewer units than waves every CU still streams
+  // units run across the blocks first: with fewer units than waves every CU still streams.
+  // Block b owns units b + j * gridDim.x and wave w starts on j = w.  For two tokens over
+  // full-size rows (more than two units per wave), each next j comes from a block counter, so a
+  // wave that gets fewer issue slots (the younger waves of a SIMD) takes fewer units and the
+  // block's waves finish together (277.2 -> 274.1 us per step; one token, or the 128-wide
+  // TP-share intermediate, measured no gain); otherwise j steps by the block's wave count.
+  // Each unit writes its own outputs, so the assignment leaves every value as it is.
+  constexpr bool kCounter = NT > 1 && CPRS >= 256;
   int cur = wave * gridDim.x + blockIdx.x;
+  const bool dyn = kCounter && units > 2 * stride;
+  auto grab = [&]() {
+    if constexpr (kCounter) {
+      if (dyn) {
+        int j = 0;
+        if (lane == 0) j = atomicAdd(&next_unit, 1);
+        return (int)blockIdx.x + __builtin_amdgcn_readfirstlane(j) * (int)gridDim.x;
+      }
+    }
+    return cur + stride;
+  };
   issue_a(cur);
   issue_b(cur);
-  for (; cur < units; cur += stride) {
+  for (int nxt; cur < units; cur = nxt) {
+    nxt = grab();
     const int a = cur / I, i = cur - a * I;
     const int p0 = __builtin_amdgcn_readlane(t_lo, min(a, 63));
     const int cnt = __builtin_amdgcn_readlane(t_cnt, min(a, 63));
@@ -812,7 +833,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
       if (NT > 1) __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(cur + stride);
+    issue_a(nxt);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < HB; ++j) {
@@ -824,7 +845,7 @@ __global__ __launch_bounds__(kGemvThreads) void gateup_gemv_kernel(
 #pragma unroll
     for (int q = 0; q < NT; ++q) asm volatile("" : "+v"(z1[q]), "+v"(z3[q]));
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(cur + stride);
+    issue_b(nxt);
 #pragma unroll
     for (int q = 0; q < NT; ++q) {
       const float g = seg_sum_dpp<64>(z1[q]);
