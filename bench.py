@@ -173,7 +173,7 @@ def roofline_for(path_name, by, kernels, workload, B):
 
 
 def sweep(main_cfg, main_w, args, s, flush) -> dict:
-    """The other workloads: batch 8 / 64 of the full-size layer, an 8-token speculative-verify
+    """The other workloads: batch 2 / 8 / 64 of the full-size layer, an 8-token speculative-verify
     batch (correlated tokens of one sequence) and the layer with an RMSNorm before the router
     and experts at batch 1 / 8, on the same resident weights (only the router bias and the
     norm weight differ), and one TP rank's share at batch 1, 2, 8, 64."""
@@ -184,10 +184,10 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
     from moe_layer_skinny_amd import kk
 
     out = {}
-    plan = ([("full_b8", 8), ("full_b64", 64), ("verify_b8", 8), ("full_norm", 1), ("full_norm", 8)]
-            + [("tp_rank", b) for b in (1, 2, 8, 64)])
+    cases = ([("full_b8", 2), ("full_b8", 8), ("full_b64", 64), ("verify_b8", 8), ("full_norm", 1),
+              ("full_norm", 8)] + [("tp_rank", b) for b in (1, 2, 8, 64)])
     weights = {}
-    for name, B in plan:
+    for name, B in cases:
         cfg = synth.CONFIGS[name]
         same = (cfg.hidden, cfg.oproj_in, cfg.inter) == (main_cfg.hidden, main_cfg.oproj_in,
                                                          main_cfg.inter)
@@ -210,16 +210,16 @@ def sweep(main_cfg, main_w, args, s, flush) -> dict:
         parts = unique_bytes(cfg, n_act)
         by = parts["total"]
         gbs = by / (us * 1e-6) / 1e9
-        plan = layer.query_plan(B)
+        lp = layer.query_plan(B)
         kern = {} if args.no_timing_pass else kernel_times(layer, B, x, r, o, idx, gate, ws, s,
                                                             flush, max(5, args.steps // 2))
         out[f"{name}@{B}"] = {"us_per_step": round(us, 3), "tokens_per_s": round(B / (us * 1e-6), 1),
                               "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                               "n_act": n_act, "unique_bytes": by,
-                              "path": plan["path_name"],
-                              "kernels_per_step": plan["kernels_per_step"],
+                              "path": lp["path_name"],
+                              "kernels_per_step": lp["kernels_per_step"],
                               "kernel_us_eager": {k: round(v, 3) for k, v in kern.items()},
-                              "roofline": roofline_for(plan["path_name"], parts, kern, name, B)}
+                              "roofline": roofline_for(lp["path_name"], parts, kern, name, B)}
         log(f"[bench] {name}@{B}: {out[f'{name}@{B}']}")
         layer.close()
     return out
