@@ -75,8 +75,11 @@ typedef enum {
 
 /* kk_layer_decode flags */
 #define KK_GRAPH 1u      /* capture the step once per (B, buffers, stream, flags), replay it */
-#define KK_TWO_STREAM 2u /* shared expert's gate/up on the context's auxiliary stream instead
-                            of inside the top-k launch (kept for comparison) */
+#define KK_TWO_STREAM 2u /* the shared expert on the context's auxiliary stream (kept for
+                            comparison; same output bits): batch 1-2 its gate/up instead of
+                            inside the top-k launch, batch 3-64 its gate/up and down-projection
+                            (forked after the o-proj, joined before the combine) instead of as
+                            the last group of the grouped launches */
 #define KK_PREFETCH 4u   /* kk_chain_decode: after layer l's o-proj, the first context's
                             auxiliary stream reads layer l+1's o-proj, router and shared gate/up
                             weights once, so that layer finds them in the memory-side cache */

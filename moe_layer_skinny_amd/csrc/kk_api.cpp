@@ -136,12 +136,12 @@ const char* kernel_names[] = {"oproj_gemv",  "router_logits_shared", "router_log
                               "oproj_reduce", "router_mfma", "gateup_mfma", "down_mfma",
                               "topk_rows",   "tables", "topk_tables", "oproj_reduce_norm",
                               "norm_rows", "prefetch", "oproj_router_gemv",
-                              "topk_shared_gateup_gemv", "oproj_router_mfma"};
+                              "topk_shared_gateup_gemv", "oproj_router_mfma", "shared_mfma"};
 enum KName {
   K_OPROJ, K_LOGITS_SHARED, K_LOGITS, K_GU_SHARED, K_GU_ROUTED, K_TOPK_GU, K_DOWN, K_PREP,
   K_COMBINE, K_OPROJ_MFMA, K_OPROJ_REDUCE, K_ROUTER_MFMA, K_GU_MFMA, K_DOWN_MFMA, K_TOPK_ROWS,
   K_TABLES, K_TOPK_TABLES, K_OPROJ_REDUCE_NORM, K_NORM_ROWS, K_PREFETCH, K_OPROJ_ROUTER,
-  K_TOPK_SHARED_GU, K_OPROJ_ROUTER_MFMA
+  K_TOPK_SHARED_GU, K_OPROJ_ROUTER_MFMA, K_SHARED_MFMA
 };
 
 struct TimingRec {
@@ -425,23 +425,50 @@ kk_status enqueue_router_mfma(kk_ctx* c, int B, const float* u, const kk::Routin
   return enqueue_topk(c, B, logit_part, kk::mfma_router_splits(c->shape), rt, s);
 }
 
-// MFMA path: grouped gate/up (from u) and down over the active experts plus the shared one,
-// combine (onto h32).
+// MFMA path, KK_TWO_STREAM: the shared expert's gate/up and down-projection on the auxiliary
+// stream from u (forked here, joined before the combine), the same kernels as in the grouped
+// launches restricted to the shared group, so the bits are the same.  They read no routing table
+// and write only As / ys and the shared positions of the gate/up scratch.
+kk_status fork_shared_mfma(kk_ctx* c, int B, const float* u, const kk::Routing& rt,
+                           const WsPtrs& p, hipStream_t s) {
+  KK_HIP(hipEventRecord(c->ev_fork, s), "fork event");
+  KK_HIP(hipStreamWaitEvent(c->aux, c->ev_fork, 0), "aux wait");
+  KK_HIP(kk::launch_delay(c->delay_ticks[1], c->aux), "delay launch");
+  KK_HIP(timed(c, K_SHARED_MFMA, c->aux,
+               [&] {
+                 hipError_t e = kk::launch_gateup_mfma(c->shape, c->dev, B, u, c->w.w13, c->w.ws13,
+                                                       rt, p.A, p.As, p.oproj_part, c->aux,
+                                                       kk::kGroupsSharedOnly);
+                 if (e != hipSuccess) return e;
+                 return kk::launch_down_mfma(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
+                                             p.Y, p.ys, p.oproj_part, c->aux,
+                                             kk::kGroupsSharedOnly);
+               }),
+         "shared expert launches");
+  KK_HIP(hipEventRecord(c->ev_join, c->aux), "join event");
+  return KK_OK;
+}
+
+// MFMA path: grouped gate/up (from u) and down over the active experts plus the shared one
+// (the active experts only when two_stream: the shared expert was forked), combine (onto h32).
 kk_status enqueue_experts_mfma(kk_ctx* c, int B, const float* u, const float* h32,
-                               const kk::Routing& rt, const WsPtrs& p, void* out, hipStream_t s) {
+                               const kk::Routing& rt, const WsPtrs& p, void* out, hipStream_t s,
+                               bool two_stream = false) {
+  const int sel = two_stream ? kk::kGroupsRoutedOnly : kk::kGroupsEvery;
   KK_HIP(timed(c, K_GU_MFMA, s,
                [&] {
                  // (the o-proj partials are consumed by now: their region is scratch)
                  return kk::launch_gateup_mfma(c->shape, c->dev, B, u, c->w.w13, c->w.ws13, rt,
-                                               p.A, p.As, p.oproj_part, s);
+                                               p.A, p.As, p.oproj_part, s, sel);
                }),
          "gate/up launch");
   KK_HIP(timed(c, K_DOWN_MFMA, s,
                [&] {
                  return kk::launch_down_mfma(c->shape, c->dev, B, p.A, p.As, c->w.w2, c->w.ws2, rt,
-                                             p.Y, p.ys, p.oproj_part, s);
+                                             p.Y, p.ys, p.oproj_part, s, sel);
                }),
          "down launch");
+  if (two_stream) KK_HIP(hipStreamWaitEvent(s, c->ev_join, 0), "join wait");
   KK_HIP(timed(c, K_COMBINE, s,
                [&] { return kk::launch_combine(c->shape, B, h32, p.Y, p.ys, rt, out, s); }),
          "combine launch");
@@ -599,18 +626,21 @@ kk_status enqueue_layer(kk_ctx* c, int B, const void* x, const void* r, void* ou
       kk_status st = enqueue_prefetch(*pf, s);
       if (st != KK_OK) return st;
     }
-    kk_status st = enqueue_topk(c, B, p.logit_part, kk::mfma_fused_splits(c->shape), rt, s);
+    kk_status st = two_stream ? fork_shared_mfma(c, B, p.h32, rt, p, s) : KK_OK;
     if (st != KK_OK) return st;
-    return enqueue_experts_mfma(c, B, p.h32, p.h32, rt, p, out, s);
+    st = enqueue_topk(c, B, p.logit_part, kk::mfma_fused_splits(c->shape), rt, s);
+    if (st != KK_OK) return st;
+    return enqueue_experts_mfma(c, B, p.h32, p.h32, rt, p, out, s, two_stream);
   }
   kk_status st = enqueue_oproj(c, B, x, r, p.h32, nullptr, p.oproj_part, p.u32, path, s);
   if (st != KK_OK) return st;
   if (pf && (st = enqueue_prefetch(*pf, s)) != KK_OK) return st;
   if (path == KK_PATH_SPLITK_MFMA) {
     const float* u = c->norm.gamma ? p.u32 : p.h32;
+    if (two_stream && (st = fork_shared_mfma(c, B, u, rt, p, s)) != KK_OK) return st;
     st = enqueue_router_mfma(c, B, u, rt, p.logit_part, s);
     if (st != KK_OK) return st;
-    return enqueue_experts_mfma(c, B, u, p.h32, rt, p, out, s);
+    return enqueue_experts_mfma(c, B, u, p.h32, rt, p, out, s, two_stream);
   }
   if (!two_stream) {
     // the shared expert's gate/up streams with the router logits, its down-projection
@@ -914,8 +944,6 @@ kk_status kk_layer_decode(kk_ctx* c, int32_t B, const void* x, const void* resid
     const bool two = (flags & KK_TWO_STREAM) != 0;
     kk_plan plan0;
     if ((st = plan_for(c, B, &plan0)) != KK_OK) return st;
-    if (two && plan0.path != KK_PATH_GEMV)
-      return fail(KK_ERR_UNSUPPORTED, "KK_TWO_STREAM applies to the GEMV path (batch 1-2)");
     hipStream_t s = (hipStream_t)stream;
     if (!(flags & KK_GRAPH))
       return enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, ws, s, two, plan0.path);
@@ -987,8 +1015,6 @@ kk_status kk_layer_decode_static(kk_ctx* c, int32_t B, const void* x, const void
     const bool two = (flags & KK_TWO_STREAM) != 0;
     kk_plan plan;
     if ((st = plan_for(c, B, &plan)) != KK_OK) return st;
-    if (two && plan.path != KK_PATH_GEMV)
-      return fail(KK_ERR_UNSUPPORTED, "KK_TWO_STREAM applies to the GEMV path (batch 1-2)");
     c->no_alloc = true;
     st = enqueue_layer(c, B, x, resid, out, topk_idx, topk_gate, c->scratch, (hipStream_t)stream,
                        two, plan.path, nullptr, &Ls);

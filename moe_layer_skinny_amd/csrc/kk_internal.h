@@ -187,9 +187,13 @@ size_t mfma_scratch_floats(const Shape& s, int B);
 // Whether batch B's gate/up also splits every group over K chunks (small intermediates), with
 // a SwiGLU launch of its own after it (or, with mfma_swiglu_in_down, inside the down-projection).
 bool mfma_gateup_split(const Shape& s, int B);
+// `sel` picks the groups (both launches): every group, the active experts only, or the shared
+// expert only (which reads no routing table), so that the shared expert can run on a stream of
+// its own with the same kernels and the same bits.
+constexpr int kGroupsEvery = 0, kGroupsRoutedOnly = 1, kGroupsSharedOnly = 2;
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
-                              float* As, float* scratch, hipStream_t st);
+                              float* As, float* scratch, hipStream_t st, int sel = 0);
 // Whether the down-projection forms its activations itself, as the SwiGLU of the gate/up K-chunk
 // partials (small intermediate up to 16 tokens): the gate/up launch then leaves A / As unwritten.
 bool mfma_swiglu_in_down(const Shape& s, int B);
@@ -200,6 +204,7 @@ bool mfma_y_by_slot(int B);
 // with mfma_swiglu_in_down the SwiGLU of the gate/up partials in gu_part (the gate/up's scratch).
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, const float* gu_part, hipStream_t st);
+                            float* Y, float* ys, const float* gu_part, hipStream_t st,
+                            int sel = 0);
 
 }  // namespace kk

@@ -185,6 +185,9 @@ struct UnitArgs {
   float* h32;
   // MODE 1: rows of Y by slot t*k + j (up to 16 tokens) instead of by position
   bool y_by_slot;
+  // MODE 0 / 1: the groups this launch covers: kGroupsEvery, kGroupsRoutedOnly (the active
+  // experts) or kGroupsSharedOnly (the shared expert, which reads no routing table)
+  int sel;
 };
 
 // ------------------------------------------------------------------------------ LDS-staged
@@ -477,14 +480,18 @@ __device__ __forceinline__ Group group_of(const UnitArgs& x, int a, int n_groups
 template <int MODE, int TT, int KS, int NTERM, bool BF16SRC, int GSEL>
 __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];  // weights then activations; reused for the final reduction
-  const int n_groups = MODE == 2 ? 1 : *x.rt.n_act + 1;
+  // groups: the active experts 0 .. n_act - 1, then the shared expert; a launch covers all of
+  // them, the routed ones (ng = n_act) or the shared one (n_act taken as 0: no table is read)
+  const int n_act = (MODE == 2 || x.sel == kGroupsSharedOnly) ? 0 : *x.rt.n_act;
+  const int n_groups = n_act + 1;
+  const int ng = x.sel == kGroupsRoutedOnly ? n_act : n_groups;
   const int out_rows = MODE == 0 ? x.I : (MODE == 1 ? x.H : x.N);
   const int tiles = MODE == 0 ? x.I / 16 : out_rows / 32;
   const int chunks = (MODE == 2 || (MODE == 0 && x.gu_part)) ? x.chunks : 1;
   if constexpr (GSEL >= 4) {
     static_assert(TT == 1 && MODE != 2, "pieces are one token tile of a grouped launch");
-    const int nv = *x.rt.n_vg;
-    const int pieces = nv + (GSEL == 5 ? (x.B + 15) / 16 : 0);
+    const int nv = x.sel == kGroupsSharedOnly ? 0 : *x.rt.n_vg;
+    const int pieces = nv + (GSEL == 5 && x.sel != kGroupsRoutedOnly ? (x.B + 15) / 16 : 0);
     const int units = pieces * tiles * chunks;
     for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
       const int v = unit / (tiles * chunks);
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(256) void mfma_staged_kernel(UnitArgs x) {
     }
     return;
   }
-  const int units = n_groups * tiles * chunks;
+  const int units = (MODE == 2 ? 1 : ng) * tiles * chunks;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
     const int a = unit / (tiles * chunks);
     const int rem = unit - a * tiles * chunks;
@@ -537,9 +544,10 @@ __global__ __launch_bounds__(256) void mfma_down_shortk_kernel(UnitArgs x) {
   u32x4* lw = lds;              // [ROWS][WP]
   u32x4* la = lds + ROWS * WP;  // [2 terms][16 tokens][AP]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c = lane & 15;
-  const int n_groups = *x.rt.n_act + 1;
+  const int n_act = x.sel == kGroupsSharedOnly ? 0 : *x.rt.n_act;
+  const int n_groups = n_act + 1;  // the shared expert last
   const int tiles = x.H / ROWS;
-  const int units = n_groups * tiles;
+  const int units = (x.sel == kGroupsRoutedOnly ? n_act : n_groups) * tiles;
   u32x4 wreg[WLD];
   auto load_w = [&](int un) {
     const int u = min(un, units - 1);  // past the end: a valid unit's rows, never used
@@ -861,12 +869,15 @@ __global__ __launch_bounds__(256) void mfma_oproj_router_kernel(MultiArgs m) {
 template <int MODE, int TTB, int KSB, int KS1>
 __global__ __launch_bounds__(256) void mfma_grouped_kernel(UnitArgs x) {
   extern __shared__ u32x4 lds[];
-  const int n_groups = *x.rt.n_act + 1;
+  const int n_act = x.sel == kGroupsSharedOnly ? 0 : *x.rt.n_act;
+  const int n_groups = n_act + 1;
+  // the launch's groups, from the top
+  const int ng = x.sel == kGroupsRoutedOnly ? n_act : n_groups;
   const int tiles = MODE == 0 ? x.I / 16 : x.H / 32;
-  const int units = n_groups * tiles;
+  const int units = ng * tiles;
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int a = n_groups - 1 - unit / tiles;
-    const int tile = unit - (n_groups - 1 - a) * tiles;
+    const int a = ng - 1 - unit / tiles;
+    const int tile = unit - (ng - 1 - a) * tiles;
     const Group gr = group_of<MODE>(x, a, n_groups);
     if (gr.cnt > 16)
       staged_unit<MODE, TTB, KSB, 2, false>(x, lds, tile, 0, gr.p0, gr.cnt, gr.wbase, gr.shared);
@@ -1115,8 +1126,10 @@ hipError_t launch_router_mfma(const Shape& s, const Device& d, int B, const floa
 
 hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const float* h32,
                               const void* w13, const void* ws13, const Routing& rt, float* A,
-                              float* As, float* scratch, hipStream_t st) {
+                              float* As, float* scratch, hipStream_t st, int sel) {
+  const bool routed = sel != kGroupsSharedOnly, shared = sel != kGroupsRoutedOnly;
   UnitArgs a{};
+  a.sel = sel;
   a.w_routed = (const uint16_t*)w13;
   a.w_shared = (const uint16_t*)ws13;
   a.act_routed = h32;
@@ -1133,6 +1146,7 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   const int nslot = B * s.k;
   auto reduce = [&](const SwigluRegion& r0, const SwigluRegion& r1) {
     const int n = (r0.rows + r1.rows) * s.I;
+    if (n == 0) return hipSuccess;
     if (r0.chunks > 8 || r1.chunks > 8)
       hipLaunchKernelGGL((swiglu_reduce_kernel<16>), dim3((n + 255) / 256), dim3(256), 0, st, r0,
                          r1, s.I);
@@ -1155,8 +1169,9 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
     if (e != hipSuccess) return e;
     if (mfma_swiglu_in_down(s, B)) return hipSuccess;  // the down-projection sums the chunks
     const size_t cs = (size_t)a.gu_P * 2 * s.I;
-    return reduce(SwigluRegion{scratch, cs, nslot, kGateupSplits, A},
-                  SwigluRegion{scratch + (size_t)nslot * 2 * s.I, cs, B, kGateupSplits, As});
+    return reduce(SwigluRegion{scratch, cs, routed ? nslot : 0, kGateupSplits, A},
+                  SwigluRegion{scratch + (size_t)nslot * 2 * s.I, cs, shared ? B : 0,
+                               kGateupSplits, As});
   }
   if (B > 16 && B <= 32) {
     // every routed expert and the shared one cut into pieces of 16 positions, one-tile units
@@ -1176,19 +1191,20 @@ hipError_t launch_gateup_mfma(const Shape& s, const Device& d, int B, const floa
   sh.N = 2 * s.Is;
   sh.K = s.H;
   sh.chunks = kSharedSplits;
-  hipError_t e = tall_t<4, 128, 2, false>(d, sh, st);
+  hipError_t e = shared ? tall_t<4, 128, 2, false>(d, sh, st) : hipSuccess;
   if (e != hipSuccess) return e;
   const int units = (s.E + nslot / 16 + 1) * (s.I / 16);
-  e = staged_t<0, 1, 256, 2, false, 4>(d, a, units, st);
+  e = routed ? staged_t<0, 1, 256, 2, false, 4>(d, a, units, st) : hipSuccess;
   if (e != hipSuccess) return e;
   return reduce(SwigluRegion{scratch, 0, 0, 1, A},
-                SwigluRegion{scratch, (size_t)B * 2 * s.Is, B, kSharedSplits, As});
+                SwigluRegion{scratch, (size_t)B * 2 * s.Is, shared ? B : 0, kSharedSplits, As});
 }
 
 hipError_t launch_down_mfma(const Shape& s, const Device& d, int B, const float* A,
                             const float* As, const void* w2, const void* ws2, const Routing& rt,
-                            float* Y, float* ys, const float* gu_part, hipStream_t st) {
+                            float* Y, float* ys, const float* gu_part, hipStream_t st, int sel) {
   UnitArgs a{};
+  a.sel = sel;
   if (mfma_swiglu_in_down(s, B)) {
     a.gu_part = const_cast<float*>(gu_part);
     a.gu_P = B * s.k + B;

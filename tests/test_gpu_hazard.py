@@ -25,8 +25,12 @@ def _torch():
 
 
 # (the full-width layer at two tokens takes the 3-launch step, its shared gate/up on the
-# auxiliary stream beside the top-k + routed gate/up launch)
-@pytest.mark.parametrize("name,B", [("tp_rank", 1), ("tp_rank", 2), ("full_b1", 1), ("full_b64", 2)])
+# auxiliary stream beside the top-k + routed gate/up launch; from three tokens the split-K path
+# forks the shared expert's gate/up and down-projection after the o-proj and joins before the
+# combine)
+@pytest.mark.parametrize("name,B", [("tp_rank", 1), ("tp_rank", 2), ("full_b1", 1), ("full_b64", 2),
+                                    ("tp_rank", 8), ("tp_rank", 64), ("full_b64", 24),
+                                    ("full_b64", 64)])
 def test_two_stream_step_is_timing_independent(name, B):
     log(f"[hazard-two-stream] {name} B={B}")
     torch = _torch()

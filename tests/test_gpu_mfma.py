@@ -170,15 +170,37 @@ def test_forced_plans_are_visible_and_agree():
     assert L.query_plan(2)["forced"] == 0
 
 
-def test_two_stream_flag_rejected_on_mfma_path():
-    log("[two-stream-mfma] tp_rank B=8")
+# (TP share: K-chunk gate/up with the SwiGLU in the down-projection up to 16 tokens, pieces at 24,
+# K chunks and a SwiGLU launch at 64, the fused o-proj + router; with a norm: the fork after the
+# norm; full size: grouped launches at 8, pieces and the mixed down at 24, the shared expert's
+# split-K gate/up at 64)
+TWO_STREAM_CASES = [("tp_rank", 3), ("tp_rank", 8), ("tp_rank", 16), ("tp_rank", 24),
+                    ("tp_rank", 64), ("tp_norm", 8), ("full_b8", 8), ("full_b64", 24),
+                    ("full_b64", 64)]
+
+
+@pytest.mark.parametrize("name,B", TWO_STREAM_CASES)
+def test_two_stream_mfma_step_equals_one_stream(name, B):
+    """The shared expert on the auxiliary stream runs the grouped launches' own kernels on its
+    group alone, so the step's bits equal the one-stream step's."""
+    log(f"[two-stream-mfma] {name} B={B}")
     torch = _torch()
-    from moe_layer_skinny_amd import kk
-    cfg, _, L = gpu_layer("tp_rank")
-    b = _bufs(cfg, 8)
+    import synth.device as sd
+    cfg, _, L = gpu_layer(name)
+    assert L.query_plan(B)["path_name"] == "splitk_mfma"
+    x, r, _, _ = sd.device_tokens(cfg, B)
+    b = _bufs(cfg, B)
     ws = L.new_workspace()
-    x = torch.zeros(8, cfg.oproj_in, dtype=torch.bfloat16, device="cuda")
-    r = torch.zeros(8, cfg.hidden, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(kk.KKError) as e:
-        L.layer_decode(8, x, r, b["out"], ws, two_stream=True)
-    assert e.value.status == kk.KK_ERR_UNSUPPORTED
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s)
+    s.synchronize()
+    ref, ref_idx, ref_gate = b["out"].clone(), b["idx"].clone(), b["gate"].clone()
+    for graph in (False, True, True):
+        b["out"].zero_()
+        with torch.cuda.stream(s):
+            L.layer_decode(B, x, r, b["out"], ws, b["idx"], b["gate"], stream=s, two_stream=True,
+                           graph=graph)
+        s.synchronize()
+        assert torch.equal(b["out"], ref), f"two-stream step differs (graph={graph})"
+        assert torch.equal(b["idx"], ref_idx) and torch.equal(b["gate"], ref_gate)

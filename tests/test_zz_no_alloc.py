@@ -54,10 +54,13 @@ def test_static_entry_two_stream_and_errors():
     import synth.device as sd
     from moe_layer_skinny_amd import kk
     cfg, _, L = gpu_layer("tp_rank")
+    # (batch 8: the split-K path, its shared expert forked onto the auxiliary stream)
+    for B in (8, 2):
+        xb, rb, _, _ = sd.device_tokens(cfg, B)
+        want = _run_pair(L, cfg, B, xb, rb, static=False)
+        got = _run_pair(L, cfg, B, xb, rb, static=True, two_stream=True)
+        assert all(torch.equal(w, g) for w, g in zip(want, got)), f"B={B}"
     x, r, _, _ = sd.device_tokens(cfg, 2)
-    want = _run_pair(L, cfg, 2, x, r, static=False)
-    got = _run_pair(L, cfg, 2, x, r, static=True, two_stream=True)
-    assert all(torch.equal(w, g) for w, g in zip(want, got))
     out = torch.empty(2, cfg.hidden, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kk.KKError) as e:  # no graph capture through this entry point
         kk.lib()
