@@ -1424,7 +1424,9 @@ hipError_t launch_down_combine_gemv(const Shape& s, const Device& d, int B, cons
   const int c = cpr_of(s.I, s.dtype);
   if (s.dtype == 1) {
     if (c == 256) return down_combine_t<uint16_t, 256, 1>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
-    if (c == 16) return down_combine_t<uint16_t, 16, 4>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
+    // (128-wide rows: two 4-row items per buffer; with four the TP share's batch-1 and batch-2
+    // steps took 1.2 and 0.9 us longer: each wave's first wait covered more loads)
+    if (c == 16) return down_combine_t<uint16_t, 16, 2>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
   } else if (c == 32) {
     return down_combine_t<float, 32, 2>(s, d, B, A, ys, w2, h32, rt, out, ws2, As, st);
   }
