@@ -1022,11 +1022,13 @@ hipError_t launch_oproj_mfma(const Shape& s, const Device& d, int B, const void*
   a.chunks = mfma_oproj_splits(s);
   const int units = (s.H / 32) * a.chunks;
   if (s.Ko == 7168) {  // 7 x 1024 k
-    // over 16 tokens 128-row units, so that the tokens' activations are staged once per 128
-    // weight rows
+    // 128-row units, so that the tokens' activations are staged once per 128 weight rows and
+    // each wave runs the whole K chunk for its rows (no cross-wave reduction): up to 16 tokens
+    // too, where they measured 0.4-1.8 us shorter than 32-row units with K split over the waves
+    (void)units;
     if (B > 32) return tall_t<4, 128, 1, true>(d, a, st);
     if (B > 16) return tall_t<2, 128, 1, true>(d, a, st);
-    return staged_dispatch<2, 1, true>(d, a, units, st);
+    return tall_t<1, 128, 1, true>(d, a, st);
   }
   if (s.Ko == 448) {  // up to 32 tokens the whole 448 k in one stage (one weight round trip)
     if (B <= 16) return staged_t<2, 1, 448, 1, true>(d, a, units, st);
