@@ -38,7 +38,11 @@ TRAFFIC_RECORDS = {("gemv", "full_b1", 1): "profiles/topk_gateup_gemv_full_b1.js
                    ("splitk_mfma", "tp_rank", 64): "profiles/mfma_tp_rank_b64.json",
                    ("splitk_mfma", "full_b8", 8): "profiles/grouped_mfma_full_b8.json",
                    ("splitk_mfma", "verify_b8", 8): "profiles/grouped_mfma_verify_b8.json",
-                   ("splitk_mfma", "full_b64", 64): "profiles/grouped_mfma_full_b64.json"}
+                   ("splitk_mfma", "full_b64", 64): "profiles/grouped_mfma_full_b64.json",
+                   ("gemv", "full_b8", 2): "profiles/topk_shared_gateup_gemv_full_b8_batch2.json",
+                   ("gemv", "tp_rank", 2): "profiles/topk_shared_gateup_gemv_tp_rank_b2.json",
+                   ("gemv", "full_norm", 1): "profiles/topk_gateup_gemv_full_norm_b1.json",
+                   ("splitk_mfma", "full_norm", 8): "profiles/grouped_mfma_full_norm_b8.json"}
 
 
 def measured_traffic(path_name: str, workload: str, B: int):
